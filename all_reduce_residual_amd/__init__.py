@@ -1,0 +1,195 @@
+"""Python binding of the MI355X fused all-reduce-sum (+ residual + RMSNorm) library.
+
+Thin marshalling over the C ABI in ``include/ar_fused.h`` (``libar_fused.so``, built from
+``csrc/`` for gfx950): each function takes torch tensors on the GPU, checks that they are
+contiguous, of one element type and of the [M, H] shape the call implies, and passes their
+device pointers, sizes and the current HIP stream to the function of the same name.  Every
+step of the computation runs in the library's HIP kernels; there is no other code path.  If the
+library has not been built, every call raises.
+
+Operations (fusion patterns kAllReduce and kARResidualRMSNorm):
+  ar_sum(inputs, out)                    out = sum of the W partials (binary32, rank order)
+  ar_residual_rmsnorm(inputs, residual, gamma, eps, residual_out, norm_out)
+                                         residual_out = sum + residual
+                                         norm_out = RMSNorm(residual_out) * gamma
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import threading
+from typing import Dict, Optional, Sequence
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libar_fused.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "ar_fused.h")
+
+DTYPE_FP32, DTYPE_FP16, DTYPE_BF16 = 0, 1, 2
+PATTERN_ALLREDUCE, PATTERN_AR_RESIDUAL_RMSNORM = 0, 1
+AR_OK, AR_ERR_INVALID_ARG, AR_ERR_UNSUPPORTED, AR_ERR_MISALIGNED = 0, 1, 2, 3
+AR_ERR_ALIAS, AR_ERR_LAUNCH, AR_ERR_DEVICE = 4, 5, 6
+SUPPORTED_W = (1, 2, 4, 8, 16, 32, 64)
+
+_lib = None
+_lock = threading.Lock()
+
+
+class ArError(RuntimeError):
+    """A non-zero status from the library."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (where, status_string(status), status))
+
+
+class LaunchConfig(ctypes.Structure):
+    _fields_ = [("threads_per_block", ctypes.c_int32), ("vecs_per_thread", ctypes.c_int32),
+                ("lanes_per_row", ctypes.c_int32), ("rows_per_block", ctypes.c_int32),
+                ("grid", ctypes.c_int32), ("flat", ctypes.c_int32)]
+
+    def as_dict(self) -> Dict[str, int]:
+        return {name: int(getattr(self, name)) for name, _ in self._fields_}
+
+    @classmethod
+    def from_dict(cls, d: Dict[str, int]) -> "LaunchConfig":
+        return cls(**{name: int(d[name]) for name, _ in cls._fields_})
+
+
+def lib():
+    """The loaded library (ctypes.CDLL); raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("HIP library %s is not built; run __graft_entry__.build() or "
+                               "python all_reduce_residual_amd/_build.py" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+        cfgp = ctypes.POINTER(LaunchConfig)
+        sig = {
+            "ar_sum": [vp, i32, i64, i64, i32, vp, vp],
+            "ar_sum_with_config": [vp, i32, i64, i64, i32, vp, vp, cfgp],
+            "ar_residual_rmsnorm": [vp, i32, i64, i64, i32, vp, vp, f32, vp, vp, vp],
+            "ar_residual_rmsnorm_with_config": [vp, i32, i64, i64, i32, vp, vp, f32, vp, vp, vp,
+                                                cfgp],
+            "ar_supports": [i32, i32, i64, i64, i32],
+            "ar_launch_config": [i32, i32, i64, i64, i32, i32, cfgp],
+            "ar_status_string": [i32],
+            "ar_device_cu_count": [ctypes.POINTER(ctypes.c_int)],
+        }
+        for name, argtypes in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = argtypes
+            fn.restype = ctypes.c_char_p if name == "ar_status_string" else ctypes.c_int
+        _lib = L
+        return L
+
+
+def header_functions() -> Sequence[str]:
+    """Names of the functions include/ar_fused.h declares."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(ar_\w+)\s*\(", text, flags=re.M)))
+
+
+def status_string(status: int) -> str:
+    return lib().ar_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != AR_OK:
+        raise ArError(status, where)
+
+
+def dtype_code(torch_dtype) -> int:
+    import torch
+    codes = {torch.float32: DTYPE_FP32, torch.float16: DTYPE_FP16, torch.bfloat16: DTYPE_BF16}
+    if torch_dtype not in codes:
+        raise TypeError("unsupported element type %s" % (torch_dtype,))
+    return codes[torch_dtype]
+
+
+def _stream_handle(stream, device) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _marshal_inputs(inputs, out_like):
+    """Check the partials against the [M, H] output and return (ptr array, W, M, H, dtype)."""
+    if len(inputs) == 0:
+        raise ValueError("need at least one partial")
+    if out_like.dim() != 2:
+        raise ValueError("tensors must be [M, H]")
+    M, H = out_like.shape
+    for t in list(inputs) + [out_like]:
+        if t.dtype != out_like.dtype or tuple(t.shape) != (M, H):
+            raise ValueError("every tensor must be [%d, %d] %s" % (M, H, out_like.dtype))
+        if not t.is_cuda or t.device != out_like.device:
+            raise ValueError("every tensor must be on %s" % out_like.device)
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    ptrs = (ctypes.c_void_p * len(inputs))(*[t.data_ptr() for t in inputs])
+    return ptrs, len(inputs), M, H, dtype_code(out_like.dtype)
+
+
+def ar_sum(inputs, out, stream=None, config: Optional[Dict[str, int]] = None) -> None:
+    """kAllReduce: out = RN_T(x_0 + ... + x_{W-1}), binary32 in rank order."""
+    ptrs, W, M, H, dt = _marshal_inputs(inputs, out)
+    s = _stream_handle(stream, out.device)
+    if config is None:
+        st = lib().ar_sum(ptrs, W, M, H, dt, out.data_ptr(), s)
+    else:
+        cfg = LaunchConfig.from_dict(config)
+        st = lib().ar_sum_with_config(ptrs, W, M, H, dt, out.data_ptr(), s, ctypes.byref(cfg))
+    _check(st, "ar_sum")
+
+
+def ar_residual_rmsnorm(inputs, residual, gamma, eps: float, residual_out, norm_out,
+                        stream=None, config: Optional[Dict[str, int]] = None) -> None:
+    """kARResidualRMSNorm: residual_out = RN_T(sum + residual); norm_out = RMSNorm * gamma."""
+    import torch
+    ptrs, W, M, H, dt = _marshal_inputs(inputs, residual_out)
+    _marshal_inputs([residual], norm_out)
+    _marshal_inputs([residual], residual_out)
+    if gamma.dtype != torch.float32 or tuple(gamma.shape) != (H,) or not gamma.is_contiguous():
+        raise ValueError("gamma must be a contiguous float32 [%d] tensor" % H)
+    if gamma.device != residual_out.device:
+        raise ValueError("gamma must be on %s" % residual_out.device)
+    s = _stream_handle(stream, residual_out.device)
+    args = (ptrs, W, M, H, dt, residual.data_ptr(), gamma.data_ptr(), float(eps),
+            residual_out.data_ptr(), norm_out.data_ptr(), s)
+    if config is None:
+        st = lib().ar_residual_rmsnorm(*args)
+    else:
+        cfg = LaunchConfig.from_dict(config)
+        st = lib().ar_residual_rmsnorm_with_config(*args, ctypes.byref(cfg))
+    _check(st, "ar_residual_rmsnorm")
+
+
+def ar_supports(pattern: int, W: int, M: int, H: int, dtype: int) -> int:
+    """Status the pattern would return for this shape (AR_OK if supported); no device access."""
+    return int(lib().ar_supports(pattern, W, M, H, dtype))
+
+
+def ar_launch_config(pattern: int, W: int, M: int, H: int, dtype: int,
+                     cu_count: int = 0) -> Dict[str, int]:
+    """The launch shape the library picks (cu_count <= 0: query the current device)."""
+    cfg = LaunchConfig()
+    _check(lib().ar_launch_config(pattern, W, M, H, dtype, cu_count, ctypes.byref(cfg)),
+           "ar_launch_config")
+    return cfg.as_dict()
+
+
+def ar_device_cu_count() -> int:
+    n = ctypes.c_int(0)
+    _check(lib().ar_device_cu_count(ctypes.byref(n)), "ar_device_cu_count")
+    return int(n.value)
+
+
+def ar_status_string(status: int) -> str:
+    return status_string(status)

@@ -1,0 +1,491 @@
+// ar_fused.hip -- host side of the C ABI declared in include/ar_fused.h: argument validation,
+// the launch-shape heuristic, and dispatch to the gfx950 kernels in ar_kernels.hpp.
+//
+// Nothing here allocates device memory or synchronises: each entry point validates, picks a
+// launch shape and enqueues exactly one kernel on the caller's stream.  Validation runs before
+// any HIP call, so a rejected call touches neither the device nor the outputs.
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "ar_fused.h"
+#include "ar_kernels.hpp"
+
+namespace {
+
+using arf::F16;
+using arf::F32;
+using arf::Bf16;
+using arf::RankPtrs;
+using arf::u32x4;
+using arf::f32x4;
+
+constexpr int kVecBytes = 16;
+
+int elem_size(int dtype) { return dtype == AR_DTYPE_FP32 ? 4 : 2; }
+bool valid_dtype(int dtype) {
+  return dtype == AR_DTYPE_FP32 || dtype == AR_DTYPE_FP16 || dtype == AR_DTYPE_BF16;
+}
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+int64_t pow2_ceil(int64_t x) {
+  int64_t p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+// ---- shape-level checks ---------------------------------------------------------------------
+
+// Status for (pattern, W, M, H, dtype) alone.  Supported world sizes follow the pages' set
+// {2, 4, 8, 16, 32, 64} (vLLM pull request "[Perf] Tune FlashInfer all-reduce selection on
+// SM103", Scope) plus W = 1.
+int check_shape(int pattern, int W, int64_t M, int64_t H, int dtype) {
+  if (pattern != AR_PATTERN_ALLREDUCE && pattern != AR_PATTERN_AR_RESIDUAL_RMSNORM)
+    return AR_ERR_INVALID_ARG;
+  if (W < 1 || M < 0 || H < 1 || !valid_dtype(dtype)) return AR_ERR_INVALID_ARG;
+  if (W > AR_MAX_W || !is_pow2(W)) return AR_ERR_UNSUPPORTED;
+  const int64_t es = elem_size(dtype);
+  // Keep every byte offset far from int64 overflow.
+  if (M > 0 && H > (int64_t(1) << 60) / (M * es)) return AR_ERR_UNSUPPORTED;
+  if (pattern == AR_PATTERN_AR_RESIDUAL_RMSNORM) {
+    const int64_t vec = kVecBytes / es;
+    if (H % vec != 0) return AR_ERR_UNSUPPORTED;
+    if (H > (dtype == AR_DTYPE_FP32 ? AR_MAX_H_FP32 : AR_MAX_H_16BIT)) return AR_ERR_UNSUPPORTED;
+  }
+  return AR_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+Range range_of(const void* p, int64_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, lo + static_cast<uintptr_t>(bytes)};
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+// An output may coincide exactly with a same-sized input (in place); any other overlap is
+// rejected.  Each element is read and written by the same thread, reads first.
+bool bad_alias_with_input(Range out, Range in) {
+  return overlap(out, in) && !(out.lo == in.lo && out.hi == in.hi);
+}
+
+// ---- device facts -----------------------------------------------------------------------------
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+int query_cu_count(int* cu) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return AR_ERR_DEVICE;
+  if (dev < kMaxDevices) {
+    const int cached = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (cached > 0) {
+      *cu = cached;
+      return AR_OK;
+    }
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0)
+    return AR_ERR_DEVICE;
+  if (dev < kMaxDevices) g_cu_count[dev].store(n, std::memory_order_relaxed);
+  *cu = n;
+  return AR_OK;
+}
+
+// ---- launch-shape heuristic ---------------------------------------------------------------------
+//
+// The MI355X counterpart of the pages' thread-block / cluster sizing against the SM count
+// (flashinfer pull request "update allreduce to match trtllm", Description and Summary).  The
+// pages give no formula; this one is derived from the gfx950 machine: 256 CUs in 8 XCDs,
+// 64-lane waves, at most 1024 threads per block, and a bandwidth-bound kernel that needs many
+// 16-byte loads in flight on every CU.
+
+int cap_grid(int64_t blocks) {
+  if (blocks < 1) return 1;
+  return blocks > INT_MAX ? INT_MAX : static_cast<int>(blocks);
+}
+
+void plan_sum(int W, int64_t n, int dtype, int cu, ar_launch_cfg_t* c) {
+  const int64_t vec = kVecBytes / elem_size(dtype);
+  const int64_t nvec = n / vec;
+  const int64_t waves_full = ceil_div(nvec, 64);
+  int threads = 256;
+  int u = 1;
+  // Enough vectors to give every CU several 256-thread blocks: let each thread own more
+  // vectors per iteration (more independent loads in flight, fewer block launches).
+  if (nvec >= int64_t(cu) * 256 * 8) u = W >= 16 ? 1 : 2;
+  if (nvec >= int64_t(cu) * 256 * 32) u = W >= 16 ? 2 : 4;
+  // Small payloads: single-wave blocks spread the loads over as many CUs as possible.
+  if (waves_full < int64_t(cu) * 4) threads = 64;
+  c->threads_per_block = threads;
+  c->vecs_per_thread = u;
+  c->lanes_per_row = 0;
+  c->rows_per_block = 0;
+  c->grid = cap_grid(ceil_div(nvec, int64_t(threads) * u));
+  c->flat = 1;
+}
+
+void plan_norm(int W, int64_t M, int64_t H, int dtype, int cu, ar_launch_cfg_t* c) {
+  (void)W;
+  const int64_t vec = kVecBytes / elem_size(dtype);
+  const int64_t V = H / vec;
+  int vpt, lanes, threads;
+  if (V <= 32) {
+    // Narrow rows: a power-of-two lane segment per row, several rows per wave.
+    vpt = 1;
+    lanes = static_cast<int>(pow2_ceil(V));
+    const int64_t rows_per_wave = 64 / lanes;
+    threads = (M >= int64_t(cu) * rows_per_wave * 4 * 4) ? 256 : 64;
+  } else {
+    // Wide rows: one row per block, spread over as many threads as the row count allows.
+    // Few rows (decode): a row per CU at most, so use the widest row (most loads in flight).
+    // Many rows: fewer, fatter threads (fewer barriers per byte), several blocks per CU.
+    int64_t target = 1024;
+    if (M > int64_t(cu)) target = 512;
+    if (M > int64_t(cu) * 4) target = 256;
+    vpt = 1;
+    while (vpt < 8 && ceil_div(V, vpt) > target) vpt *= 2;
+    while (vpt < 8 && round_up(ceil_div(V, vpt), 64) > 1024) vpt *= 2;
+    // Rounding the lane count up to whole waves can leave a vector slot that no lane uses
+    // (e.g. 1792 vectors at 8 per thread on 256 lanes); halve the vectors per thread instead.
+    while (vpt > 1 && round_up(ceil_div(V, vpt), 64) * vpt - V >= round_up(ceil_div(V, vpt), 64) &&
+           round_up(ceil_div(V, vpt / 2), 64) <= 1024)
+      vpt /= 2;
+    lanes = static_cast<int>(round_up(ceil_div(V, vpt), 64));
+    threads = lanes;
+  }
+  c->threads_per_block = threads;
+  c->vecs_per_thread = vpt;
+  c->lanes_per_row = lanes;
+  c->rows_per_block = threads / lanes;
+  c->grid = cap_grid(ceil_div(M, c->rows_per_block));
+  c->flat = 0;
+}
+
+// A caller-supplied shape must be well formed and cover the row; then every kernel access is
+// in bounds for any grid.
+int check_cfg(int pattern, int64_t H, int dtype, const ar_launch_cfg_t* c) {
+  if (!c) return AR_ERR_INVALID_ARG;
+  const int t = c->threads_per_block;
+  if (t < 64 || t > arf::kMaxThreads || t % 64 != 0) return AR_ERR_INVALID_ARG;
+  const int u = c->vecs_per_thread;
+  if (u != 1 && u != 2 && u != 4 && u != 8) return AR_ERR_INVALID_ARG;
+  if (c->grid < 1) return AR_ERR_INVALID_ARG;
+  if (pattern == AR_PATTERN_ALLREDUCE) {
+    if (c->flat != 1 || u == 8) return AR_ERR_INVALID_ARG;
+    return AR_OK;
+  }
+  if (c->flat != 0) return AR_ERR_INVALID_ARG;
+  const int L = c->lanes_per_row;
+  const bool seg_ok = (L >= 1 && L <= 64 && is_pow2(L)) || (L > 64 && L % 64 == 0);
+  if (!seg_ok || L > t || t % L != 0) return AR_ERR_INVALID_ARG;
+  if (c->rows_per_block != t / L) return AR_ERR_INVALID_ARG;
+  const int64_t V = H / (kVecBytes / elem_size(dtype));
+  if (int64_t(L) * u < V) return AR_ERR_INVALID_ARG;
+  return AR_OK;
+}
+
+// ---- dispatch -----------------------------------------------------------------------------------
+
+template <int W>
+RankPtrs<W> pack_ptrs(const void* const* inputs) {
+  RankPtrs<W> p;
+  for (int r = 0; r < W; ++r) p.p[r] = static_cast<const u32x4*>(inputs[r]);
+  return p;
+}
+
+template <class T, int W, int U>
+hipError_t launch_sum_u(const void* const* inputs, void* out, int64_t nvec, int tail,
+                        const ar_launch_cfg_t& c, hipStream_t s) {
+  RankPtrs<W> p = pack_ptrs<W>(inputs);
+  u32x4* o = static_cast<u32x4*>(out);
+  void* args[] = {&p, &o, &nvec, &tail};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&arf::ar_sum_kernel<T, W, U>),
+                         dim3(c.grid), dim3(c.threads_per_block), args, 0, s);
+}
+
+template <class T, int W>
+hipError_t launch_sum_w(const void* const* inputs, void* out, int64_t nvec, int tail,
+                        const ar_launch_cfg_t& c, hipStream_t s) {
+  switch (c.vecs_per_thread) {
+    case 1: return launch_sum_u<T, W, 1>(inputs, out, nvec, tail, c, s);
+    case 2: return launch_sum_u<T, W, 2>(inputs, out, nvec, tail, c, s);
+    default: return launch_sum_u<T, W, 4>(inputs, out, nvec, tail, c, s);
+  }
+}
+
+template <class T>
+hipError_t launch_sum_t(const void* const* inputs, int W, void* out, int64_t nvec, int tail,
+                        const ar_launch_cfg_t& c, hipStream_t s) {
+  switch (W) {
+    case 1: return launch_sum_w<T, 1>(inputs, out, nvec, tail, c, s);
+    case 2: return launch_sum_w<T, 2>(inputs, out, nvec, tail, c, s);
+    case 4: return launch_sum_w<T, 4>(inputs, out, nvec, tail, c, s);
+    case 8: return launch_sum_w<T, 8>(inputs, out, nvec, tail, c, s);
+    case 16: return launch_sum_w<T, 16>(inputs, out, nvec, tail, c, s);
+    case 32: return launch_sum_w<T, 32>(inputs, out, nvec, tail, c, s);
+    default: return launch_sum_w<T, 64>(inputs, out, nvec, tail, c, s);
+  }
+}
+
+template <class T, int W, int VPT>
+hipError_t launch_norm_v(const void* const* inputs, const void* residual, const float* gamma,
+                         float eps, void* residual_out, void* norm_out, int64_t M, int64_t H,
+                         const ar_launch_cfg_t& c, hipStream_t s) {
+  RankPtrs<W> p = pack_ptrs<W>(inputs);
+  const u32x4* res = static_cast<const u32x4*>(residual);
+  const f32x4* gam = reinterpret_cast<const f32x4*>(gamma);
+  u32x4* ro = static_cast<u32x4*>(residual_out);
+  u32x4* no = static_cast<u32x4*>(norm_out);
+  int V = static_cast<int>(H / T::kVec);
+  int L = c.lanes_per_row;
+  int R = c.rows_per_block;
+  float count_h = static_cast<float>(H);  // exact: H <= 2^16
+  void* args[] = {&p, &res, &gam, &ro, &no, &M, &V, &L, &R, &eps, &count_h};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&arf::ar_norm_kernel<T, W, VPT>),
+                         dim3(c.grid), dim3(c.threads_per_block), args, 0, s);
+}
+
+template <class T, int W>
+hipError_t launch_norm_w(const void* const* inputs, const void* residual, const float* gamma,
+                         float eps, void* residual_out, void* norm_out, int64_t M, int64_t H,
+                         const ar_launch_cfg_t& c, hipStream_t s) {
+  switch (c.vecs_per_thread) {
+    case 1:
+      return launch_norm_v<T, W, 1>(inputs, residual, gamma, eps, residual_out, norm_out, M, H,
+                                    c, s);
+    case 2:
+      return launch_norm_v<T, W, 2>(inputs, residual, gamma, eps, residual_out, norm_out, M, H,
+                                    c, s);
+    case 4:
+      return launch_norm_v<T, W, 4>(inputs, residual, gamma, eps, residual_out, norm_out, M, H,
+                                    c, s);
+    default:
+      return launch_norm_v<T, W, 8>(inputs, residual, gamma, eps, residual_out, norm_out, M, H,
+                                    c, s);
+  }
+}
+
+template <class T>
+hipError_t launch_norm_t(const void* const* inputs, int W, const void* residual,
+                         const float* gamma, float eps, void* residual_out, void* norm_out,
+                         int64_t M, int64_t H, const ar_launch_cfg_t& c, hipStream_t s) {
+#define AR_NORM_W(w)                                                                        \
+  case w:                                                                                   \
+    return launch_norm_w<T, w>(inputs, residual, gamma, eps, residual_out, norm_out, M, H, \
+                               c, s);
+  switch (W) {
+    AR_NORM_W(1)
+    AR_NORM_W(2)
+    AR_NORM_W(4)
+    AR_NORM_W(8)
+    AR_NORM_W(16)
+    AR_NORM_W(32)
+    default:
+      return launch_norm_w<T, 64>(inputs, residual, gamma, eps, residual_out, norm_out, M, H, c,
+                                  s);
+  }
+#undef AR_NORM_W
+}
+
+// ---- argument validation shared by the entry points ----------------------------------------------
+
+int validate_sum(const void* const* inputs, int W, int64_t M, int64_t H, int dtype,
+                 const void* out) {
+  const int st = check_shape(AR_PATTERN_ALLREDUCE, W, M, H, dtype);
+  if (st != AR_OK) return st;
+  if (M == 0) return AR_OK;
+  if (!inputs || !out) return AR_ERR_INVALID_ARG;
+  for (int r = 0; r < W; ++r)
+    if (!inputs[r]) return AR_ERR_INVALID_ARG;
+  for (int r = 0; r < W; ++r)
+    if (!aligned16(inputs[r])) return AR_ERR_MISALIGNED;
+  if (!aligned16(out)) return AR_ERR_MISALIGNED;
+  const int64_t bytes = M * H * elem_size(dtype);
+  const Range o = range_of(out, bytes);
+  for (int r = 0; r < W; ++r)
+    if (bad_alias_with_input(o, range_of(inputs[r], bytes))) return AR_ERR_ALIAS;
+  return AR_OK;
+}
+
+int validate_norm(const void* const* inputs, int W, int64_t M, int64_t H, int dtype,
+                  const void* residual, const float* gamma, float eps, const void* residual_out,
+                  const void* norm_out) {
+  const int st = check_shape(AR_PATTERN_AR_RESIDUAL_RMSNORM, W, M, H, dtype);
+  if (st != AR_OK) return st;
+  if (!std::isfinite(eps) || eps < 0.0f) return AR_ERR_INVALID_ARG;
+  if (M == 0) return AR_OK;
+  if (!inputs || !residual || !gamma || !residual_out || !norm_out) return AR_ERR_INVALID_ARG;
+  for (int r = 0; r < W; ++r)
+    if (!inputs[r]) return AR_ERR_INVALID_ARG;
+  for (int r = 0; r < W; ++r)
+    if (!aligned16(inputs[r])) return AR_ERR_MISALIGNED;
+  if (!aligned16(residual) || !aligned16(gamma) || !aligned16(residual_out) ||
+      !aligned16(norm_out))
+    return AR_ERR_MISALIGNED;
+  const int64_t bytes = M * H * elem_size(dtype);
+  const Range ro = range_of(residual_out, bytes);
+  const Range no = range_of(norm_out, bytes);
+  const Range g = range_of(gamma, H * int64_t(sizeof(float)));
+  if (overlap(ro, no) || overlap(ro, g) || overlap(no, g)) return AR_ERR_ALIAS;
+  const Range res = range_of(residual, bytes);
+  if (bad_alias_with_input(ro, res) || bad_alias_with_input(no, res)) return AR_ERR_ALIAS;
+  for (int r = 0; r < W; ++r) {
+    const Range in = range_of(inputs[r], bytes);
+    if (bad_alias_with_input(ro, in) || bad_alias_with_input(no, in)) return AR_ERR_ALIAS;
+  }
+  return AR_OK;
+}
+
+int run_sum(const void* const* inputs, int W, int64_t M, int64_t H, int dtype, void* out,
+            void* stream, const ar_launch_cfg_t* user_cfg) {
+  int st = validate_sum(inputs, W, M, H, dtype, out);
+  if (st != AR_OK) return st;
+  if (user_cfg) {
+    st = check_cfg(AR_PATTERN_ALLREDUCE, H, dtype, user_cfg);
+    if (st != AR_OK) return st;
+  }
+  if (M == 0) return AR_OK;
+  ar_launch_cfg_t cfg;
+  if (user_cfg) {
+    cfg = *user_cfg;
+  } else {
+    int cu = 0;
+    st = query_cu_count(&cu);
+    if (st != AR_OK) return st;
+    plan_sum(W, M * H, dtype, cu, &cfg);
+  }
+  const int64_t vec = kVecBytes / elem_size(dtype);
+  const int64_t n = M * H;
+  const int64_t nvec = n / vec;
+  const int tail = static_cast<int>(n - nvec * vec);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  switch (dtype) {
+    case AR_DTYPE_FP32: e = launch_sum_t<F32>(inputs, W, out, nvec, tail, cfg, s); break;
+    case AR_DTYPE_FP16: e = launch_sum_t<F16>(inputs, W, out, nvec, tail, cfg, s); break;
+    default: e = launch_sum_t<Bf16>(inputs, W, out, nvec, tail, cfg, s); break;
+  }
+  return e == hipSuccess ? AR_OK : AR_ERR_LAUNCH;
+}
+
+int run_norm(const void* const* inputs, int W, int64_t M, int64_t H, int dtype,
+             const void* residual, const float* gamma, float eps, void* residual_out,
+             void* norm_out, void* stream, const ar_launch_cfg_t* user_cfg) {
+  int st = validate_norm(inputs, W, M, H, dtype, residual, gamma, eps, residual_out, norm_out);
+  if (st != AR_OK) return st;
+  if (user_cfg) {
+    st = check_cfg(AR_PATTERN_AR_RESIDUAL_RMSNORM, H, dtype, user_cfg);
+    if (st != AR_OK) return st;
+  }
+  if (M == 0) return AR_OK;
+  ar_launch_cfg_t cfg;
+  if (user_cfg) {
+    cfg = *user_cfg;
+  } else {
+    int cu = 0;
+    st = query_cu_count(&cu);
+    if (st != AR_OK) return st;
+    plan_norm(W, M, H, dtype, cu, &cfg);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  switch (dtype) {
+    case AR_DTYPE_FP32:
+      e = launch_norm_t<F32>(inputs, W, residual, gamma, eps, residual_out, norm_out, M, H, cfg,
+                             s);
+      break;
+    case AR_DTYPE_FP16:
+      e = launch_norm_t<F16>(inputs, W, residual, gamma, eps, residual_out, norm_out, M, H, cfg,
+                             s);
+      break;
+    default:
+      e = launch_norm_t<Bf16>(inputs, W, residual, gamma, eps, residual_out, norm_out, M, H,
+                              cfg, s);
+      break;
+  }
+  return e == hipSuccess ? AR_OK : AR_ERR_LAUNCH;
+}
+
+}  // namespace
+
+// ---- C ABI ----------------------------------------------------------------------------------------
+
+extern "C" {
+
+int ar_sum(const void* const* inputs, int W, int64_t M, int64_t H, int dtype, void* out,
+           void* stream) {
+  return run_sum(inputs, W, M, H, dtype, out, stream, nullptr);
+}
+
+int ar_sum_with_config(const void* const* inputs, int W, int64_t M, int64_t H, int dtype,
+                       void* out, void* stream, const ar_launch_cfg_t* cfg) {
+  if (!cfg) return AR_ERR_INVALID_ARG;
+  return run_sum(inputs, W, M, H, dtype, out, stream, cfg);
+}
+
+int ar_residual_rmsnorm(const void* const* inputs, int W, int64_t M, int64_t H, int dtype,
+                        const void* residual, const float* gamma, float eps, void* residual_out,
+                        void* norm_out, void* stream) {
+  return run_norm(inputs, W, M, H, dtype, residual, gamma, eps, residual_out, norm_out, stream,
+                  nullptr);
+}
+
+int ar_residual_rmsnorm_with_config(const void* const* inputs, int W, int64_t M, int64_t H,
+                                    int dtype, const void* residual, const float* gamma,
+                                    float eps, void* residual_out, void* norm_out, void* stream,
+                                    const ar_launch_cfg_t* cfg) {
+  if (!cfg) return AR_ERR_INVALID_ARG;
+  return run_norm(inputs, W, M, H, dtype, residual, gamma, eps, residual_out, norm_out, stream,
+                  cfg);
+}
+
+int ar_supports(int pattern, int W, int64_t M, int64_t H, int dtype) {
+  return check_shape(pattern, W, M, H, dtype);
+}
+
+int ar_launch_config(int pattern, int W, int64_t M, int64_t H, int dtype, int cu_count,
+                     ar_launch_cfg_t* cfg) {
+  if (!cfg) return AR_ERR_INVALID_ARG;
+  const int st = check_shape(pattern, W, M, H, dtype);
+  if (st != AR_OK) return st;
+  int cu = cu_count;
+  if (cu <= 0) {
+    const int q = query_cu_count(&cu);
+    if (q != AR_OK) return q;
+  }
+  if (pattern == AR_PATTERN_ALLREDUCE) {
+    plan_sum(W, M * H, dtype, cu, cfg);
+  } else {
+    plan_norm(W, M, H, dtype, cu, cfg);
+  }
+  return AR_OK;
+}
+
+const char* ar_status_string(int status) {
+  switch (status) {
+    case AR_OK: return "ok";
+    case AR_ERR_INVALID_ARG: return "invalid argument";
+    case AR_ERR_UNSUPPORTED: return "unsupported shape or world size";
+    case AR_ERR_MISALIGNED: return "pointer not 16-byte aligned";
+    case AR_ERR_ALIAS: return "output buffers overlap";
+    case AR_ERR_LAUNCH: return "kernel launch failed";
+    case AR_ERR_DEVICE: return "no usable HIP device";
+    default: return "unknown status";
+  }
+}
+
+int ar_device_cu_count(int* cu_count) {
+  if (!cu_count) return AR_ERR_INVALID_ARG;
+  return query_cu_count(cu_count);
+}
+
+}  // extern "C"

@@ -1,0 +1,383 @@
+// ar_kernels.hpp -- gfx950 device code of the fused all-reduce-sum (+ residual + RMSNorm) core.
+//
+// Two kernels, templated on the element type T, the number of partials W and the number of
+// 16-byte vectors per thread:
+//
+//   ar_sum_kernel   kAllReduce.  A flat grid-stride walk over the [M, H] tensors viewed as
+//                   16-byte vectors.  Each thread issues the W loads of its vectors before it
+//                   starts the binary32 chain, so a wave keeps W x U x 1 KiB of reads in flight.
+//   ar_norm_kernel  kARResidualRMSNorm.  `lanes_per_row` consecutive threads own one row; each
+//                   holds its vectors' rounded residual_out values in registers between the sum
+//                   and the norm, so every byte is read once and written once.  The per-row sum
+//                   of squares is reduced with DPP lane moves and a swizzle inside a wave, then
+//                   across waves through LDS with one barrier per row (LDS slots alternate
+//                   between two banks so consecutive rows need no second barrier).
+//
+// The fusion patterns are the ones named in the tokenspeed pull request "perf(comm): route
+// generic MNNVL AR patterns to upstream flashinfer" (Summary).  The peers' buffers are passed as
+// a by-value pointer array in the kernel arguments (they land in scalar registers), the AMD
+// counterpart of the GPU-side pointer array in the flashinfer pull request "Optimizations for
+// TRTLLM MNNVL Allreduce" (Description).
+//
+// Arithmetic contract (identical for every launch shape):
+//  * rank sum: binary32, rank order 0..W-1, one round-to-nearest-even per add, started from
+//    -0.0f (-0 + x == x for every x, so this equals seeding with x_0 and keeps -0 sums);
+//  * residual: added after the W partials; one rounding to T (v_cvt_pk_bf16_f32 /
+//    v_cvt_pk_f16_f32 round to nearest even in the default mode);
+//  * norm: computed from the rounded residual_out; no flush of subnormals.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace arf {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kMaxThreads = 1024;
+constexpr int kMaxWavesPerBlock = kMaxThreads / 64;
+
+template <int W>
+struct RankPtrs {
+  const u32x4* p[W];
+};
+
+// ---- element types: a 16-byte vector <-> binary32 lanes ------------------------------------
+
+struct Bf16 {
+  static constexpr int kVec = 8;
+  __device__ static inline void widen(u32x4 v, float (&f)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(v[i] << 16);
+      f[2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
+    }
+  }
+  __device__ static inline u32x4 narrow(const float (&f)[8]) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bf16x2 h = __builtin_convertvector(f32x2{f[2 * i], f[2 * i + 1]}, bf16x2);
+      r[i] = __builtin_bit_cast(uint32_t, h);
+    }
+    return r;
+  }
+  __device__ static inline float widen1(const void* p, int64_t i) {
+    return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16);
+  }
+  __device__ static inline void store1(void* p, int64_t i, float x) {
+    static_cast<__bf16*>(p)[i] = static_cast<__bf16>(x);
+  }
+};
+
+struct F16 {
+  static constexpr int kVec = 8;
+  __device__ static inline void widen(u32x4 v, float (&f)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // The word goes through a scalar first: this compiler folds __builtin_bit_cast of a
+      // vector subscript (v[i]) to element 0 for every i.
+      const uint32_t word = v[i];
+      const f32x2 w = __builtin_convertvector(__builtin_bit_cast(f16x2, word), f32x2);
+      f[2 * i] = w.x;
+      f[2 * i + 1] = w.y;
+    }
+  }
+  __device__ static inline u32x4 narrow(const float (&f)[8]) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f16x2 h = __builtin_convertvector(f32x2{f[2 * i], f[2 * i + 1]}, f16x2);
+      r[i] = __builtin_bit_cast(uint32_t, h);
+    }
+    return r;
+  }
+  __device__ static inline float widen1(const void* p, int64_t i) {
+    return static_cast<float>(static_cast<const _Float16*>(p)[i]);
+  }
+  __device__ static inline void store1(void* p, int64_t i, float x) {
+    static_cast<_Float16*>(p)[i] = static_cast<_Float16>(x);
+  }
+};
+
+struct F32 {
+  static constexpr int kVec = 4;
+  __device__ static inline void widen(u32x4 v, float (&f)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v[i]);
+  }
+  __device__ static inline u32x4 narrow(const float (&f)[4]) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = __float_as_uint(f[i]);
+    return r;
+  }
+  __device__ static inline float widen1(const void* p, int64_t i) {
+    return static_cast<const float*>(p)[i];
+  }
+  __device__ static inline void store1(void* p, int64_t i, float x) {
+    static_cast<float*>(p)[i] = x;
+  }
+};
+
+// ---- wave-level reduction -------------------------------------------------------------------
+
+// x + (x of the lane selected by a DPP control).  All four controls used here stay inside a
+// 16-lane DPP row, so every source lane exists.
+template <int kCtrl>
+__device__ inline float dpp_add(float x) {
+  const int y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false);
+  return x + __int_as_float(y);
+}
+
+// Sum of x over aligned groups of min(seg, 64) lanes; seg is a power of two <= 64 or a multiple
+// of 64, uniform across the wave, and every lane of the wave is active.  Each step adds a lane
+// to its partner under an involution, so every lane of a group ends with the same value.
+__device__ inline float segment_sum(float x, int seg) {
+  if (seg >= 2) x = dpp_add<0xB1>(x);    // quad_perm [1,0,3,2]: lane ^ 1
+  if (seg >= 4) x = dpp_add<0x4E>(x);    // quad_perm [2,3,0,1]: lane ^ 2
+  if (seg >= 8) x = dpp_add<0x141>(x);   // row_half_mirror: lane i <-> 7 - i within 8
+  if (seg >= 16) x = dpp_add<0x140>(x);  // row_mirror: lane i <-> 15 - i within 16
+  if (seg >= 32) {                       // ds_swizzle bit mode, xor 0x10: lane ^ 16 within 32
+    x = x + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+  }
+  if (seg >= 64) {                       // halves of the wave, lane 0 + lane 32, uniform
+    x = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0)) +
+        __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+  }
+  return x;
+}
+
+// ---- rank batching ----------------------------------------------------------------------------
+//
+// A thread sums W ranks for each of its N vectors.  Left alone, the compiler hoists every load
+// of the unrolled rank loop to the top, which for large W x N needs more than the 128 VGPRs a
+// 1024-thread block allows and spills to scratch.  The rank loop is therefore cut into batches
+// of kBatch ranks (at most 8 or 16 16-byte loads in flight per thread) with a compiler fence
+// after each batch: an empty asm statement that reads and writes every accumulator and clobbers
+// memory, so the batch's adds stay before it and the next batch's loads stay after it.  It
+// emits no instruction.  Latency is hidden by the other waves on the SIMD.
+
+template <int W, int N, int kMaxLoads>
+constexpr int rank_batch() {
+  int b = kMaxLoads / N;
+  if (b < 1) b = 1;
+  return b > W ? W : b;
+}
+
+template <int N, int K>
+__device__ inline void batch_fence(float (&acc)[N][K]) {
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+#pragma unroll
+    for (int e = 0; e < K; ++e) asm volatile("" : "+v"(acc[k][e]) : : "memory");
+  }
+}
+
+// acc[k] = -0 + x_0[k] + x_1[k] + ... + x_{W-1}[k] for the N vectors at offsets off[k].
+template <class T, int W, int N, int kMaxLoads = (N * T::kVec >= 32 ? 8 : 16)>
+__device__ inline void rank_sum(const RankPtrs<W>& in, const int64_t (&off)[N],
+                                float (&acc)[N][T::kVec]) {
+  constexpr int kBatch = rank_batch<W, N, kMaxLoads>();
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+#pragma unroll
+    for (int e = 0; e < T::kVec; ++e) acc[k][e] = -0.0f;
+  }
+#pragma unroll
+  for (int r0 = 0; r0 < W; r0 += kBatch) {
+#pragma unroll
+    for (int r = r0; r < r0 + kBatch && r < W; ++r) {
+#pragma unroll
+      for (int k = 0; k < N; ++k) {
+        float x[T::kVec];
+        T::widen(in.p[r][off[k]], x);
+#pragma unroll
+        for (int e = 0; e < T::kVec; ++e) acc[k][e] = acc[k][e] + x[e];
+      }
+    }
+    if (kBatch < W && r0 + kBatch < W) batch_fence(acc);
+  }
+}
+
+// ---- kAllReduce -----------------------------------------------------------------------------
+
+// out = RN_T(x_0 + ... + x_{W-1}) over n elements: nvec full 16-byte vectors, then a tail of
+// fewer than one vector handled element by element by block 0.
+template <class T, int W, int U>
+__global__ __launch_bounds__(kMaxThreads) void ar_sum_kernel(RankPtrs<W> in, u32x4* out,
+                                                             int64_t nvec, int tail) {
+  constexpr int kVec = T::kVec;
+  const int64_t bdim = blockDim.x;
+  const int64_t step = static_cast<int64_t>(gridDim.x) * bdim * U;
+  for (int64_t base = static_cast<int64_t>(blockIdx.x) * bdim * U + threadIdx.x; base < nvec;
+       base += step) {
+    int64_t off[U];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      off[u] = base + u * bdim;
+      ok[u] = off[u] < nvec;
+      if (!ok[u]) off[u] = base;  // in bounds; the value is discarded
+    }
+    float acc[U][kVec];
+    rank_sum<T, W, U>(in, off, acc);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (ok[u]) out[off[u]] = T::narrow(acc[u]);
+    }
+  }
+  if (tail > 0 && blockIdx.x == 0 && static_cast<int>(threadIdx.x) < tail) {
+    const int64_t i = nvec * kVec + threadIdx.x;
+    float a = -0.0f;
+#pragma unroll
+    for (int r = 0; r < W; ++r) a = a + T::widen1(in.p[r], i);
+    T::store1(out, i, a);
+  }
+}
+
+// ---- kARResidualRMSNorm ---------------------------------------------------------------------
+
+// acc += widen(v), element by element (one binary32 add each).
+template <class T>
+__device__ inline void accumulate(float (&acc)[T::kVec], u32x4 v) {
+  float x[T::kVec];
+  T::widen(v, x);
+#pragma unroll
+  for (int e = 0; e < T::kVec; ++e) acc[e] = acc[e] + x[e];
+}
+
+// The kVec gamma values of element vector `vec` (gamma is binary32 [H], 16-byte aligned).
+template <int kVec>
+__device__ inline void load_gamma(const f32x4* gamma, int vec, float (&g)[kVec]) {
+#pragma unroll
+  for (int j = 0; j < kVec / 4; ++j) {
+    const f32x4 q = gamma[static_cast<int64_t>(vec) * (kVec / 4) + j];
+    g[4 * j + 0] = q.x;
+    g[4 * j + 1] = q.y;
+    g[4 * j + 2] = q.z;
+    g[4 * j + 3] = q.w;
+  }
+}
+
+// One row = V vectors of 16 bytes.  Thread t of a block serves row slot t / L (R slots per
+// block) and, within the row, vectors lane + k * L for k < VPT.  L * VPT >= V.
+template <class T, int W, int VPT>
+__global__ __launch_bounds__(kMaxThreads) void ar_norm_kernel(
+    RankPtrs<W> in, const u32x4* residual, const f32x4* gamma, u32x4* residual_out,
+    u32x4* norm_out, int64_t M, int V, int L, int R, float eps, float count_h) {
+  constexpr int kVec = T::kVec;
+  __shared__ float red[2][kMaxWavesPerBlock];
+
+  const int tid = threadIdx.x;
+  const int slot = tid / L;
+  const int lane = tid - slot * L;
+  const int wave = tid >> 6;
+  const int64_t groups = (M + R - 1) / R;
+
+  int idx[VPT];
+  bool col_ok[VPT];
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int i = lane + k * L;
+    col_ok[k] = i < V;
+    idx[k] = col_ok[k] ? i : 0;
+  }
+
+  // gamma does not depend on the row.  With few vectors per thread this thread's slice is
+  // loaded once and kept in registers; with many it is re-read (from L2) in the epilogue.
+  constexpr bool kKeepGamma = VPT <= 2;
+  float gam[kKeepGamma ? VPT : 1][kVec];
+  if constexpr (kKeepGamma) {
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) load_gamma(gamma, idx[k], gam[k]);
+  }
+
+  int bank = 0;
+  for (int64_t grp = blockIdx.x; grp < groups; grp += gridDim.x) {
+    const int64_t m = grp * R + slot;
+    const bool row_ok = m < M;
+    const int64_t row_base = (row_ok ? m : 0) * static_cast<int64_t>(V);
+
+    // Sum of the W partials and the residual, binary32 in rank order, rounded once to T.
+    int64_t off[VPT];
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) off[k] = row_base + idx[k];
+    u32x4 rounded[VPT];
+    if constexpr (VPT <= 2) {
+      // All vectors' chains together: the most independent loads per batch.
+      float acc[VPT][kVec];
+      rank_sum<T, W, VPT>(in, off, acc);
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) {
+        accumulate<T>(acc[k], residual[off[k]]);
+        rounded[k] = T::narrow(acc[k]);
+      }
+    } else {
+      // One vector's chain at a time keeps the live accumulators to one vector.
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) {
+        const int64_t off_k[1] = {off[k]};
+        float acc[1][kVec];
+        rank_sum<T, W, 1, 8>(in, off_k, acc);
+        accumulate<T>(acc[0], residual[off[k]]);
+        rounded[k] = T::narrow(acc[0]);
+        batch_fence(acc);
+      }
+    }
+    float ss = 0.0f;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      if (row_ok && col_ok[k]) {
+        residual_out[off[k]] = rounded[k];
+        float v[kVec];
+        T::widen(rounded[k], v);
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) ss += v[e] * v[e];
+      }
+    }
+
+    // Row sum of squares: inside the wave, then across the row's waves through LDS.
+    ss = segment_sum(ss, L);
+    if (L > 64) {
+      if ((tid & 63) == 0) red[bank][wave] = ss;
+      __syncthreads();
+      const int waves_per_row = L >> 6;
+      const int w0 = slot * waves_per_row;
+      float t = red[bank][w0];
+      for (int j = 1; j < waves_per_row; ++j) t += red[bank][w0 + j];
+      ss = t;
+      bank ^= 1;
+    }
+    const float rstd = rsqrtf(ss / count_h + eps);
+
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      if (row_ok && col_ok[k]) {
+        float v[kVec];
+        T::widen(rounded[k], v);
+        float g[kVec];
+        if constexpr (kKeepGamma) {
+#pragma unroll
+          for (int e = 0; e < kVec; ++e) g[e] = gam[k][e];
+        } else {
+          // Opaque index: keeps the compiler from hoisting these loop-invariant loads out of
+          // the row loop, where all VPT x kVec values would stay live in registers.
+          int gi = idx[k];
+          asm volatile("" : "+v"(gi));
+          load_gamma(gamma, gi, g);
+        }
+        float y[kVec];
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) y[e] = (v[e] * rstd) * g[e];
+        norm_out[off[k]] = T::narrow(y);
+      }
+    }
+  }
+}
+
+}  // namespace arf

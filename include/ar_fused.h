@@ -1,0 +1,159 @@
+/*
+ * ar_fused.h -- C ABI of the MI355X (gfx950) fused all-reduce-sum (+ residual + RMSNorm) core.
+ *
+ * The library computes one GPU's share of a one-shot all-reduce: the element-wise sum of W
+ * per-rank partial tensors [M, H] that are all readable from this GPU, optionally followed by a
+ * residual add and RMSNorm, in one kernel launch.  The two operations are the fusion patterns
+ * "kAllReduce" and "kARResidualRMSNorm" named in the tokenspeed pull request "perf(comm): route
+ * generic MNNVL AR patterns to upstream flashinfer" (Summary, Routing).
+ *
+ * Arithmetic (the same for every launch shape):
+ *   a            = x_0 + x_1 + ... + x_{W-1}        binary32, in rank order 0..W-1, one
+ *                                                   round-to-nearest-even per add, seeded with
+ *                                                   x_0 (a sum of -0 stays -0)
+ *   ar_sum:        out = RN_T(a)
+ *   ar_residual_rmsnorm:
+ *                  a            = a + residual      (the residual is the last term)
+ *                  residual_out = RN_T(a)
+ *                  v            = residual_out, widened exactly to binary32
+ *                  norm_out     = RN_T( v * rsqrt(mean_i(v_i^2) + eps) * gamma )
+ * out and residual_out are bit-identical to that definition; norm_out is computed in binary32
+ * (sum of squares reduced in a fixed tree order) and is within one unit in the last place of T
+ * of the same expression evaluated exactly.  RMSNorm is the textbook form (mean over the whole
+ * row, eps inside the square root, gamma after normalising, no bias); the pages name the
+ * pattern but give no formula.  Subnormals are kept (no flush to zero); T overflow gives inf.
+ *
+ * Layout: every [M, H] tensor is row-major and contiguous (row stride H elements), one
+ * allocation per partial.  gamma is binary32 [H] for every element type.
+ *
+ * Ownership: the caller owns every buffer.  `inputs` is a HOST array of W DEVICE pointers; it is
+ * read during the call and not retained.  The library allocates no device memory, keeps no
+ * workspace and retains no pointer, so calls are safe to capture in a hipGraph and replay.  The
+ * only state is a per-device cache of the compute-unit count.
+ *
+ * Streams: `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue one kernel and
+ * return without synchronising; the return code reports argument validation and the launch only.
+ * Device faults surface on the stream as usual.
+ *
+ * Errors: every entry point returns an ar_status_t.  On any non-zero status nothing was launched
+ * and no output byte was written.  Rejections follow the pages' runtime rejection of unsupported
+ * world sizes with a caller-side fallback (vLLM pull request "[Perf] Tune FlashInfer all-reduce
+ * selection on SM103", Scope and Tests: world size 12 is rejected, {2, 4, 8, 16, 32, 64} are
+ * supported); W = 1 is accepted as well.
+ */
+#ifndef AR_FUSED_H
+#define AR_FUSED_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type T of the partials, residual and outputs. */
+typedef enum {
+  AR_DTYPE_FP32 = 0, /* binary32 */
+  AR_DTYPE_FP16 = 1, /* binary16 */
+  AR_DTYPE_BF16 = 2  /* bfloat16 */
+} ar_dtype_t;
+
+/* Fusion pattern (for ar_supports / ar_launch_config). */
+typedef enum {
+  AR_PATTERN_ALLREDUCE = 0,             /* kAllReduce: out = sum */
+  AR_PATTERN_AR_RESIDUAL_RMSNORM = 1    /* kARResidualRMSNorm */
+} ar_pattern_t;
+
+typedef enum {
+  AR_OK = 0,
+  AR_ERR_INVALID_ARG = 1, /* null pointer, W < 1, M < 0, H < 1, bad dtype/pattern, bad eps,
+                             malformed launch config */
+  AR_ERR_UNSUPPORTED = 2, /* W not in {1,2,4,8,16,32,64}; H not a multiple of 16/sizeof(T)
+                             (norm pattern) or H above AR_MAX_H_16BIT / AR_MAX_H_FP32 */
+  AR_ERR_MISALIGNED = 3,  /* a tensor pointer is not 16-byte aligned (gamma: 16 bytes too) */
+  AR_ERR_ALIAS = 4,       /* outputs overlap each other, gamma, or partially overlap an input */
+  AR_ERR_LAUNCH = 5,      /* the HIP launch itself failed */
+  AR_ERR_DEVICE = 6       /* no usable HIP device (device query failed) */
+} ar_status_t;
+
+/* Largest hidden size accepted by the residual+RMSNorm pattern (a row is held in registers
+ * by at most 1024 threads x 8 vectors of 16 bytes). */
+#define AR_MAX_H_16BIT 65536
+#define AR_MAX_H_FP32 32768
+/* Largest number of partials. */
+#define AR_MAX_W 64
+
+/* Launch shape.  Produced by ar_launch_config; accepted by the *_with_config entry points for
+ * tuning (the kernel and its arithmetic are the same for every valid shape).
+ *   threads_per_block : multiple of 64, 64..1024
+ *   vecs_per_thread   : 16-byte vectors each thread handles per row (norm: 1, 2, 4 or 8) or
+ *                       per grid-stride iteration (sum: 1, 2 or 4)
+ *   lanes_per_row     : norm pattern only: threads that share one row; a power of two <= 64
+ *                       or a multiple of 64; threads_per_block % lanes_per_row == 0 and
+ *                       lanes_per_row * vecs_per_thread >= H / (16 / sizeof(T))
+ *   rows_per_block    : norm pattern only: threads_per_block / lanes_per_row
+ *   grid              : number of blocks (>= 1); blocks loop over the work with a grid stride
+ *   flat              : 1 for the sum pattern (flat vector decomposition), 0 for the norm */
+typedef struct {
+  int32_t threads_per_block;
+  int32_t vecs_per_thread;
+  int32_t lanes_per_row;
+  int32_t rows_per_block;
+  int32_t grid;
+  int32_t flat;
+} ar_launch_cfg_t;
+
+/* kAllReduce.  out[m, i] = RN_T(x_0[m, i] + ... + x_{W-1}[m, i]).
+ *   inputs : host array of W device pointers to [M, H] tensors of type `dtype`
+ *   out    : device [M, H]; may be exactly one of the inputs (in place), must not partially
+ *            overlap any input
+ * M = 0 returns AR_OK without launching.  Any M * H is accepted (a tail shorter than one
+ * 16-byte vector is handled element-wise). */
+int ar_sum(const void* const* inputs, int W, int64_t M, int64_t H, int dtype, void* out,
+           void* stream);
+
+/* kARResidualRMSNorm.
+ *   inputs       : host array of W device pointers to [M, H] tensors of type `dtype`
+ *   residual     : device [M, H] of type `dtype`
+ *   gamma        : device [H] binary32
+ *   eps          : finite, >= 0
+ *   residual_out : device [M, H]; may be exactly `residual` or an input (in place)
+ *   norm_out     : device [M, H]; may be exactly `residual` or an input; must not overlap
+ *                  residual_out or gamma
+ * H must be a multiple of 16 / sizeof(T) (8 for 16-bit types, 4 for binary32).
+ * M = 0 returns AR_OK without launching. */
+int ar_residual_rmsnorm(const void* const* inputs, int W, int64_t M, int64_t H, int dtype,
+                        const void* residual, const float* gamma, float eps, void* residual_out,
+                        void* norm_out, void* stream);
+
+/* Shape-level support check, no device access: AR_OK if the pattern accepts (W, M, H, dtype),
+ * else the status the entry point would return.  Lets a caller pick its fallback first. */
+int ar_supports(int pattern, int W, int64_t M, int64_t H, int dtype);
+
+/* Launch-shape heuristic: maps (pattern, W, M, H, dtype) and the compute-unit count to a launch
+ * shape -- the MI355X counterpart of the thread-block / cluster sizing against the SM count in
+ * the flashinfer pull request "update allreduce to match trtllm" (Description, Summary).
+ *   cu_count : compute units to plan for; <= 0 queries the current HIP device (cached).
+ * Pure host arithmetic when cu_count > 0.  Returns AR_OK and fills *cfg, or an error status. */
+int ar_launch_config(int pattern, int W, int64_t M, int64_t H, int dtype, int cu_count,
+                     ar_launch_cfg_t* cfg);
+
+/* Same as ar_sum / ar_residual_rmsnorm with an explicit launch shape (tuning and tests).
+ * A shape that is malformed or does not cover the row returns AR_ERR_INVALID_ARG. */
+int ar_sum_with_config(const void* const* inputs, int W, int64_t M, int64_t H, int dtype,
+                       void* out, void* stream, const ar_launch_cfg_t* cfg);
+int ar_residual_rmsnorm_with_config(const void* const* inputs, int W, int64_t M, int64_t H,
+                                    int dtype, const void* residual, const float* gamma,
+                                    float eps, void* residual_out, void* norm_out, void* stream,
+                                    const ar_launch_cfg_t* cfg);
+
+/* Static, human-readable name of a status code ("unknown status" for anything else). */
+const char* ar_status_string(int status);
+
+/* Compute units of the current HIP device (cached per device).  AR_OK or AR_ERR_DEVICE. */
+int ar_device_cu_count(int* cu_count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AR_FUSED_H */

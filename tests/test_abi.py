@@ -1,0 +1,167 @@
+"""Host-only checks of the C ABI library: it loads, exports every function include/ar_fused.h
+declares, and its host logic (shape checks, status strings, the launch-shape heuristic and
+argument validation that rejects before any device access) behaves as documented.  No call here
+reaches the device: every entry-point call is one the library must reject during validation.
+"""
+import ctypes
+import itertools
+
+import pytest
+
+import all_reduce_residual_amd as ar
+
+BF16, FP16, FP32 = ar.DTYPE_BF16, ar.DTYPE_FP16, ar.DTYPE_FP32
+RMS, SUM = ar.PATTERN_AR_RESIDUAL_RMSNORM, ar.PATTERN_ALLREDUCE
+
+
+@pytest.fixture(scope="module")
+def L():
+    return ar.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = ar.header_functions()
+    assert set(names) == {"ar_sum", "ar_residual_rmsnorm", "ar_supports", "ar_launch_config",
+                          "ar_sum_with_config", "ar_residual_rmsnorm_with_config",
+                          "ar_status_string", "ar_device_cu_count"}
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    seen = set()
+    for code in range(7):
+        s = ar.status_string(code)
+        assert s and s != "unknown status"
+        seen.add(s)
+    assert len(seen) == 7
+    assert ar.status_string(99) == "unknown status"
+
+
+def test_supports_world_sizes():
+    for W in range(0, 70):
+        st = ar.ar_supports(RMS, W, 4, 256, BF16)
+        if W < 1:
+            assert st == ar.AR_ERR_INVALID_ARG
+        elif W in ar.SUPPORTED_W:
+            assert st == ar.AR_OK, W
+        else:
+            assert st == ar.AR_ERR_UNSUPPORTED, W
+    assert ar.ar_supports(SUM, 12, 4, 256, BF16) == ar.AR_ERR_UNSUPPORTED
+
+
+def test_supports_shapes():
+    assert ar.ar_supports(RMS, 8, 0, 7168, BF16) == ar.AR_OK
+    assert ar.ar_supports(RMS, 8, -1, 7168, BF16) == ar.AR_ERR_INVALID_ARG
+    assert ar.ar_supports(RMS, 8, 4, 0, BF16) == ar.AR_ERR_INVALID_ARG
+    assert ar.ar_supports(RMS, 8, 4, 7168, 3) == ar.AR_ERR_INVALID_ARG
+    assert ar.ar_supports(7, 8, 4, 7168, BF16) == ar.AR_ERR_INVALID_ARG
+    assert ar.ar_supports(RMS, 8, 4, 7170, BF16) == ar.AR_ERR_UNSUPPORTED   # not a multiple of 8
+    assert ar.ar_supports(SUM, 8, 4, 7170, BF16) == ar.AR_OK                # any size for sum
+    assert ar.ar_supports(RMS, 8, 4, 1020, FP32) == ar.AR_OK                # multiple of 4
+    assert ar.ar_supports(RMS, 8, 4, 65536, BF16) == ar.AR_OK
+    assert ar.ar_supports(RMS, 8, 4, 65544, BF16) == ar.AR_ERR_UNSUPPORTED
+    assert ar.ar_supports(RMS, 8, 4, 32768, FP32) == ar.AR_OK
+    assert ar.ar_supports(RMS, 8, 4, 32772, FP32) == ar.AR_ERR_UNSUPPORTED
+    assert ar.ar_supports(SUM, 8, 1 << 40, 1 << 30, BF16) == ar.AR_ERR_UNSUPPORTED
+
+
+SHAPES = list(itertools.product(
+    [1, 2, 4, 8, 16, 32, 64], [1, 3, 4, 8, 31, 32, 33, 64, 128, 255, 256, 257, 512, 2048, 5120,
+                               65536],
+    [8, 64, 256, 520, 1016, 4096, 7168, 8192, 16384, 65536], [BF16, FP16, FP32]))
+
+
+def _vec(dtype):
+    return 4 if dtype == FP32 else 8
+
+
+@pytest.mark.parametrize("cu", [256, 80, 304])
+def test_launch_config_invariants(cu):
+    for W, M, H, dt in SHAPES:
+        for pat in (SUM, RMS):
+            if ar.ar_supports(pat, W, M, H, dt) != ar.AR_OK:
+                continue
+            c = ar.ar_launch_config(pat, W, M, H, dt, cu_count=cu)
+            assert c == ar.ar_launch_config(pat, W, M, H, dt, cu_count=cu)   # deterministic
+            t = c["threads_per_block"]
+            assert 64 <= t <= 1024 and t % 64 == 0, c
+            assert c["grid"] >= 1
+            if pat == SUM:
+                assert c["flat"] == 1 and c["vecs_per_thread"] in (1, 2, 4)
+                nvec = M * H // _vec(dt)
+                assert c["grid"] * t * c["vecs_per_thread"] >= nvec or c["grid"] == 2 ** 31 - 1
+            else:
+                L_, vpt, R = c["lanes_per_row"], c["vecs_per_thread"], c["rows_per_block"]
+                assert c["flat"] == 0 and vpt in (1, 2, 4, 8)
+                assert (L_ <= 64 and L_ & (L_ - 1) == 0) or L_ % 64 == 0
+                assert t % L_ == 0 and R == t // L_
+                assert L_ * vpt >= H // _vec(dt), c                     # row covered
+                assert c["grid"] * R >= M                              # rows covered
+                # No thread is idle for a whole row when the row fits the block.
+                assert L_ * vpt - H // _vec(dt) < L_ or L_ <= 64, c
+
+
+def test_launch_config_headline_shapes():
+    """The wide-hidden decode/prefill sweep (W=8, H=7168 bf16) keeps every CU busy as M grows."""
+    for M in (1, 8, 32, 64, 128, 512, 2048):
+        c = ar.ar_launch_config(RMS, 8, M, 7168, BF16, cu_count=256)
+        assert c["grid"] == M and c["rows_per_block"] == 1
+        assert c["lanes_per_row"] * c["vecs_per_thread"] >= 896
+
+
+def test_launch_config_rejects():
+    with pytest.raises(ar.ArError) as e:
+        ar.ar_launch_config(RMS, 12, 4, 256, BF16, cu_count=256)
+    assert e.value.status == ar.AR_ERR_UNSUPPORTED
+
+
+def _ptrs(vals):
+    return (ctypes.c_void_p * len(vals))(*vals)
+
+
+def test_validation_rejects_before_device_access(L):
+    """Every call below is invalid and must be rejected by host validation (fake pointers are
+    never dereferenced)."""
+    p = [0x10000 * (i + 1) for i in range(16)]   # 16-byte aligned, never touched
+    out = 0x900000
+    # World size 12.
+    assert L.ar_sum(_ptrs(p[:12]), 12, 4, 256, BF16, out, None) == ar.AR_ERR_UNSUPPORTED
+    assert L.ar_residual_rmsnorm(_ptrs(p[:12]), 12, 4, 256, BF16, 0xA00000, 0xB00000, 1e-6,
+                                 0xC00000, 0xD00000, None) == ar.AR_ERR_UNSUPPORTED
+    # Null input array / null partial / null output.
+    assert L.ar_sum(None, 2, 4, 256, BF16, out, None) == ar.AR_ERR_INVALID_ARG
+    assert L.ar_sum(_ptrs([p[0], 0]), 2, 4, 256, BF16, out, None) == ar.AR_ERR_INVALID_ARG
+    assert L.ar_sum(_ptrs(p[:2]), 2, 4, 256, BF16, None, None) == ar.AR_ERR_INVALID_ARG
+    # Misaligned.
+    assert L.ar_sum(_ptrs([p[0] + 2, p[1]]), 2, 4, 256, BF16, out, None) == ar.AR_ERR_MISALIGNED
+    assert L.ar_sum(_ptrs(p[:2]), 2, 4, 256, BF16, out + 8, None) == ar.AR_ERR_MISALIGNED
+    # Partial overlap of out with an input (4*256*2 = 2048 bytes each).
+    assert L.ar_sum(_ptrs(p[:2]), 2, 4, 256, BF16, p[0] + 1024, None) == ar.AR_ERR_ALIAS
+    # norm_out overlapping residual_out; gamma inside an output.
+    args = (_ptrs(p[:2]), 2, 4, 256, BF16, 0xA00000, 0xB00000, 1e-6)
+    assert L.ar_residual_rmsnorm(*args, 0xC00000, 0xC00000 + 512, None) == ar.AR_ERR_ALIAS
+    assert L.ar_residual_rmsnorm(_ptrs(p[:2]), 2, 4, 256, BF16, 0xA00000, 0xC00000 + 256, 1e-6,
+                                 0xC00000, 0xD00000, None) == ar.AR_ERR_ALIAS
+    # Bad eps, bad dtype, bad H for the norm.
+    assert L.ar_residual_rmsnorm(_ptrs(p[:2]), 2, 4, 256, BF16, 0xA00000, 0xB00000, -1e-6,
+                                 0xC00000, 0xD00000, None) == ar.AR_ERR_INVALID_ARG
+    assert L.ar_residual_rmsnorm(_ptrs(p[:2]), 2, 4, 256, BF16, 0xA00000, 0xB00000,
+                                 float("inf"), 0xC00000, 0xD00000, None) == ar.AR_ERR_INVALID_ARG
+    assert L.ar_sum(_ptrs(p[:2]), 2, 4, 256, 9, out, None) == ar.AR_ERR_INVALID_ARG
+    assert L.ar_residual_rmsnorm(_ptrs(p[:2]), 2, 4, 260, BF16, 0xA00000, 0xB00000, 1e-6,
+                                 0xC00000, 0xD00000, None) == ar.AR_ERR_UNSUPPORTED
+    # A with_config call with a malformed shape or a null shape.
+    bad = ar.LaunchConfig(threads_per_block=100, vecs_per_thread=1, lanes_per_row=0,
+                          rows_per_block=0, grid=1, flat=1)
+    assert L.ar_sum_with_config(_ptrs(p[:2]), 2, 4, 256, BF16, out, None,
+                                ctypes.byref(bad)) == ar.AR_ERR_INVALID_ARG
+    assert L.ar_sum_with_config(_ptrs(p[:2]), 2, 4, 256, BF16, out, None,
+                                None) == ar.AR_ERR_INVALID_ARG
+
+
+def test_zero_rows_returns_ok_without_device(L):
+    """M = 0 is accepted before any device access (null pointers allowed for empty tensors)."""
+    assert L.ar_sum(None, 2, 0, 256, BF16, None, None) == ar.AR_OK
+    assert L.ar_residual_rmsnorm(None, 2, 0, 256, BF16, None, None, 1e-6, None, None,
+                                 None) == ar.AR_OK

@@ -1,0 +1,232 @@
+"""Parity of the HIP path (called through the C ABI) with the CPU oracle, element by element.
+
+Bar (written in gpu_util): out and residual_out bit-identical; norm_out within 1 ulp for
+bf16/fp16 and within 1e-5 relative for fp32.  Inputs come from synth (seeded), the same arrays
+go to both sides.  Covers the five workloads at their full sizes in the launch shape the
+library picks (the one the benchmark times), every supported W and element type, ragged rows
+and tails, every launch-shape family, the hand-derived golden fixtures and special values.
+"""
+import numpy as np
+import pytest
+import torch
+
+import all_reduce_residual_amd as ar
+import synth
+from golden_fixtures import all_fixtures
+from gpu_util import assert_bit_exact, assert_norm_close, dev, host_np
+
+pytestmark = pytest.mark.gpu
+
+TD = synth.TORCH_DTYPES
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+    ar.lib()
+
+
+def run_sum_both(oracle_mod, parts, dtype, config=None):
+    d_parts = [dev(p) for p in parts]
+    out = torch.empty_like(d_parts[0])
+    ar.ar_sum(d_parts, out, config=config)
+    torch.cuda.synchronize()
+    want = oracle_mod.ar_sum([host_np(p) for p in parts], dtype)
+    assert_bit_exact(host_np(out.cpu()), want, dtype, "out")
+
+
+def run_rms_both(oracle_mod, parts, res, gam, eps, dtype, config=None, oracle_out=None):
+    d_parts = [dev(p) for p in parts]
+    d_res, d_gam = dev(res), dev(gam)
+    ro = torch.empty_like(d_res)
+    no = torch.empty_like(d_res)
+    ar.ar_residual_rmsnorm(d_parts, d_res, d_gam, eps, ro, no, config=config)
+    torch.cuda.synchronize()
+    if oracle_out is None:
+        oracle_out = oracle_mod.ar_residual_rmsnorm([host_np(p) for p in parts], host_np(res),
+                                                    gam.numpy(), eps, dtype)
+    want_ro, want_no = oracle_out
+    assert_bit_exact(host_np(ro.cpu()), want_ro, dtype, "residual_out")
+    return assert_norm_close(host_np(no.cpu()), want_no, dtype)
+
+
+# ---- the five workloads at full size ---------------------------------------------------------
+
+WL_CASES = [(name, M, pat) for name, wl in synth.WORKLOADS.items() for M in wl.Ms
+            for pat in wl.patterns]
+
+
+@pytest.mark.parametrize("name,M,pattern", WL_CASES,
+                         ids=["%s-M%d-%s" % c for c in WL_CASES])
+def test_workload_full_size(oracle_mod, name, M, pattern):
+    wl = synth.WORKLOADS[name]
+    print("case", name, M, pattern, flush=True)
+    parts, res, gam = synth.inputs(wl, M)
+    if pattern == "sum":
+        run_sum_both(oracle_mod, parts, wl.dtype)
+    else:
+        run_rms_both(oracle_mod, parts, res, gam, wl.eps, wl.dtype)
+
+
+# ---- every W x element type, ragged shapes --------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("W", [1, 2, 4, 8, 16, 32, 64])
+def test_all_world_sizes(oracle_mod, dtype, W):
+    M, H = 5, 1016 if dtype != "fp32" else 1012   # 127 / 253 vectors per row: ragged
+    parts, res, gam = synth.custom(W, M, H, dtype, seed=1000 + W)
+    run_sum_both(oracle_mod, parts, dtype)
+    run_rms_both(oracle_mod, parts, res, gam, 1e-6, dtype)
+
+
+RAGGED = [(1, 8), (3, 24), (2, 56), (31, 256), (33, 520), (7, 4104), (3, 8192), (2, 16384),
+          (2, 32768), (1, 65536), (257, 64)]
+
+
+@pytest.mark.parametrize("M,H", RAGGED, ids=["M%d-H%d" % c for c in RAGGED])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_ragged_shapes(oracle_mod, M, H, dtype):
+    W = 4
+    parts, res, gam = synth.custom(W, M, H, dtype, seed=M * 131 + H)
+    run_sum_both(oracle_mod, parts, dtype)
+    run_rms_both(oracle_mod, parts, res, gam, 1e-5, dtype)
+
+
+@pytest.mark.parametrize("M,H", [(3, 13), (1, 1), (1, 7), (5, 3), (2, 1001)])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+def test_sum_element_tail(oracle_mod, M, H, dtype):
+    """kAllReduce accepts any M*H: the part after the last full 16-byte vector is summed
+    element by element."""
+    parts, _, _ = synth.custom(4, M, H, dtype, seed=7 * M + H, with_norm=False)
+    run_sum_both(oracle_mod, parts, dtype)
+
+
+def test_fp32_largest_row(oracle_mod):
+    parts, res, gam = synth.custom(2, 2, 32768, "fp32", seed=5)
+    run_rms_both(oracle_mod, parts, res, gam, 1e-6, "fp32")
+
+
+# ---- every launch-shape family gives the same result ---------------------------------------
+
+def _norm_configs(V, M):
+    cfgs = []
+    for vpt in (1, 2, 4, 8):
+        need = -(-V // vpt)
+        if need <= 64:
+            lanes = 1
+            while lanes < need:
+                lanes *= 2
+            for threads in (64, 256, 1024):
+                cfgs.append(dict(threads_per_block=threads, vecs_per_thread=vpt,
+                                 lanes_per_row=lanes, rows_per_block=threads // lanes,
+                                 grid=max(1, min(3, M)), flat=0))
+        lanes = -(-need // 64) * 64
+        if lanes <= 1024:
+            for grid in (1, 2, M):
+                cfgs.append(dict(threads_per_block=lanes, vecs_per_thread=vpt,
+                                 lanes_per_row=lanes, rows_per_block=1, grid=max(grid, 1),
+                                 flat=0))
+            if lanes * 2 <= 1024:
+                cfgs.append(dict(threads_per_block=lanes * 2, vecs_per_thread=vpt,
+                                 lanes_per_row=lanes, rows_per_block=2, grid=max(1, M // 3),
+                                 flat=0))
+    return cfgs
+
+
+@pytest.mark.parametrize("H", [64, 256, 1016, 7168])
+def test_norm_launch_shapes_agree(oracle_mod, H):
+    dtype, M, W = "bf16", 9, 8
+    parts, res, gam = synth.custom(W, M, H, dtype, seed=H)
+    want = oracle_mod.ar_residual_rmsnorm([host_np(p) for p in parts], host_np(res),
+                                          gam.numpy(), 1e-6, dtype)
+    cfgs = _norm_configs(H // 8, M)
+    assert len(cfgs) >= 4
+    for cfg in cfgs:
+        run_rms_both(oracle_mod, parts, res, gam, 1e-6, dtype, config=cfg, oracle_out=want)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_sum_launch_shapes_agree(oracle_mod, dtype):
+    parts, _, _ = synth.custom(8, 37, 1000, dtype, seed=77, with_norm=False)
+    for threads in (64, 256, 1024):
+        for u in (1, 2, 4):
+            for grid in (1, 7, 10000):
+                run_sum_both(oracle_mod, parts, dtype,
+                             config=dict(threads_per_block=threads, vecs_per_thread=u,
+                                         lanes_per_row=0, rows_per_block=0, grid=grid, flat=1))
+
+
+# ---- hand-derived golden fixtures --------------------------------------------------------------
+
+FIXTURES = all_fixtures()
+
+
+def _from_storage(a: np.ndarray, dtype: str) -> torch.Tensor:
+    if dtype == "fp32":
+        return torch.from_numpy(a.copy())
+    return torch.from_numpy(a.view(np.int16).copy()).view(TD[dtype])
+
+
+@pytest.mark.parametrize("fx", FIXTURES, ids=[f["name"] for f in FIXTURES])
+def test_golden_fixtures_on_gpu(fx):
+    dt = fx["dtype"]
+    parts = [dev(_from_storage(x, dt)) for x in fx["inputs"]]
+    if fx["pattern"] == "sum":
+        out = torch.empty_like(parts[0])
+        ar.ar_sum(parts, out)
+        assert_bit_exact(host_np(out.cpu()), fx["out"], dt, "out")
+    else:
+        res = dev(_from_storage(fx["residual"], dt))
+        gam = dev(torch.from_numpy(fx["gamma"]))
+        ro, no = torch.empty_like(res), torch.empty_like(res)
+        ar.ar_residual_rmsnorm(parts, res, gam, fx["eps"], ro, no)
+        assert_bit_exact(host_np(ro.cpu()), fx["residual_out"], dt, "residual_out")
+        assert_bit_exact(host_np(no.cpu()), fx["norm_out"], dt, "norm_out")
+
+
+# ---- special values ------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+def test_special_values(oracle_mod, dtype):
+    """Subnormals, signed zeros, overflow to infinity, infinities and NaN in the partials."""
+    M, H, W = 4, 64, 4
+    rng = np.random.default_rng(3)
+    if dtype == "fp32":
+        pool = np.array([0.0, -0.0, 1e-45, -1e-45, 1.1754942e-38, 3.4e38, -3.4e38, np.inf,
+                         -np.inf, np.nan, 1.0, -2.5, 65504.0], dtype=np.float32)
+        parts = [torch.from_numpy(rng.choice(pool, size=(M, H)).astype(np.float32))
+                 for _ in range(W)]
+    else:
+        if dtype == "fp16":
+            pool = [0x0000, 0x8000, 0x0001, 0x8001, 0x03FF, 0x0400, 0x7BFF, 0xFBFF, 0x7C00,
+                    0xFC00, 0x7E00, 0x3C00, 0xC100]
+        else:
+            pool = [0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x0080, 0x7F7F, 0xFF7F, 0x7F80,
+                    0xFF80, 0x7FC0, 0x3F80, 0xC020]
+        parts = [torch.from_numpy(rng.choice(np.array(pool, dtype=np.uint16), size=(M, H))
+                                  .view(np.int16)).view(TD[dtype]) for _ in range(W)]
+    run_sum_both(oracle_mod, parts, dtype)
+    res = torch.zeros(M, H, dtype=TD[dtype])
+    gam = torch.ones(H, dtype=torch.float32)
+    run_rms_both(oracle_mod, parts, res, gam, 1e-6, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_subnormal_results_kept(oracle_mod, dtype):
+    """Cancellation into the subnormal range of T: no flush to zero on either side."""
+    M, H = 2, 256
+    tiny = {"fp16": 2.0 ** -20, "bf16": 2.0 ** -130}[dtype]
+    x0 = torch.full((M, H), 3 * tiny, dtype=torch.float32)
+    x1 = torch.full((M, H), -2 * tiny, dtype=torch.float32)
+    parts = [x0.to(TD[dtype]), x1.to(TD[dtype])]
+    run_sum_both(oracle_mod, parts, dtype)
+
+
+def test_fp16_outliers_cancel(oracle_mod):
+    """+-50 outliers over 16 ranks (the many-rank fp16 workload's distribution) at a small
+    shape: cancellation makes the rank order visible in the last bits."""
+    wl = synth.WORKLOADS["fp16_many_rank"]
+    parts = [synth.partial(wl, r, 6) for r in range(wl.W)]
+    run_sum_both(oracle_mod, parts, "fp16")
