@@ -1,0 +1,540 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused all-reduce-sum + residual + RMSNorm core on one MI355X.
+
+One step = one ar_residual_rmsnorm call (kARResidualRMSNorm: W partials summed in binary32,
+residual added, residual_out and norm_out written) on the wide-hidden prefill workload:
+W=8 partials, M=2048 tokens, H=7168, bf16.  Inputs are resident in HBM before the timed region.
+Buffer sets are rotated so that the bytes a timed batch touches exceed the 256 MB Infinity
+Cache (the numbers are HBM numbers, not cache numbers).  Steps are timed with HIP events on the
+stream the kernel is launched on.
+
+Output: ONE JSON line with the metric (effective HBM GB/s = algorithmic bytes / time, bytes =
+(W + 3) * M * H * 2: W partial reads, residual read, residual_out and norm_out writes), the
+roofline of the kernel against the 8 TB/s HBM peak, the oracle's CPU baseline, and a sweep over
+M = 1..2048 for both patterns (stream-launched and hipGraph-replayed µs/call).
+
+Modes:
+  (default)              the benchmark above
+  --mode pmc             a short run for rocprofv3 --pmc: a plain device copy of known size
+                         (calibrates FETCH_SIZE / WRITE_SIZE) and a few headline steps
+  --summarize-stats DIR  markdown summary of a rocprofv3 --kernel-trace --stats output dir
+  --summarize-pmc DIR... markdown summary of rocprofv3 --pmc output dirs (FETCH_SIZE run, then
+                         WRITE_SIZE run) scaled by the copy calibration
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import ctypes
+import glob
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import threading
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
+INFINITY_CACHE = 256 * 2 ** 20
+ROTATE_BYTES = 512 * 2 ** 20   # bytes a timed batch must touch (2x the Infinity Cache)
+COPY_CAL_BYTES = 256 * 2 ** 20
+
+HEADLINE = dict(workload="wide_hidden", pattern="rms", W=8, M=2048, H=7168, dtype="bf16",
+                eps=1e-6)
+SWEEP_M = (1, 8, 32, 64, 128, 512, 2048)
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+PMC_SUMMARY = os.path.join(PROFILE_DIR, "norm_kernel_wide_hidden_M2048_pmc.md")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in ("all_reduce_residual_amd/csrc/ar_kernels.hpp",
+                "all_reduce_residual_amd/csrc/ar_fused.hip",
+                "all_reduce_residual_amd/_build.py"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def metric_bytes(pattern: str, W: int, M: int, H: int, esize: int) -> int:
+    extra = 3 if pattern == "rms" else 1
+    return (W + extra) * M * H * esize
+
+
+# ---- GPU cases -------------------------------------------------------------------------------
+
+class Case:
+    """One (pattern, W, M, H) problem with R rotated buffer sets carved from one allocation per
+    tensor role, and pre-marshalled C-ABI arguments for every set."""
+
+    def __init__(self, ar, torch, pattern, W, M, H, dtype="bf16", eps=1e-6, rotate=True,
+                 seed=1234, dist=(0.0, 0.05)):
+        self.ar, self.torch = ar, torch
+        self.pattern, self.W, self.M, self.H, self.dtype, self.eps = pattern, W, M, H, dtype, eps
+        tdt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[dtype]
+        self.esize = 4 if dtype == "fp32" else 2
+        self.bytes = metric_bytes(pattern, W, M, H, self.esize)
+        footprint = self.bytes
+        self.R = max(1, min(4096, math.ceil(ROTATE_BYTES / footprint))) if rotate else 1
+        g = torch.Generator(device="cuda")
+        g.manual_seed(seed)
+        rows = self.R * M
+
+        def randn(mu, sigma):
+            t = torch.empty((rows, H), dtype=torch.float32, device="cuda")
+            t.normal_(mu, sigma, generator=g)
+            return t.to(tdt)
+
+        self.parts = [randn(*dist) for _ in range(W)]
+        if pattern == "rms":
+            self.res = randn(0.0, 1.0)
+            self.gamma = torch.empty(H, dtype=torch.float32, device="cuda").uniform_(
+                0.8, 1.2, generator=g)
+            self.ro = torch.empty_like(self.res)
+            self.no = torch.empty_like(self.res)
+            self.fn = ar.lib().ar_residual_rmsnorm
+        else:
+            self.out = torch.empty_like(self.parts[0])
+            self.fn = ar.lib().ar_sum
+        self.dt = ar.dtype_code(tdt)
+        self._keep = []
+        self.args = [self._args_for(r) for r in range(self.R)]
+        torch.cuda.synchronize()
+
+    def _sl(self, t, r):
+        return t[r * self.M:(r + 1) * self.M].data_ptr()
+
+    def _args_for(self, r):
+        ptrs = (ctypes.c_void_p * self.W)(*[self._sl(p, r) for p in self.parts])
+        self._keep.append(ptrs)
+        if self.pattern == "rms":
+            return (ptrs, self.W, self.M, self.H, self.dt, self._sl(self.res, r),
+                    self.gamma.data_ptr(), ctypes.c_float(self.eps), self._sl(self.ro, r),
+                    self._sl(self.no, r))
+        return (ptrs, self.W, self.M, self.H, self.dt, self._sl(self.out, r))
+
+    def call(self, i: int, stream_handle: int) -> None:
+        st = self.fn(*self.args[i % self.R], ctypes.c_void_p(stream_handle))
+        if st != 0:
+            raise RuntimeError("library call failed: %s" % self.ar.status_string(st))
+
+    def calls_per_batch(self, minimum: int) -> int:
+        """A batch covers every rotation set equally and has at least `minimum` calls."""
+        return self.R * max(1, math.ceil(minimum / self.R))
+
+    def time_stream(self, calls: int, reps: int = 5) -> float:
+        """Median µs/call of `calls` back-to-back launches on the current stream."""
+        torch = self.torch
+        s = torch.cuda.current_stream()
+        h = s.cuda_stream
+        for i in range(min(calls, 3 * self.R) + 3):
+            self.call(i, h)
+        torch.cuda.synchronize()
+        res = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(s)
+            for i in range(calls):
+                self.call(i, h)
+            b.record(s)
+            b.synchronize()
+            res.append(a.elapsed_time(b) * 1000.0 / calls)
+        return sorted(res)[len(res) // 2]
+
+    def time_graph(self, calls: int, reps: int = 5) -> float:
+        """Median µs/call of a hipGraph replay holding `calls` launches."""
+        torch = self.torch
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(3):
+                self.call(i, side.cuda_stream)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            h = torch.cuda.current_stream().cuda_stream
+            for i in range(calls):
+                self.call(i, h)
+        graph.replay()
+        torch.cuda.synchronize()
+        res = []
+        s = torch.cuda.current_stream()
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(s)
+            graph.replay()
+            b.record(s)
+            b.synchronize()
+            res.append(a.elapsed_time(b) * 1000.0 / calls)
+        del graph
+        return sorted(res)[len(res) // 2]
+
+
+def check_headline_parity(ar, torch, case) -> dict:
+    """Put the seeded workload inputs into rotation set 0 and compare sampled rows of both
+    outputs with the oracle (residual_out bit-exact, norm_out within 1 ulp)."""
+    import numpy as np
+    import oracle
+    import synth
+    wl = synth.WORKLOADS[HEADLINE["workload"]]
+    M, H = case.M, case.H
+    parts, res, gam = synth.inputs(wl, M)
+    for d, h in zip(case.parts, parts):
+        d[:M].copy_(h)
+    case.res[:M].copy_(res)
+    case.gamma.copy_(gam)
+    torch.cuda.synchronize()
+    case.call(0, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    rows = sorted(set([0, 1, M // 2, M - 1] + list(rng.integers(0, M, size=12))))
+    hp = [synth.storage_numpy(p) for p in parts]
+    hr = synth.storage_numpy(res)
+    got_ro = synth.storage_numpy(case.ro[:M].cpu())
+    got_no = synth.storage_numpy(case.no[:M].cpu())
+    worst = 0
+    for r in rows:
+        ro, no = oracle.ar_residual_rmsnorm(hp, hr, gam.numpy(), wl.eps, wl.dtype, rows=(r, r + 1))
+        if not np.array_equal(got_ro[r], ro[r]):
+            raise AssertionError("bench parity: residual_out row %d differs from the oracle" % r)
+        a = got_no[r].astype(np.int32)
+        b = no[r].astype(np.int32)
+        oa = np.where(a & 0x8000, -(a & 0x7FFF), a & 0x7FFF)
+        ob = np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+        worst = max(worst, int(np.abs(oa - ob).max()))
+    if worst > 1:
+        raise AssertionError("bench parity: norm_out %d ulp from the oracle" % worst)
+    return {"rows_checked": len(rows), "residual_out": "bit-exact", "norm_out_max_ulp": worst}
+
+
+# ---- CPU baseline -------------------------------------------------------------------------------
+
+def cpu_baseline(min_wall: float = 1.5) -> dict:
+    """The oracle (unchanged) on the headline workload, row slices over the host's threads."""
+    import oracle
+    import synth
+    wl = synth.WORKLOADS[HEADLINE["workload"]]
+    M, H, W = HEADLINE["M"], HEADLINE["H"], HEADLINE["W"]
+    parts, res, gam = synth.inputs(wl, M)
+    hp = [synth.storage_numpy(p) for p in parts]
+    hr = synth.storage_numpy(res)
+    g = gam.numpy()
+    import numpy as np
+    ro = np.empty_like(hr)
+    no = np.empty_like(hr)
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    threads = max(1, min(16, avail))
+    bounds = [(M * i // threads, M * (i + 1) // threads) for i in range(threads)]
+
+    def one_call():
+        ts = [threading.Thread(target=oracle.ar_residual_rmsnorm,
+                               args=(hp, hr, g, wl.eps, wl.dtype),
+                               kwargs=dict(rows=b, residual_out=ro, norm_out=no))
+              for b in bounds]
+        for t in ts:
+            t.start()
+        for t in ts:
+            t.join()
+
+    one_call()  # warm-up
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        one_call()
+        n += 1
+        if time.perf_counter() - t0 >= min_wall:
+            break
+    dt = (time.perf_counter() - t0) / n
+    nbytes = metric_bytes("rms", W, M, H, 2)
+    # One-core figure on a 256-row slice.
+    t1 = time.perf_counter()
+    oracle.ar_residual_rmsnorm(hp, hr, g, wl.eps, wl.dtype, rows=(0, 256), residual_out=ro,
+                               norm_out=no)
+    dt1 = time.perf_counter() - t1
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "full W=8 M=2048 H=7168 bf16 residual+RMSNorm call, rows split over %d "
+                      "threads, %d call(s) timed (%.1f s wall, ~%.0f s CPU)" % (
+                          threads, n, dt * n, dt * n * threads),
+            "us_per_call": round(dt * 1e6, 1),
+            "one_core_GBs": round(metric_bytes("rms", W, 256, H, 2) / dt1 / 1e9, 4),
+            "cpu_model": cpu_model()}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# ---- rocprofv3 summaries ----------------------------------------------------------------------
+
+def _read_csvs(d: str, pattern: str):
+    rows = []
+    for path in glob.glob(os.path.join(d, "**", pattern), recursive=True):
+        with open(path) as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def summarize_stats(d: str) -> str:
+    rows = _read_csvs(d, "*kernel_stats.csv")
+    if not rows:
+        raise SystemExit("no kernel_stats.csv under %s" % d)
+    out = ["| kernel | calls | avg µs | min µs | max µs | share % |", "|---|---|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        name = r["Name"]
+        short = re.sub(r"\(.*", "", name)[:90]
+        out.append("| `%s` | %s | %.2f | %.2f | %.2f | %.1f |" % (
+            short, r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    return "\n".join(out)
+
+
+def _pmc_by_kernel(d: str, counter: str):
+    rows = _read_csvs(d, "*counter_collection.csv")
+    vals = {}
+    for r in rows:
+        if r.get("Counter_Name") != counter:
+            continue
+        vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return vals
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str) -> str:
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the norm kernel, scaled by what the same
+    counters read for torch's device copy of COPY_CAL_BYTES (reads and writes that many bytes)."""
+    fetch = _pmc_by_kernel(fetch_dir, "FETCH_SIZE")
+    write = _pmc_by_kernel(write_dir, "WRITE_SIZE")
+
+    def pick(d, pred):
+        ks = [k for k in d if pred(k)]
+        if not ks:
+            raise SystemExit("kernel not found in counter data: %s" % list(d)[:5])
+        vals = [v for k in ks for v in d[k]]
+        return ks[0], sum(vals) / len(vals), len(vals)
+
+    is_norm = lambda k: "ar_norm_kernel" in k
+    is_copy = lambda k: k.startswith("__amd_rocclr_copyBuffer")   # hipMemcpy device-to-device
+    kn, f_norm, n1 = pick(fetch, is_norm)
+    kc, f_copy, n2 = pick(fetch, is_copy)
+    _, w_norm, n3 = pick(write, is_norm)
+    _, w_copy, n4 = pick(write, is_copy)
+    f_factor = COPY_CAL_BYTES / (f_copy * 1024.0)
+    w_factor = COPY_CAL_BYTES / (w_copy * 1024.0)
+    W, M, H = HEADLINE["W"], HEADLINE["M"], HEADLINE["H"]
+    alg_read = (W + 1) * M * H * 2
+    alg_write = 2 * M * H * 2
+    fetch_b = f_norm * 1024.0 * f_factor
+    write_b = w_norm * 1024.0 * w_factor
+    data = {"kernel_hash": kernel_source_hash(), "fetch_bytes": round(fetch_b),
+            "write_bytes": round(write_b), "traffic_bytes": round(fetch_b + write_b),
+            "algorithmic_read_bytes": alg_read, "algorithmic_write_bytes": alg_write,
+            "fetch_factor": round(f_factor, 4), "write_factor": round(w_factor, 4)}
+    lines = [
+        "norm kernel: `%s` (%d + %d dispatches)" % (re.sub(r"\(.*", "", kn), n1, n3),
+        "copy kernel: `%s` (%d + %d dispatches), %d bytes read and written per dispatch" % (
+            re.sub(r"\(.*", "", kc)[:80], n2, n4, COPY_CAL_BYTES),
+        "scale = copy bytes / (copy counter KiB * 1024); scaled bytes = norm counter KiB * 1024 "
+        "* scale",
+        "",
+        "| counter | norm kernel KiB/dispatch | copy KiB/dispatch | scale | scaled bytes | "
+        "algorithmic bytes | ratio |",
+        "|---|---|---|---|---|---|---|",
+        "| FETCH_SIZE | %.0f | %.0f | %.4f | %.0f | %d | %.3f |" % (
+            f_norm, f_copy, f_factor, fetch_b, alg_read, fetch_b / alg_read),
+        "| WRITE_SIZE | %.0f | %.0f | %.4f | %.0f | %d | %.3f |" % (
+            w_norm, w_copy, w_factor, write_b, alg_write, write_b / alg_write),
+        "",
+        "traffic_json: " + json.dumps(data),
+    ]
+    return "\n".join(lines)
+
+
+def read_traffic():
+    """Traffic from the committed counter summary, if it was taken on the current kernel."""
+    try:
+        with open(PMC_SUMMARY) as f:
+            for line in f:
+                if line.startswith("traffic_json:"):
+                    d = json.loads(line.split(":", 1)[1])
+                    if d.get("kernel_hash") == kernel_source_hash():
+                        return d["traffic_bytes"]
+    except (OSError, ValueError):
+        pass
+    return None
+
+
+# ---- main ---------------------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--mode", choices=["bench", "pmc"], default="bench")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--summarize-stats", metavar="DIR")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    args = ap.parse_args()
+
+    if args.summarize_stats:
+        print(summarize_stats(args.summarize_stats))
+        return 0
+    if args.summarize_pmc:
+        print(summarize_pmc(*args.summarize_pmc))
+        return 0
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU's share of the fused all-reduce on a single MI355X; "
+              "runs on more than one GPU are not part of this build (got --gpus %d, "
+              "WORLD_SIZE=%d)." % (args.gpus, world), file=sys.stderr)
+        return 2
+
+    import torch
+    import all_reduce_residual_amd as ar
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    ar.lib()
+
+    H, W, M = HEADLINE["H"], HEADLINE["W"], HEADLINE["M"]
+    if args.mode == "pmc":
+        # Copy calibration: torch's device copy reads and writes COPY_CAL_BYTES per dispatch.
+        src = torch.empty(COPY_CAL_BYTES // 4, dtype=torch.float32, device="cuda").uniform_()
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        case = Case(ar, torch, "rms", W, M, H)
+        h = torch.cuda.current_stream().cuda_stream
+        for i in range(max(2, args.steps)):
+            case.call(i, h)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "pmc", "copy_bytes": COPY_CAL_BYTES, "norm_calls":
+                          max(2, args.steps), "rotation_sets": case.R}))
+        return 0
+
+    print("# device: %s, %d CUs, host %s, %d host threads" % (
+        torch.cuda.get_device_name(0), ar.ar_device_cu_count(), cpu_model(),
+        len(os.sched_getaffinity(0))), file=sys.stderr, flush=True)
+
+    # Headline: warm-up, then exactly `steps` timed steps on rotated buffer sets.
+    case = Case(ar, torch, "rms", W, M, H)
+    parity = check_headline_parity(ar, torch, case)
+    s = torch.cuda.current_stream()
+    hnd = s.cuda_stream
+    for i in range(args.warmup):
+        case.call(i, hnd)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(s)
+    for i in range(args.steps):
+        case.call(i, hnd)
+    b.record(s)
+    b.synchronize()
+    torch.cuda.synchronize()
+    ms_total = a.elapsed_time(b)
+    us_per_call = ms_total * 1000.0 / args.steps
+    gbs = case.bytes / (us_per_call * 1e-6) / 1e9
+    launch_cfg = ar.ar_launch_config(ar.PATTERN_AR_RESIDUAL_RMSNORM, W, M, H, ar.DTYPE_BF16)
+    print("# headline: %.2f us/call, %.1f GB/s (%.1f%% of peak), R=%d sets, cfg=%s" % (
+        us_per_call, gbs, 100 * gbs / HBM_PEAK_GBS, case.R, launch_cfg), file=sys.stderr,
+        flush=True)
+    del case
+    torch.cuda.empty_cache()
+
+    result = {
+        "metric": "µs/call and effective HBM GB/s (% of peak), AR+residual+RMSNorm, W=8 H=7168",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_total / args.steps, 6),
+        "us_per_call": round(us_per_call, 3),
+        "pct_of_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "wide_hidden prefill, kARResidualRMSNorm", "W": W, "M": M,
+                   "H": H, "element_type": "bf16", "gamma": "fp32", "eps": HEADLINE["eps"],
+                   "bytes_per_call": metric_bytes("rms", W, M, H, 2),
+                   "launch": launch_cfg, "parity": parity},
+    }
+    traffic = read_traffic()
+    result["roofline"] = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                          "traffic": traffic}
+
+    # Calibrations: minimal-work launch floor and device-copy bandwidth.
+    floor = Case(ar, torch, "sum", 1, 1, 8, rotate=False)
+    calib = {"launch_floor_us_stream": round(floor.time_stream(200), 3),
+             "launch_floor_us_graph": round(floor.time_graph(200), 3)}
+    del floor
+    src = torch.empty(2 ** 30 // 4, dtype=torch.float32, device="cuda").uniform_()
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    calib["d2d_copy_GBs"] = round(2 * 2 ** 30 / (sorted(ts)[2] * 1e-3) / 1e9, 1)
+    del src, dst
+    torch.cuda.empty_cache()
+    result["calibration"] = calib
+
+    if not args.no_sweep:
+        sweep = []
+        for pattern in ("rms", "sum"):
+            for m in SWEEP_M:
+                c = Case(ar, torch, pattern, W, m, H)
+                calls = c.calls_per_batch(50 if m >= 512 else 200)
+                us_s = c.time_stream(calls)
+                us_g = c.time_graph(calls)
+                warm = Case(ar, torch, pattern, W, m, H, rotate=False) if c.R > 1 else c
+                us_w = warm.time_graph(200)
+                best = min(us_s, us_g)
+                sweep.append({"pattern": "kARResidualRMSNorm" if pattern == "rms" else
+                              "kAllReduce", "M": m, "bytes": c.bytes, "rotation_sets": c.R,
+                              "us_stream": round(us_s, 3), "us_graph": round(us_g, 3),
+                              "us_graph_cache_warm": round(us_w, 3),
+                              "GBs": round(c.bytes / (best * 1e-6) / 1e9, 1),
+                              "pct_of_peak": round(100 * c.bytes / (best * 1e-6) / 1e9 /
+                                                   HBM_PEAK_GBS, 2)})
+                print("# sweep %s" % json.dumps(sweep[-1]), file=sys.stderr, flush=True)
+                del c, warm
+                torch.cuda.empty_cache()
+        result["sweep"] = sweep
+
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
