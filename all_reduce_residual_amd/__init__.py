@@ -46,14 +46,14 @@ class ArError(RuntimeError):
 class LaunchConfig(ctypes.Structure):
     _fields_ = [("threads_per_block", ctypes.c_int32), ("vecs_per_thread", ctypes.c_int32),
                 ("lanes_per_row", ctypes.c_int32), ("rows_per_block", ctypes.c_int32),
-                ("grid", ctypes.c_int32), ("flat", ctypes.c_int32)]
+                ("grid", ctypes.c_int32), ("flat", ctypes.c_int32), ("nt_store", ctypes.c_int32)]
 
     def as_dict(self) -> Dict[str, int]:
         return {name: int(getattr(self, name)) for name, _ in self._fields_}
 
     @classmethod
     def from_dict(cls, d: Dict[str, int]) -> "LaunchConfig":
-        return cls(**{name: int(d[name]) for name, _ in cls._fields_})
+        return cls(**{name: int(d.get(name, 0)) for name, _ in cls._fields_})
 
 
 def lib():

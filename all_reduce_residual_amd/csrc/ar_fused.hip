@@ -116,21 +116,21 @@ int cap_grid(int64_t blocks) {
 void plan_sum(int W, int64_t n, int dtype, int cu, ar_launch_cfg_t* c) {
   const int64_t vec = kVecBytes / elem_size(dtype);
   const int64_t nvec = n / vec;
-  const int64_t waves_full = ceil_div(nvec, 64);
-  int threads = 256;
-  int u = 1;
-  // Enough vectors to give every CU several 256-thread blocks: let each thread own more
-  // vectors per iteration (more independent loads in flight, fewer block launches).
-  if (nvec >= int64_t(cu) * 256 * 8) u = W >= 16 ? 1 : 2;
-  if (nvec >= int64_t(cu) * 256 * 32) u = W >= 16 ? 2 : 4;
-  // Small payloads: single-wave blocks spread the loads over as many CUs as possible.
-  if (waves_full < int64_t(cu) * 4) threads = 64;
+  // Single-wave blocks, one 16-byte vector per thread, one block per 64 vectors: the most
+  // independent waves for the dispatcher to spread over the 256 CUs.  Small payloads (fewer
+  // than 16 such blocks per CU) do better with two vectors per thread and half the blocks.
+  const int threads = 64;
+  const int u = ceil_div(nvec, threads) < int64_t(cu) * 16 ? 2 : 1;
   c->threads_per_block = threads;
   c->vecs_per_thread = u;
   c->lanes_per_row = 0;
   c->rows_per_block = 0;
   c->grid = cap_grid(ceil_div(nvec, int64_t(threads) * u));
   c->flat = 1;
+  // Non-temporal stores measured faster except for outputs that are large next to the reads
+  // (W <= 4 at 64 MiB and beyond, W = 8 at 160 MiB): there ordinary stores win by 3-8 %.
+  const int64_t out_bytes = n * elem_size(dtype);
+  c->nt_store = out_bytes < int64_t(W) * (12 << 20) ? 1 : 0;
 }
 
 void plan_norm(int W, int64_t M, int64_t H, int dtype, int cu, ar_launch_cfg_t* c) {
@@ -145,12 +145,9 @@ void plan_norm(int W, int64_t M, int64_t H, int dtype, int cu, ar_launch_cfg_t* 
     const int64_t rows_per_wave = 64 / lanes;
     threads = (M >= int64_t(cu) * rows_per_wave * 4 * 4) ? 256 : 64;
   } else {
-    // Wide rows: one row per block, spread over as many threads as the row count allows.
-    // Few rows (decode): a row per CU at most, so use the widest row (most loads in flight).
-    // Many rows: fewer, fatter threads (fewer barriers per byte), several blocks per CU.
-    int64_t target = 1024;
-    if (M > int64_t(cu)) target = 512;
-    if (M > int64_t(cu) * 4) target = 256;
+    // Wide rows: one row per block of up to 512 threads (two 16-byte vectors per thread at
+    // H = 7168 bf16: 7 waves), the shape that measured fastest from decode to prefill sizes.
+    const int64_t target = 512;
     vpt = 1;
     while (vpt < 8 && ceil_div(V, vpt) > target) vpt *= 2;
     while (vpt < 8 && round_up(ceil_div(V, vpt), 64) > 1024) vpt *= 2;
@@ -168,6 +165,7 @@ void plan_norm(int W, int64_t M, int64_t H, int dtype, int cu, ar_launch_cfg_t* 
   c->rows_per_block = threads / lanes;
   c->grid = cap_grid(ceil_div(M, c->rows_per_block));
   c->flat = 0;
+  c->nt_store = 1;  // measured faster from decode to prefill sizes
 }
 
 // A caller-supplied shape must be well formed and cover the row; then every kernel access is
@@ -179,6 +177,7 @@ int check_cfg(int pattern, int64_t H, int dtype, const ar_launch_cfg_t* c) {
   const int u = c->vecs_per_thread;
   if (u != 1 && u != 2 && u != 4 && u != 8) return AR_ERR_INVALID_ARG;
   if (c->grid < 1) return AR_ERR_INVALID_ARG;
+  if (c->nt_store != 0 && c->nt_store != 1) return AR_ERR_INVALID_ARG;
   if (pattern == AR_PATTERN_ALLREDUCE) {
     if (c->flat != 1 || u == 8) return AR_ERR_INVALID_ARG;
     return AR_OK;
@@ -208,8 +207,9 @@ hipError_t launch_sum_u(const void* const* inputs, void* out, int64_t nvec, int 
   RankPtrs<W> p = pack_ptrs<W>(inputs);
   u32x4* o = static_cast<u32x4*>(out);
   void* args[] = {&p, &o, &nvec, &tail};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&arf::ar_sum_kernel<T, W, U>),
-                         dim3(c.grid), dim3(c.threads_per_block), args, 0, s);
+  const void* fn = c.nt_store ? reinterpret_cast<const void*>(&arf::ar_sum_kernel<T, W, U, true>)
+                              : reinterpret_cast<const void*>(&arf::ar_sum_kernel<T, W, U, false>);
+  return hipLaunchKernel(fn, dim3(c.grid), dim3(c.threads_per_block), args, 0, s);
 }
 
 template <class T, int W>
@@ -250,8 +250,10 @@ hipError_t launch_norm_v(const void* const* inputs, const void* residual, const 
   int R = c.rows_per_block;
   float count_h = static_cast<float>(H);  // exact: H <= 2^16
   void* args[] = {&p, &res, &gam, &ro, &no, &M, &V, &L, &R, &eps, &count_h};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&arf::ar_norm_kernel<T, W, VPT>),
-                         dim3(c.grid), dim3(c.threads_per_block), args, 0, s);
+  const void* fn =
+      c.nt_store ? reinterpret_cast<const void*>(&arf::ar_norm_kernel<T, W, VPT, true>)
+                 : reinterpret_cast<const void*>(&arf::ar_norm_kernel<T, W, VPT, false>);
+  return hipLaunchKernel(fn, dim3(c.grid), dim3(c.threads_per_block), args, 0, s);
 }
 
 template <class T, int W>

@@ -1,7 +1,7 @@
 // ar_kernels.hpp -- gfx950 device code of the fused all-reduce-sum (+ residual + RMSNorm) core.
 //
-// Two kernels, templated on the element type T, the number of partials W and the number of
-// 16-byte vectors per thread:
+// Two kernels, templated on the element type T, the number of partials W, the number of
+// 16-byte vectors per thread and the store policy:
 //
 //   ar_sum_kernel   kAllReduce.  A flat grid-stride walk over the [M, H] tensors viewed as
 //                   16-byte vectors.  Each thread issues the W loads of its vectors before it
@@ -29,6 +29,8 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 namespace arf {
 
@@ -124,6 +126,25 @@ struct F32 {
   }
 };
 
+// ---- memory access ----------------------------------------------------------------------------
+//
+// Every input byte is read exactly once, so loads are non-temporal (global_load_dwordx4 ... nt):
+// they do not displace useful lines from L2 and the Infinity Cache.  Stores are non-temporal
+// when the launch shape asks for it (large outputs that no cache would keep anyway).
+
+__device__ inline u32x4 load_stream(const u32x4* p) { return __builtin_nontemporal_load(p); }
+
+// The policy is a template parameter: with a run-time flag the compiler merges the two stores
+// and drops the non-temporal hint.
+template <bool kNt>
+__device__ inline void store_vec(u32x4* p, u32x4 v) {
+  if constexpr (kNt) {
+    __builtin_nontemporal_store(v, p);
+  } else {
+    *p = v;
+  }
+}
+
 // ---- wave-level reduction -------------------------------------------------------------------
 
 // x + (x of the lane selected by a DPP control).  All four controls used here stay inside a
@@ -152,6 +173,19 @@ __device__ inline float segment_sum(float x, int seg) {
   return x;
 }
 
+// ---- addressing ---------------------------------------------------------------------------------
+//
+// Every address is a wave-uniform base (a tensor pointer plus a uniform element offset, computed
+// in scalar registers) plus a 32-bit per-lane byte offset.  That maps onto the scalar-base +
+// vector-offset form of the global memory instructions: one VGPR per vector slot, shared by all
+// W + 1 input tensors and both outputs, instead of a 64-bit VGPR pair per load.
+
+template <class P>
+__device__ inline P* at(P* base, uint32_t byte_off) {
+  using C = typename std::conditional<std::is_const<P>::value, const char, char>::type;
+  return reinterpret_cast<P*>(reinterpret_cast<C*>(base) + byte_off);
+}
+
 // ---- rank batching ----------------------------------------------------------------------------
 //
 // A thread sums W ranks for each of its N vectors.  Left alone, the compiler hoists every load
@@ -178,57 +212,76 @@ __device__ inline void batch_fence(float (&acc)[N][K]) {
   }
 }
 
-// acc[k] = -0 + x_0[k] + x_1[k] + ... + x_{W-1}[k] for the N vectors at offsets off[k].
+// acc[k] += x_R0[k] + x_{R0+1}[k] + ... + x_{W-1}[k] (in that order) for the N vectors at
+// element offset `base` (uniform) + byte offset boff[k] (per lane) of every partial.
+template <class T, int W, int N, int R0 = 0, int kMaxLoads = (N * T::kVec >= 32 ? 8 : 16)>
+__device__ inline void rank_sum_range(const RankPtrs<W>& in, int64_t base,
+                                      const uint32_t (&boff)[N], float (&acc)[N][T::kVec]) {
+  constexpr int kBatch = rank_batch<W - R0 < 1 ? 1 : W - R0, N, kMaxLoads>();
+#pragma unroll
+  for (int r0 = R0; r0 < W; r0 += kBatch) {
+#pragma unroll
+    for (int r = r0; r < r0 + kBatch && r < W; ++r) {
+      const u32x4* src = in.p[r] + base;
+#pragma unroll
+      for (int k = 0; k < N; ++k) {
+        float x[T::kVec];
+        T::widen(load_stream(at(src, boff[k])), x);
+#pragma unroll
+        for (int e = 0; e < T::kVec; ++e) acc[k][e] = acc[k][e] + x[e];
+      }
+    }
+    if (r0 + kBatch < W) batch_fence(acc);
+  }
+}
+
+// acc[k] = -0 + x_0[k] + x_1[k] + ... + x_{W-1}[k].
 template <class T, int W, int N, int kMaxLoads = (N * T::kVec >= 32 ? 8 : 16)>
-__device__ inline void rank_sum(const RankPtrs<W>& in, const int64_t (&off)[N],
+__device__ inline void rank_sum(const RankPtrs<W>& in, int64_t base, const uint32_t (&boff)[N],
                                 float (&acc)[N][T::kVec]) {
-  constexpr int kBatch = rank_batch<W, N, kMaxLoads>();
 #pragma unroll
   for (int k = 0; k < N; ++k) {
 #pragma unroll
     for (int e = 0; e < T::kVec; ++e) acc[k][e] = -0.0f;
   }
-#pragma unroll
-  for (int r0 = 0; r0 < W; r0 += kBatch) {
-#pragma unroll
-    for (int r = r0; r < r0 + kBatch && r < W; ++r) {
-#pragma unroll
-      for (int k = 0; k < N; ++k) {
-        float x[T::kVec];
-        T::widen(in.p[r][off[k]], x);
-#pragma unroll
-        for (int e = 0; e < T::kVec; ++e) acc[k][e] = acc[k][e] + x[e];
-      }
-    }
-    if (kBatch < W && r0 + kBatch < W) batch_fence(acc);
-  }
+  rank_sum_range<T, W, N, 0, kMaxLoads>(in, base, boff, acc);
 }
 
 // ---- kAllReduce -----------------------------------------------------------------------------
 
 // out = RN_T(x_0 + ... + x_{W-1}) over n elements: nvec full 16-byte vectors, then a tail of
-// fewer than one vector handled element by element by block 0.
-template <class T, int W, int U>
+// fewer than one vector handled element by element by block 0.  Blocks walk chunks of
+// blockDim.x * U vectors with a grid stride; lane t of a chunk owns vectors t + u * blockDim.x.
+template <class T, int W, int U, bool kNtStore>
 __global__ __launch_bounds__(kMaxThreads) void ar_sum_kernel(RankPtrs<W> in, u32x4* out,
                                                              int64_t nvec, int tail) {
   constexpr int kVec = T::kVec;
-  const int64_t bdim = blockDim.x;
-  const int64_t step = static_cast<int64_t>(gridDim.x) * bdim * U;
-  for (int64_t base = static_cast<int64_t>(blockIdx.x) * bdim * U + threadIdx.x; base < nvec;
-       base += step) {
-    int64_t off[U];
-    bool ok[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      off[u] = base + u * bdim;
-      ok[u] = off[u] < nvec;
-      if (!ok[u]) off[u] = base;  // in bounds; the value is discarded
-    }
+  const int64_t chunk = static_cast<int64_t>(blockDim.x) * U;
+  for (int64_t cbase = blockIdx.x * chunk; cbase < nvec; cbase += gridDim.x * chunk) {
+    uint32_t boff[U];
     float acc[U][kVec];
-    rank_sum<T, W, U>(in, off, acc);
+    if (cbase + chunk <= nvec) {
+      // Whole chunk in range (uniform branch): no predicate anywhere near the loads.
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (ok[u]) out[off[u]] = T::narrow(acc[u]);
+      for (int u = 0; u < U; ++u) boff[u] = (threadIdx.x + u * blockDim.x) * 16u;
+      rank_sum<T, W, U>(in, cbase, boff, acc);
+#pragma unroll
+      for (int u = 0; u < U; ++u) store_vec<kNtStore>(at(out + cbase, boff[u]), T::narrow(acc[u]));
+    } else {
+      // Last, partial chunk: slots past the end re-read the last vector (a clamp, not a
+      // branch, so the loads stay unconditional) and are not stored.
+      const uint32_t last = static_cast<uint32_t>(nvec - cbase - 1);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t i = threadIdx.x + u * blockDim.x;
+        boff[u] = (i < last ? i : last) * 16u;
+      }
+      rank_sum<T, W, U>(in, cbase, boff, acc);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (threadIdx.x + u * blockDim.x <= last)
+          store_vec<kNtStore>(at(out + cbase, boff[u]), T::narrow(acc[u]));
+      }
     }
   }
   if (tail > 0 && blockIdx.x == 0 && static_cast<int>(threadIdx.x) < tail) {
@@ -253,10 +306,10 @@ __device__ inline void accumulate(float (&acc)[T::kVec], u32x4 v) {
 
 // The kVec gamma values of element vector `vec` (gamma is binary32 [H], 16-byte aligned).
 template <int kVec>
-__device__ inline void load_gamma(const f32x4* gamma, int vec, float (&g)[kVec]) {
+__device__ inline void load_gamma(const f32x4* gamma, uint32_t vec, float (&g)[kVec]) {
 #pragma unroll
   for (int j = 0; j < kVec / 4; ++j) {
-    const f32x4 q = gamma[static_cast<int64_t>(vec) * (kVec / 4) + j];
+    const f32x4 q = *at(gamma, (vec * (kVec / 4) + j) * 16u);
     g[4 * j + 0] = q.x;
     g[4 * j + 1] = q.y;
     g[4 * j + 2] = q.z;
@@ -265,8 +318,9 @@ __device__ inline void load_gamma(const f32x4* gamma, int vec, float (&g)[kVec])
 }
 
 // One row = V vectors of 16 bytes.  Thread t of a block serves row slot t / L (R slots per
-// block) and, within the row, vectors lane + k * L for k < VPT.  L * VPT >= V.
-template <class T, int W, int VPT>
+// block) and, within the row, vectors lane + k * L for k < VPT.  L * VPT >= V.  Blocks walk
+// groups of R rows with a grid stride.
+template <class T, int W, int VPT, bool kNtStore>
 __global__ __launch_bounds__(kMaxThreads) void ar_norm_kernel(
     RankPtrs<W> in, const u32x4* residual, const f32x4* gamma, u32x4* residual_out,
     u32x4* norm_out, int64_t M, int V, int L, int R, float eps, float count_h) {
@@ -288,6 +342,14 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_kernel(
     idx[k] = col_ok[k] ? i : 0;
   }
 
+  // Byte offsets of this thread's vectors inside its row group (uniform base: the group's
+  // first row).  A slot past the last row re-reads the group's first row (never stored).
+  auto group_offsets = [&](int64_t grp, uint32_t (&boff)[VPT]) {
+    const bool ok = grp * R + slot < M;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) boff[k] = ((ok ? slot * V : 0) + idx[k]) * 16u;
+  };
+
   // gamma does not depend on the row.  With few vectors per thread this thread's slice is
   // loaded once and kept in registers; with many it is re-read (from L2) in the epilogue.
   constexpr bool kKeepGamma = VPT <= 2;
@@ -299,32 +361,30 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_kernel(
 
   int bank = 0;
   for (int64_t grp = blockIdx.x; grp < groups; grp += gridDim.x) {
-    const int64_t m = grp * R + slot;
-    const bool row_ok = m < M;
-    const int64_t row_base = (row_ok ? m : 0) * static_cast<int64_t>(V);
+    const bool row_ok = grp * R + slot < M;
+    const int64_t base = grp * R * static_cast<int64_t>(V);
+    uint32_t boff[VPT];
+    group_offsets(grp, boff);
 
     // Sum of the W partials and the residual, binary32 in rank order, rounded once to T.
-    int64_t off[VPT];
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) off[k] = row_base + idx[k];
     u32x4 rounded[VPT];
     if constexpr (VPT <= 2) {
       // All vectors' chains together: the most independent loads per batch.
       float acc[VPT][kVec];
-      rank_sum<T, W, VPT>(in, off, acc);
+      rank_sum<T, W, VPT>(in, base, boff, acc);
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {
-        accumulate<T>(acc[k], residual[off[k]]);
+        accumulate<T>(acc[k], load_stream(at(residual + base, boff[k])));
         rounded[k] = T::narrow(acc[k]);
       }
     } else {
       // One vector's chain at a time keeps the live accumulators to one vector.
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {
-        const int64_t off_k[1] = {off[k]};
+        const uint32_t boff_k[1] = {boff[k]};
         float acc[1][kVec];
-        rank_sum<T, W, 1, 8>(in, off_k, acc);
-        accumulate<T>(acc[0], residual[off[k]]);
+        rank_sum<T, W, 1, 8>(in, base, boff_k, acc);
+        accumulate<T>(acc[0], load_stream(at(residual + base, boff[k])));
         rounded[k] = T::narrow(acc[0]);
         batch_fence(acc);
       }
@@ -333,7 +393,7 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_kernel(
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
       if (row_ok && col_ok[k]) {
-        residual_out[off[k]] = rounded[k];
+        store_vec<kNtStore>(at(residual_out + base, boff[k]), rounded[k]);
         float v[kVec];
         T::widen(rounded[k], v);
 #pragma unroll
@@ -374,7 +434,7 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_kernel(
         float y[kVec];
 #pragma unroll
         for (int e = 0; e < kVec; ++e) y[e] = (v[e] * rstd) * g[e];
-        norm_out[off[k]] = T::narrow(y);
+        store_vec<kNtStore>(at(norm_out + base, boff[k]), T::narrow(y));
       }
     }
   }

@@ -92,7 +92,9 @@ typedef enum {
  *                       lanes_per_row * vecs_per_thread >= H / (16 / sizeof(T))
  *   rows_per_block    : norm pattern only: threads_per_block / lanes_per_row
  *   grid              : number of blocks (>= 1); blocks loop over the work with a grid stride
- *   flat              : 1 for the sum pattern (flat vector decomposition), 0 for the norm */
+ *   flat              : 1 for the sum pattern (flat vector decomposition), 0 for the norm
+ *   nt_store          : 1 = outputs are written with non-temporal stores, 0 = ordinary stores
+ *                       (inputs are always read with non-temporal loads) */
 typedef struct {
   int32_t threads_per_block;
   int32_t vecs_per_thread;
@@ -100,6 +102,7 @@ typedef struct {
   int32_t rows_per_block;
   int32_t grid;
   int32_t flat;
+  int32_t nt_store;
 } ar_launch_cfg_t;
 
 /* kAllReduce.  out[m, i] = RN_T(x_0[m, i] + ... + x_{W-1}[m, i]).

@@ -86,6 +86,7 @@ def test_launch_config_invariants(cu):
             assert c == ar.ar_launch_config(pat, W, M, H, dt, cu_count=cu)   # deterministic
             t = c["threads_per_block"]
             assert 64 <= t <= 1024 and t % 64 == 0, c
+            assert c["nt_store"] in (0, 1)
             assert c["grid"] >= 1
             if pat == SUM:
                 assert c["flat"] == 1 and c["vecs_per_thread"] in (1, 2, 4)

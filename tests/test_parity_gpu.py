@@ -143,7 +143,8 @@ def test_norm_launch_shapes_agree(oracle_mod, H):
                                           gam.numpy(), 1e-6, dtype)
     cfgs = _norm_configs(H // 8, M)
     assert len(cfgs) >= 4
-    for cfg in cfgs:
+    for i, cfg in enumerate(cfgs):
+        cfg["nt_store"] = i % 2          # both store policies
         run_rms_both(oracle_mod, parts, res, gam, 1e-6, dtype, config=cfg, oracle_out=want)
 
 
@@ -155,7 +156,8 @@ def test_sum_launch_shapes_agree(oracle_mod, dtype):
             for grid in (1, 7, 10000):
                 run_sum_both(oracle_mod, parts, dtype,
                              config=dict(threads_per_block=threads, vecs_per_thread=u,
-                                         lanes_per_row=0, rows_per_block=0, grid=grid, flat=1))
+                                         lanes_per_row=0, rows_per_block=0, grid=grid, flat=1,
+                                         nt_store=(threads + u + grid) % 2))
 
 
 # ---- hand-derived golden fixtures --------------------------------------------------------------
