@@ -77,6 +77,9 @@ def lib():
             "ar_supports": [i32, i32, i64, i64, i32],
             "ar_launch_config": [i32, i32, i64, i64, i32, i32, cfgp],
             "ar_status_string": [i32],
+            "ar_row_partition": [i32, i64, i32, ctypes.POINTER(ctypes.c_int64),
+                                 ctypes.POINTER(ctypes.c_int64)],
+            "ar_all_gather": [vp, i32, i64, i64, i32, vp, vp],
             "ar_device_cu_count": [ctypes.POINTER(ctypes.c_int)],
         }
         for name, argtypes in sig.items():
@@ -169,6 +172,38 @@ def ar_residual_rmsnorm(inputs, residual, gamma, eps: float, residual_out, norm_
         cfg = LaunchConfig.from_dict(config)
         st = lib().ar_residual_rmsnorm_with_config(*args, ctypes.byref(cfg))
     _check(st, "ar_residual_rmsnorm")
+
+
+def ar_row_partition(W: int, M: int, rank: int):
+    """(row_begin, row_count) of `rank`'s slice in the W-way row partition (two-shot share)."""
+    b, c = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(lib().ar_row_partition(W, M, rank, ctypes.byref(b), ctypes.byref(c)),
+           "ar_row_partition")
+    return int(b.value), int(c.value)
+
+
+def ar_all_gather(slices, out, stream=None) -> None:
+    """All-gather share: out[row_begin(j):row_begin(j)+row_count(j)] = slices[j] for all j."""
+    if out.dim() != 2:
+        raise ValueError("out must be [M, H]")
+    M, H = out.shape
+    W = len(slices)
+    if W == 0:
+        raise ValueError("need at least one slice")
+    ptrs = []
+    for j, t in enumerate(slices):
+        b, c = ar_row_partition(W, M, j)
+        if t.dtype != out.dtype or tuple(t.shape) != (c, H):
+            raise ValueError("slice %d must be [%d, %d] %s" % (j, c, H, out.dtype))
+        if c and (not t.is_cuda or t.device != out.device or not t.is_contiguous()):
+            raise ValueError("slice %d must be a contiguous tensor on %s" % (j, out.device))
+        ptrs.append(t.data_ptr() if c else 0)
+    if not out.is_contiguous() or not out.is_cuda:
+        raise ValueError("out must be a contiguous GPU tensor")
+    arr = (ctypes.c_void_p * W)(*ptrs)
+    st = lib().ar_all_gather(arr, W, M, H, dtype_code(out.dtype), out.data_ptr(),
+                             _stream_handle(stream, out.device))
+    _check(st, "ar_all_gather")
 
 
 def ar_supports(pattern: int, W: int, M: int, H: int, dtype: int) -> int:

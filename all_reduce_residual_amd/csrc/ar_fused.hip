@@ -7,6 +7,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <climits>
 #include <cmath>
@@ -417,6 +418,71 @@ int run_norm(const void* const* inputs, int W, int64_t M, int64_t H, int dtype,
   return e == hipSuccess ? AR_OK : AR_ERR_LAUNCH;
 }
 
+// ---- two-shot share ------------------------------------------------------------------------------
+
+void row_slice(int W, int64_t M, int rank, int64_t* begin, int64_t* count) {
+  // floor(rank * M / W) without overflow for any M < 2^62 / 64.
+  const int64_t b = (M / W) * rank + ((M % W) * rank) / W;
+  const int64_t e = (M / W) * (rank + 1) + ((M % W) * (rank + 1)) / W;
+  *begin = b;
+  *count = e - b;
+}
+
+int run_gather(const void* const* slices, int W, int64_t M, int64_t H, int dtype, void* out,
+               void* stream) {
+  // The sum pattern's shape rules plus whole 16-byte vectors per row (every slice then starts
+  // on a vector boundary of `out`).
+  int st = check_shape(AR_PATTERN_ALLREDUCE, W, M, H, dtype);
+  if (st != AR_OK) return st;
+  if (H % (kVecBytes / elem_size(dtype)) != 0) return AR_ERR_UNSUPPORTED;
+  if (M == 0) return AR_OK;
+  if (!slices || !out) return AR_ERR_INVALID_ARG;
+  if (!aligned16(out)) return AR_ERR_MISALIGNED;
+  const int64_t es = elem_size(dtype);
+  const int64_t V = H / (kVecBytes / es);
+  arf::GatherArgs a;
+  uint64_t skip = 0;
+  const Range o = range_of(out, M * H * es);
+  for (int j = 0; j < W; ++j) {
+    int64_t b, c;
+    row_slice(W, M, j, &b, &c);
+    a.vec_begin[j] = b * V;
+    a.src[j] = static_cast<const u32x4*>(slices[j]);
+    if (c == 0) {
+      skip |= uint64_t(1) << j;  // empty slice: pointer may be null
+      continue;
+    }
+    if (!slices[j]) return AR_ERR_INVALID_ARG;
+    if (!aligned16(slices[j])) return AR_ERR_MISALIGNED;
+    const Range in = range_of(slices[j], c * H * es);
+    const Range place = range_of(static_cast<const char*>(out) + b * H * es, c * H * es);
+    if (in.lo == place.lo) {
+      skip |= uint64_t(1) << j;  // already in place
+    } else if (overlap(in, o)) {
+      return AR_ERR_ALIAS;
+    }
+  }
+  a.vec_begin[W] = M * V;
+  int64_t max_vecs = 0;
+  for (int j = 0; j < W; ++j) max_vecs = std::max(max_vecs, a.vec_begin[j + 1] - a.vec_begin[j]);
+  int cu = 0;
+  st = query_cu_count(&cu);
+  if (st != AR_OK) return st;
+  // 256-thread blocks, one vector per thread; at most ~16 blocks per CU over all slices.
+  const int threads = 256;
+  const int64_t per_slice_cap = std::max<int64_t>(1, int64_t(cu) * 16 / W);
+  const int gx = static_cast<int>(std::min(ceil_div(max_vecs, threads), per_slice_cap));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  u32x4* dst = static_cast<u32x4*>(out);
+  void* args[] = {&a, &dst, &skip};
+  // Large gathers stream past every cache; small ones keep ordinary stores.
+  const bool nt = M * H * es >= (int64_t(64) << 20);
+  const void* fn = nt ? reinterpret_cast<const void*>(&arf::ar_gather_kernel<true>)
+                      : reinterpret_cast<const void*>(&arf::ar_gather_kernel<false>);
+  const hipError_t e = hipLaunchKernel(fn, dim3(std::max(gx, 1), W), dim3(threads), args, 0, s);
+  return e == hipSuccess ? AR_OK : AR_ERR_LAUNCH;
+}
+
 }  // namespace
 
 // ---- C ABI ----------------------------------------------------------------------------------------
@@ -470,6 +536,18 @@ int ar_launch_config(int pattern, int W, int64_t M, int64_t H, int dtype, int cu
     plan_norm(W, M, H, dtype, cu, cfg);
   }
   return AR_OK;
+}
+
+int ar_row_partition(int W, int64_t M, int rank, int64_t* row_begin, int64_t* row_count) {
+  if (!row_begin || !row_count || W < 1 || W > AR_MAX_W || M < 0 || rank < 0 || rank >= W)
+    return AR_ERR_INVALID_ARG;
+  row_slice(W, M, rank, row_begin, row_count);
+  return AR_OK;
+}
+
+int ar_all_gather(const void* const* slices, int W, int64_t M, int64_t H, int dtype, void* out,
+                  void* stream) {
+  return run_gather(slices, W, M, H, dtype, out, stream);
 }
 
 const char* ar_status_string(int status) {

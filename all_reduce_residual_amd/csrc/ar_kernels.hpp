@@ -440,4 +440,32 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_kernel(
   }
 }
 
+// ---- all-gather share (two-shot) ----------------------------------------------------------------
+
+struct GatherArgs {
+  const u32x4* src[64];     // slice j, [row_count(j) * V] vectors
+  int64_t vec_begin[65];    // first vector of slice j in `out`; vec_begin[W] = M * V
+};
+
+// out[vec_begin[j] + i] = src[j][i].  blockIdx.y = slice; blocks of a slice walk its vectors
+// with a grid stride over blockIdx.x; slices whose bit is set in `skip` are already in place.
+template <bool kNtStore>
+__global__ __launch_bounds__(kMaxThreads) void ar_gather_kernel(GatherArgs a, u32x4* out,
+                                                                uint64_t skip) {
+  const int j = blockIdx.y;
+  if ((skip >> j) & 1u) return;
+  const int64_t begin = a.vec_begin[j];
+  const int64_t n = a.vec_begin[j + 1] - begin;
+  const u32x4* src = a.src[j];
+  u32x4* dst = out + begin;
+  const int64_t chunk = blockDim.x;
+  for (int64_t cbase = blockIdx.x * chunk; cbase < n; cbase += gridDim.x * chunk) {
+    const uint32_t i = threadIdx.x;
+    if (cbase + i < n) {
+      const uint32_t boff = i * 16u;
+      store_vec<kNtStore>(at(dst + cbase, boff), load_stream(at(src + cbase, boff)));
+    }
+  }
+}
+
 }  // namespace arf

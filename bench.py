@@ -177,6 +177,56 @@ class Case:
         return sorted(res)[len(res) // 2]
 
 
+class GatherCase(Case):
+    """All-gather share: W row slices of an [M, H] tensor gathered into it, R rotated sets."""
+
+    def __init__(self, ar, torch, W, M, H, dtype="bf16"):
+        self.ar, self.torch = ar, torch
+        self.pattern, self.W, self.M, self.H, self.dtype = "gather", W, M, H, dtype
+        tdt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[dtype]
+        self.esize = 4 if dtype == "fp32" else 2
+        self.bytes = 2 * M * H * self.esize            # every slice read once, out written once
+        self.R = max(1, min(4096, math.ceil(ROTATE_BYTES / self.bytes)))
+        self.src = torch.empty((self.R * M, H), dtype=tdt, device="cuda").normal_()
+        self.out = torch.empty_like(self.src)
+        self.fn = ar.lib().ar_all_gather
+        self.dt = ar.dtype_code(tdt)
+        self._keep = []
+        self.args = []
+        for r in range(self.R):
+            ptrs = []
+            for j in range(W):
+                b, c = ar.ar_row_partition(W, M, j)
+                ptrs.append(self.src[r * M + b:r * M + b + c].data_ptr() if c else 0)
+            arr = (ctypes.c_void_p * W)(*ptrs)
+            self._keep.append(arr)
+            self.args.append((arr, W, M, H, self.dt, self._sl(self.out, r)))
+        torch.cuda.synchronize()
+
+
+def two_shot_lines(ar, torch, W=8, H=7168, Ms=(128, 512, 2048)) -> list:
+    """One GPU's two-shot share: reduce-scatter of rank 0's row slice with the fused kernels,
+    then the all-gather of each output (hipGraph replay, rotated buffers)."""
+    lines = []
+    for m in Ms:
+        b, c = ar.ar_row_partition(W, m, 0)
+        g = GatherCase(ar, torch, W, m, H)
+        ag = g.time_graph(g.calls_per_batch(100))
+        del g
+        for pattern in ("rms", "sum"):
+            rs = Case(ar, torch, pattern, W, c, H)
+            us_rs = rs.time_graph(rs.calls_per_batch(100))
+            n_out = 2 if pattern == "rms" else 1
+            lines.append({"pattern": "kARResidualRMSNorm" if pattern == "rms" else "kAllReduce",
+                          "M": m, "slice_rows": c, "us_reduce_scatter_share": round(us_rs, 3),
+                          "us_all_gather_per_output": round(ag, 3),
+                          "us_share_total": round(us_rs + n_out * ag, 3)})
+            del rs
+            torch.cuda.empty_cache()
+            print("# two-shot %s" % json.dumps(lines[-1]), file=sys.stderr, flush=True)
+    return lines
+
+
 def check_headline_parity(ar, torch, case) -> dict:
     """Put the seeded workload inputs into rotation set 0 and compare sampled rows of both
     outputs with the oracle (residual_out bit-exact, norm_out within 1 ulp)."""
@@ -529,6 +579,7 @@ def main():
                 del c, warm
                 torch.cuda.empty_cache()
         result["sweep"] = sweep
+        result["two_shot_share"] = two_shot_lines(ar, torch)
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline()

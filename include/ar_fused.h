@@ -149,6 +149,32 @@ int ar_residual_rmsnorm_with_config(const void* const* inputs, int W, int64_t M,
                                     float eps, void* residual_out, void* norm_out, void* stream,
                                     const ar_launch_cfg_t* cfg);
 
+/* ---- two-shot share -----------------------------------------------------------------------
+ *
+ * The two-shot form of the all-reduce (named beside the one-shot form in the vLLM pull request
+ * "[Perf] Tune FlashInfer all-reduce selection on SM103", Tests, and the tokenspeed pull
+ * request, Summary) splits the rows among the W ranks: rank k reduces only its row slice
+ * (reduce-scatter), then every rank gathers the W reduced slices (all-gather).  Rows are
+ * independent, so rank k's reduce-scatter share is ar_sum / ar_residual_rmsnorm called on the
+ * row slice (pointers advanced by row_begin * H elements, M = row_count); ar_all_gather is the
+ * gather share.  Both use the partition below. */
+
+/* Row slice of `rank` (0 <= rank < W) in the W-way partition of M rows:
+ * row_begin = floor(rank * M / W), row_count = floor((rank + 1) * M / W) - row_begin.
+ * Pure host arithmetic.  AR_OK, or AR_ERR_INVALID_ARG for bad arguments or null outputs. */
+int ar_row_partition(int W, int64_t M, int rank, int64_t* row_begin, int64_t* row_count);
+
+/* All-gather share: out[row_begin(j) + i, :] = slices[j][i, :] for every rank j and every row i
+ * of its slice (the partition above), one launch for all W slices.
+ *   slices : host array of W device pointers; slices[j] is [row_count(j), H] of type `dtype`
+ *            (row-major, contiguous, 16-byte aligned).  A slice that already sits at its place
+ *            in `out` (slices[j] == out + row_begin(j) * H) is skipped.
+ *   out    : device [M, H]; must not partially overlap any slice
+ * W must be in the supported set; H must be a multiple of 16 / sizeof(T).  A byte copy: the
+ * result is bit-identical to the slices. */
+int ar_all_gather(const void* const* slices, int W, int64_t M, int64_t H, int dtype, void* out,
+                  void* stream);
+
 /* Static, human-readable name of a status code ("unknown status" for anything else). */
 const char* ar_status_string(int status);
 

@@ -181,3 +181,19 @@ def ar_residual_rmsnorm(inputs, residual, gamma, eps: float, dtype: str, rows=No
     if debug:
         return residual_out, norm_out, y, rstd
     return residual_out, norm_out
+
+
+# ---- two-shot share --------------------------------------------------------------------------
+
+def row_partition(W: int, M: int, rank: int):
+    """(row_begin, row_count) of `rank` in the W-way split of M rows: row_begin(j) = floor(j*M/W)."""
+    if not (1 <= W and 0 <= rank < W and M >= 0):
+        raise ValueError("bad partition arguments")
+    b = (rank * M) // W
+    e = ((rank + 1) * M) // W
+    return b, e - b
+
+
+def all_gather(slices) -> np.ndarray:
+    """The gathered tensor: the W row slices stacked in rank order."""
+    return np.concatenate(list(slices), axis=0)

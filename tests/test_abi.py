@@ -23,7 +23,8 @@ def test_exports_every_declared_function(L):
     names = ar.header_functions()
     assert set(names) == {"ar_sum", "ar_residual_rmsnorm", "ar_supports", "ar_launch_config",
                           "ar_sum_with_config", "ar_residual_rmsnorm_with_config",
-                          "ar_status_string", "ar_device_cu_count"}
+                          "ar_status_string", "ar_device_cu_count", "ar_row_partition",
+                          "ar_all_gather"}
     for n in names:
         assert hasattr(L, n), n
 
