@@ -468,17 +468,17 @@ int run_gather(const void* const* slices, int W, int64_t M, int64_t H, int dtype
   int cu = 0;
   st = query_cu_count(&cu);
   if (st != AR_OK) return st;
-  // 256-thread blocks, one vector per thread; at most ~16 blocks per CU over all slices.
-  const int threads = 256;
-  const int64_t per_slice_cap = std::max<int64_t>(1, int64_t(cu) * 16 / W);
-  const int gx = static_cast<int>(std::min(ceil_div(max_vecs, threads), per_slice_cap));
+  // Measured on MI355X: large gathers (>= 4096 vectors per CU) run best as single-wave blocks
+  // covering every vector once; smaller ones as 256-thread blocks, at most 16 per CU over all
+  // slices.  Non-temporal stores won at every size.
+  const bool large = M * V >= int64_t(cu) * 4096;
+  const int threads = large ? 64 : 256;
+  const int64_t cap = large ? int64_t(INT_MAX) : std::max<int64_t>(1, int64_t(cu) * 16 / W);
+  const int gx = static_cast<int>(std::min(ceil_div(max_vecs, threads), cap));
   hipStream_t s = static_cast<hipStream_t>(stream);
   u32x4* dst = static_cast<u32x4*>(out);
   void* args[] = {&a, &dst, &skip};
-  // Large gathers stream past every cache; small ones keep ordinary stores.
-  const bool nt = M * H * es >= (int64_t(64) << 20);
-  const void* fn = nt ? reinterpret_cast<const void*>(&arf::ar_gather_kernel<true>)
-                      : reinterpret_cast<const void*>(&arf::ar_gather_kernel<false>);
+  const void* fn = reinterpret_cast<const void*>(&arf::ar_gather_kernel<true>);
   const hipError_t e = hipLaunchKernel(fn, dim3(std::max(gx, 1), W), dim3(threads), args, 0, s);
   return e == hipSuccess ? AR_OK : AR_ERR_LAUNCH;
 }

@@ -170,8 +170,8 @@ int ar_row_partition(int W, int64_t M, int rank, int64_t* row_begin, int64_t* ro
  *            (row-major, contiguous, 16-byte aligned).  A slice that already sits at its place
  *            in `out` (slices[j] == out + row_begin(j) * H) is skipped.
  *   out    : device [M, H]; must not partially overlap any slice
- * W must be in the supported set; H must be a multiple of 16 / sizeof(T).  A byte copy: the
- * result is bit-identical to the slices. */
+ * W must be in the supported set; H must be a multiple of 16 / sizeof(T).  A byte copy (non-
+ * temporal loads and stores): the result is bit-identical to the slices. */
 int ar_all_gather(const void* const* slices, int W, int64_t M, int64_t H, int dtype, void* out,
                   void* stream);
 
