@@ -77,6 +77,11 @@ def lib():
             "ar_supports": [i32, i32, i64, i64, i32],
             "ar_launch_config": [i32, i32, i64, i64, i32, i32, cfgp],
             "ar_status_string": [i32],
+            "ar_lamport_arm": [vp, i32, i64, i64, i32, vp],
+            "ar_lamport_push": [vp, i32, vp, i32, i64, i64, i32, vp],
+            "ar_lamport_sum": [vp, i32, i64, i64, i32, vp, vp, ctypes.c_uint32, vp],
+            "ar_lamport_residual_rmsnorm": [vp, i32, i64, i64, i32, vp, vp, f32, vp, vp, vp,
+                                            ctypes.c_uint32, vp],
             "ar_row_partition": [i32, i64, i32, ctypes.POINTER(ctypes.c_int64),
                                  ctypes.POINTER(ctypes.c_int64)],
             "ar_all_gather": [vp, i32, i64, i64, i32, vp, vp],
@@ -204,6 +209,62 @@ def ar_all_gather(slices, out, stream=None) -> None:
     st = lib().ar_all_gather(arr, W, M, H, dtype_code(out.dtype), out.data_ptr(),
                              _stream_handle(stream, out.device))
     _check(st, "ar_all_gather")
+
+
+def _check_rbuf(rbuf, like=None):
+    if rbuf.dim() != 3 or not rbuf.is_cuda or not rbuf.is_contiguous():
+        raise ValueError("rbuf must be a contiguous [W, M, H] GPU tensor")
+    if like is not None and (like.dtype != rbuf.dtype or tuple(like.shape) != tuple(rbuf.shape[1:])
+                             or like.device != rbuf.device or not like.is_contiguous()):
+        raise ValueError("tensor must be a contiguous [M, H] %s on %s" % (rbuf.dtype, rbuf.device))
+    W, M, H = rbuf.shape
+    return W, M, H, dtype_code(rbuf.dtype)
+
+
+def _check_status(status, device):
+    import torch
+    if status.dtype != torch.int32 or status.numel() < 1 or status.device != device:
+        raise ValueError("status must be an int32 GPU tensor on %s" % device)
+
+
+def ar_lamport_arm(rbuf, stream=None) -> None:
+    """Empty every slot of the receive buffer rbuf ([W, M, H])."""
+    W, M, H, dt = _check_rbuf(rbuf)
+    _check(lib().ar_lamport_arm(rbuf.data_ptr(), W, M, H, dt, _stream_handle(stream, rbuf.device)),
+           "ar_lamport_arm")
+
+
+def ar_lamport_push(partial, rank: int, rbuf, stream=None) -> None:
+    """Producer of `rank`: write `partial` ([M, H]) into its slot of rbuf."""
+    W, M, H, dt = _check_rbuf(rbuf, partial)
+    _check(lib().ar_lamport_push(partial.data_ptr(), rank, rbuf.data_ptr(), W, M, H, dt,
+                                 _stream_handle(stream, rbuf.device)), "ar_lamport_push")
+
+
+def ar_lamport_sum(rbuf, out, status, spin_limit: int = 0, stream=None) -> None:
+    """Consumer, kAllReduce: out = sum of the W slots; re-empties them."""
+    W, M, H, dt = _check_rbuf(rbuf, out)
+    _check_status(status, rbuf.device)
+    _check(lib().ar_lamport_sum(rbuf.data_ptr(), W, M, H, dt, out.data_ptr(), status.data_ptr(),
+                                spin_limit, _stream_handle(stream, rbuf.device)), "ar_lamport_sum")
+
+
+def ar_lamport_residual_rmsnorm(rbuf, residual, gamma, eps: float, residual_out, norm_out, status,
+                                spin_limit: int = 0, stream=None) -> None:
+    """Consumer, kARResidualRMSNorm over the W slots; re-empties them."""
+    import torch
+    W, M, H, dt = _check_rbuf(rbuf, residual)
+    _check_rbuf(rbuf, residual_out)
+    _check_rbuf(rbuf, norm_out)
+    _check_status(status, rbuf.device)
+    if gamma.dtype != torch.float32 or tuple(gamma.shape) != (H,) or not gamma.is_contiguous() \
+            or gamma.device != rbuf.device:
+        raise ValueError("gamma must be a contiguous float32 [%d] tensor on %s" % (H, rbuf.device))
+    st = lib().ar_lamport_residual_rmsnorm(
+        rbuf.data_ptr(), W, M, H, dt, residual.data_ptr(), gamma.data_ptr(), float(eps),
+        residual_out.data_ptr(), norm_out.data_ptr(), status.data_ptr(), spin_limit,
+        _stream_handle(stream, rbuf.device))
+    _check(st, "ar_lamport_residual_rmsnorm")
 
 
 def ar_supports(pattern: int, W: int, M: int, H: int, dtype: int) -> int:

@@ -1,19 +1,27 @@
-"""Compile the HIP library (gfx950) into all_reduce_residual_amd/libar_fused.so."""
+"""Compile the HIP library (gfx950) into all_reduce_residual_amd/libar_fused.so.
+
+The kernels are instantiated per element type in separate translation units (csrc/inst_*.hip);
+they compile in parallel and link with the host side (csrc/ar_fused.hip) into one shared
+library.
+"""
 from __future__ import annotations
 
 import os
 import subprocess
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "ar_fused.hip")
+CSRC = os.path.join(PKG, "csrc")
+SOURCES = ["ar_fused.hip", "inst_bf16.hip", "inst_f16.hip", "inst_f32.hip"]
 LIB = os.path.join(PKG, "libar_fused.so")
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from fusing binary32 adds/multiplies into packed
 # two-lane instructions; every add of the rank chain is a plain v_add_f32.
 HIPCC_FLAGS = [
-    "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
@@ -25,13 +33,23 @@ def hipcc() -> str:
     return cand if os.path.exists(cand) else "hipcc"
 
 
-def build(extra_flags=(), out: str = LIB) -> str:
+def build(extra_flags=(), out: str = LIB, jobs: int = 0) -> str:
     """Build the library and return its path (always recompiles)."""
-    tmp = out + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + HIPCC_FLAGS + list(extra_flags) + [
-        "-I" + os.path.join(ROOT, "include"), "-o", tmp, SRC]
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, out)
+    inc = "-I" + os.path.join(ROOT, "include")
+    jobs = jobs or min(len(SOURCES), os.cpu_count() or 1)
+    with tempfile.TemporaryDirectory(prefix="ar_build_") as tmpdir:
+        def compile_one(src):
+            obj = os.path.join(tmpdir, os.path.splitext(src)[0] + ".o")
+            subprocess.run([hipcc()] + HIPCC_FLAGS + list(extra_flags) +
+                           [inc, "-c", "-o", obj, os.path.join(CSRC, src)], check=True)
+            return obj
+
+        with ThreadPoolExecutor(max_workers=jobs) as pool:
+            objs = list(pool.map(compile_one, SOURCES))
+        tmp = out + ".tmp%d" % os.getpid()
+        subprocess.run([hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs,
+                       check=True)
+        os.replace(tmp, out)
     return out
 
 

@@ -1,0 +1,247 @@
+// ar_dispatch.hpp -- launch helpers shared by the per-element-type translation units.
+//
+// Each inst_<type>.hip instantiates the kernels of one element type and exports the
+// launch_<pattern>_<type> functions declared at the bottom; ar_fused.hip (validation, the
+// launch-shape heuristic and the C ABI) calls them.  Splitting the ~300 kernel instantiations
+// over several translation units lets the build compile them in parallel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "ar_fused.h"
+#include "ar_kernels.hpp"
+
+namespace arfh {
+
+using arf::F16;
+using arf::F32;
+using arf::Bf16;
+using arf::RankPtrs;
+using arf::u32x4;
+using arf::f32x4;
+
+template <int W>
+RankPtrs<W> pack_ptrs(const void* const* inputs) {
+  RankPtrs<W> p;
+  for (int r = 0; r < W; ++r) p.p[r] = static_cast<const u32x4*>(inputs[r]);
+  return p;
+}
+
+template <class T, int W, int U>
+hipError_t launch_sum_u(const void* const* inputs, void* out, int64_t nvec, int tail,
+                        const ar_launch_cfg_t& c, hipStream_t s) {
+  RankPtrs<W> p = pack_ptrs<W>(inputs);
+  u32x4* o = static_cast<u32x4*>(out);
+  arf::StreamSource src;
+  void* args[] = {&p, &o, &nvec, &tail, &src};
+  const void* fn = c.nt_store ? reinterpret_cast<const void*>(&arf::ar_sum_kernel<T, W, U, true>)
+                              : reinterpret_cast<const void*>(&arf::ar_sum_kernel<T, W, U, false>);
+  return hipLaunchKernel(fn, dim3(c.grid), dim3(c.threads_per_block), args, 0, s);
+}
+
+template <class T, int W>
+hipError_t launch_sum_w(const void* const* inputs, void* out, int64_t nvec, int tail,
+                        const ar_launch_cfg_t& c, hipStream_t s) {
+  switch (c.vecs_per_thread) {
+    case 1: return launch_sum_u<T, W, 1>(inputs, out, nvec, tail, c, s);
+    case 2: return launch_sum_u<T, W, 2>(inputs, out, nvec, tail, c, s);
+    default: return launch_sum_u<T, W, 4>(inputs, out, nvec, tail, c, s);
+  }
+}
+
+template <class T>
+inline hipError_t launch_sum_t(const void* const* inputs, int W, void* out, int64_t nvec, int tail,
+                        const ar_launch_cfg_t& c, hipStream_t s) {
+  switch (W) {
+    case 1: return launch_sum_w<T, 1>(inputs, out, nvec, tail, c, s);
+    case 2: return launch_sum_w<T, 2>(inputs, out, nvec, tail, c, s);
+    case 4: return launch_sum_w<T, 4>(inputs, out, nvec, tail, c, s);
+    case 8: return launch_sum_w<T, 8>(inputs, out, nvec, tail, c, s);
+    case 16: return launch_sum_w<T, 16>(inputs, out, nvec, tail, c, s);
+    case 32: return launch_sum_w<T, 32>(inputs, out, nvec, tail, c, s);
+    default: return launch_sum_w<T, 64>(inputs, out, nvec, tail, c, s);
+  }
+}
+
+template <class T, int W, int VPT>
+hipError_t launch_norm_v(const void* const* inputs, const void* residual, const float* gamma,
+                         float eps, void* residual_out, void* norm_out, int64_t M, int64_t H,
+                         const ar_launch_cfg_t& c, hipStream_t s) {
+  RankPtrs<W> p = pack_ptrs<W>(inputs);
+  const u32x4* res = static_cast<const u32x4*>(residual);
+  const f32x4* gam = reinterpret_cast<const f32x4*>(gamma);
+  u32x4* ro = static_cast<u32x4*>(residual_out);
+  u32x4* no = static_cast<u32x4*>(norm_out);
+  int V = static_cast<int>(H / T::kVec);
+  int L = c.lanes_per_row;
+  int R = c.rows_per_block;
+  float count_h = static_cast<float>(H);  // exact: H <= 2^16
+  arf::StreamSource src;
+  void* args[] = {&p, &res, &gam, &ro, &no, &M, &V, &L, &R, &eps, &count_h, &src};
+  const void* fn =
+      c.nt_store ? reinterpret_cast<const void*>(&arf::ar_norm_kernel<T, W, VPT, true>)
+                 : reinterpret_cast<const void*>(&arf::ar_norm_kernel<T, W, VPT, false>);
+  return hipLaunchKernel(fn, dim3(c.grid), dim3(c.threads_per_block), args, 0, s);
+}
+
+template <class T, int W>
+hipError_t launch_norm_w(const void* const* inputs, const void* residual, const float* gamma,
+                         float eps, void* residual_out, void* norm_out, int64_t M, int64_t H,
+                         const ar_launch_cfg_t& c, hipStream_t s) {
+  switch (c.vecs_per_thread) {
+    case 1:
+      return launch_norm_v<T, W, 1>(inputs, residual, gamma, eps, residual_out, norm_out, M, H,
+                                    c, s);
+    case 2:
+      return launch_norm_v<T, W, 2>(inputs, residual, gamma, eps, residual_out, norm_out, M, H,
+                                    c, s);
+    case 4:
+      return launch_norm_v<T, W, 4>(inputs, residual, gamma, eps, residual_out, norm_out, M, H,
+                                    c, s);
+    default:
+      return launch_norm_v<T, W, 8>(inputs, residual, gamma, eps, residual_out, norm_out, M, H,
+                                    c, s);
+  }
+}
+
+template <class T>
+inline hipError_t launch_norm_t(const void* const* inputs, int W, const void* residual,
+                         const float* gamma, float eps, void* residual_out, void* norm_out,
+                         int64_t M, int64_t H, const ar_launch_cfg_t& c, hipStream_t s) {
+#define AR_NORM_W(w)                                                                        \
+  case w:                                                                                   \
+    return launch_norm_w<T, w>(inputs, residual, gamma, eps, residual_out, norm_out, M, H, \
+                               c, s);
+  switch (W) {
+    AR_NORM_W(1)
+    AR_NORM_W(2)
+    AR_NORM_W(4)
+    AR_NORM_W(8)
+    AR_NORM_W(16)
+    AR_NORM_W(32)
+    default:
+      return launch_norm_w<T, 64>(inputs, residual, gamma, eps, residual_out, norm_out, M, H, c,
+                                  s);
+  }
+#undef AR_NORM_W
+}
+
+
+// ---- Lamport-style exchange (receive buffer of W slots, slot r at rbuf + r * slot_vecs) -----------
+
+template <int W>
+RankPtrs<W> slot_ptrs(const void* rbuf, int64_t slot_vecs) {
+  RankPtrs<W> p;
+  for (int r = 0; r < W; ++r) p.p[r] = static_cast<const u32x4*>(rbuf) + r * slot_vecs;
+  return p;
+}
+
+template <class T, int W>
+hipError_t launch_lamport_sum_w(void* rbuf, int64_t slot_vecs, void* out, int64_t nvec,
+                                const ar_launch_cfg_t& c, arf::LamportSource src, hipStream_t s) {
+  RankPtrs<W> p = slot_ptrs<W>(rbuf, slot_vecs);
+  u32x4* o = static_cast<u32x4*>(out);
+  int tail = 0;
+  void* args[] = {&p, &o, &nvec, &tail, &src};
+  const void* fn =
+      reinterpret_cast<const void*>(&arf::ar_sum_kernel<T, W, 1, true, arf::LamportSource>);
+  return hipLaunchKernel(fn, dim3(c.grid), dim3(c.threads_per_block), args, 0, s);
+}
+
+template <class T, int W, int VPT>
+hipError_t launch_lamport_norm_v(void* rbuf, int64_t slot_vecs, const void* residual,
+                                 const float* gamma, float eps, void* residual_out,
+                                 void* norm_out, int64_t M, int64_t H, const ar_launch_cfg_t& c,
+                                 arf::LamportSource src, hipStream_t s) {
+  RankPtrs<W> p = slot_ptrs<W>(rbuf, slot_vecs);
+  const u32x4* res = static_cast<const u32x4*>(residual);
+  const f32x4* gam = reinterpret_cast<const f32x4*>(gamma);
+  u32x4* ro = static_cast<u32x4*>(residual_out);
+  u32x4* no = static_cast<u32x4*>(norm_out);
+  int V = static_cast<int>(H / T::kVec);
+  int L = c.lanes_per_row;
+  int R = c.rows_per_block;
+  float count_h = static_cast<float>(H);
+  void* args[] = {&p, &res, &gam, &ro, &no, &M, &V, &L, &R, &eps, &count_h, &src};
+  const void* fn = reinterpret_cast<const void*>(
+      &arf::ar_norm_kernel<T, W, VPT, true, arf::LamportSource>);
+  return hipLaunchKernel(fn, dim3(c.grid), dim3(c.threads_per_block), args, 0, s);
+}
+
+#define AR_W_SWITCH(W, CALL)        \
+  switch (W) {                      \
+    case 1: return CALL(1);         \
+    case 2: return CALL(2);         \
+    case 4: return CALL(4);         \
+    case 8: return CALL(8);         \
+    case 16: return CALL(16);       \
+    case 32: return CALL(32);       \
+    default: return CALL(64);       \
+  }
+
+template <class T>
+inline hipError_t launch_lamport_sum_t(void* rbuf, int W, int64_t M, int64_t H, void* out,
+                                       const ar_launch_cfg_t& c, arf::LamportSource src,
+                                       hipStream_t s) {
+  const int64_t nvec = M * H / T::kVec;
+#define AR_CALL(w) launch_lamport_sum_w<T, w>(rbuf, nvec, out, nvec, c, src, s)
+  AR_W_SWITCH(W, AR_CALL)
+#undef AR_CALL
+}
+
+template <class T>
+inline hipError_t launch_lamport_norm_t(void* rbuf, int W, const void* residual,
+                                        const float* gamma, float eps, void* residual_out,
+                                        void* norm_out, int64_t M, int64_t H,
+                                        const ar_launch_cfg_t& c, arf::LamportSource src,
+                                        hipStream_t s) {
+  const int64_t nvec = M * H / T::kVec;
+  if (c.vecs_per_thread == 1) {
+#define AR_CALL(w) \
+  launch_lamport_norm_v<T, w, 1>(rbuf, nvec, residual, gamma, eps, residual_out, norm_out, M, H, c, src, s)
+    AR_W_SWITCH(W, AR_CALL)
+#undef AR_CALL
+  }
+#define AR_CALL(w) \
+  launch_lamport_norm_v<T, w, 2>(rbuf, nvec, residual, gamma, eps, residual_out, norm_out, M, H, c, src, s)
+  AR_W_SWITCH(W, AR_CALL)
+#undef AR_CALL
+}
+
+template <class T>
+inline hipError_t launch_lamport_push_t(const void* partial, void* slot, int64_t nvec, int grid,
+                                        hipStream_t s) {
+  const u32x4* src = static_cast<const u32x4*>(partial);
+  u32x4* dst = static_cast<u32x4*>(slot);
+  void* args[] = {&src, &dst, &nvec};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&arf::ar_lamport_push_kernel<T>),
+                         dim3(grid), dim3(256), args, 0, s);
+}
+
+// ---- per-element-type entry points (defined in inst_bf16.hip, inst_f16.hip, inst_f32.hip) ----
+
+#define AR_DECLARE_LAUNCHERS(suffix)                                                         \
+  hipError_t launch_sum_##suffix(const void* const* inputs, int W, void* out, int64_t nvec,  \
+                                 int tail, const ar_launch_cfg_t& c, hipStream_t s);         \
+  hipError_t launch_norm_##suffix(const void* const* inputs, int W, const void* residual,    \
+                                  const float* gamma, float eps, void* residual_out,         \
+                                  void* norm_out, int64_t M, int64_t H,                      \
+                                  const ar_launch_cfg_t& c, hipStream_t s);                  \
+  hipError_t launch_lamport_sum_##suffix(void* rbuf, int W, int64_t M, int64_t H, void* out,  \
+                                         const ar_launch_cfg_t& c, arf::LamportSource src,    \
+                                         hipStream_t s);                                      \
+  hipError_t launch_lamport_norm_##suffix(void* rbuf, int W, const void* residual,            \
+                                          const float* gamma, float eps, void* residual_out,  \
+                                          void* norm_out, int64_t M, int64_t H,               \
+                                          const ar_launch_cfg_t& c, arf::LamportSource src,   \
+                                          hipStream_t s);                                     \
+  hipError_t launch_lamport_push_##suffix(const void* partial, void* slot, int64_t nvec,      \
+                                          int grid, hipStream_t s);
+AR_DECLARE_LAUNCHERS(bf16)
+AR_DECLARE_LAUNCHERS(f16)
+AR_DECLARE_LAUNCHERS(f32)
+#undef AR_DECLARE_LAUNCHERS
+
+}  // namespace arfh

@@ -1,5 +1,6 @@
 // ar_fused.hip -- host side of the C ABI declared in include/ar_fused.h: argument validation,
-// the launch-shape heuristic, and dispatch to the gfx950 kernels in ar_kernels.hpp.
+// the launch-shape heuristic, and dispatch to the gfx950 kernels in ar_kernels.hpp (instantiated
+// per element type in inst_*.hip; the all-gather kernel is instantiated here).
 //
 // Nothing here allocates device memory or synchronises: each entry point validates, picks a
 // launch shape and enqueues exactly one kernel on the caller's stream.  Validation runs before
@@ -13,17 +14,13 @@
 #include <cmath>
 #include <cstdint>
 
+#include "ar_dispatch.hpp"
 #include "ar_fused.h"
 #include "ar_kernels.hpp"
 
 namespace {
 
-using arf::F16;
-using arf::F32;
-using arf::Bf16;
-using arf::RankPtrs;
 using arf::u32x4;
-using arf::f32x4;
 
 constexpr int kVecBytes = 16;
 
@@ -195,110 +192,6 @@ int check_cfg(int pattern, int64_t H, int dtype, const ar_launch_cfg_t* c) {
 
 // ---- dispatch -----------------------------------------------------------------------------------
 
-template <int W>
-RankPtrs<W> pack_ptrs(const void* const* inputs) {
-  RankPtrs<W> p;
-  for (int r = 0; r < W; ++r) p.p[r] = static_cast<const u32x4*>(inputs[r]);
-  return p;
-}
-
-template <class T, int W, int U>
-hipError_t launch_sum_u(const void* const* inputs, void* out, int64_t nvec, int tail,
-                        const ar_launch_cfg_t& c, hipStream_t s) {
-  RankPtrs<W> p = pack_ptrs<W>(inputs);
-  u32x4* o = static_cast<u32x4*>(out);
-  void* args[] = {&p, &o, &nvec, &tail};
-  const void* fn = c.nt_store ? reinterpret_cast<const void*>(&arf::ar_sum_kernel<T, W, U, true>)
-                              : reinterpret_cast<const void*>(&arf::ar_sum_kernel<T, W, U, false>);
-  return hipLaunchKernel(fn, dim3(c.grid), dim3(c.threads_per_block), args, 0, s);
-}
-
-template <class T, int W>
-hipError_t launch_sum_w(const void* const* inputs, void* out, int64_t nvec, int tail,
-                        const ar_launch_cfg_t& c, hipStream_t s) {
-  switch (c.vecs_per_thread) {
-    case 1: return launch_sum_u<T, W, 1>(inputs, out, nvec, tail, c, s);
-    case 2: return launch_sum_u<T, W, 2>(inputs, out, nvec, tail, c, s);
-    default: return launch_sum_u<T, W, 4>(inputs, out, nvec, tail, c, s);
-  }
-}
-
-template <class T>
-hipError_t launch_sum_t(const void* const* inputs, int W, void* out, int64_t nvec, int tail,
-                        const ar_launch_cfg_t& c, hipStream_t s) {
-  switch (W) {
-    case 1: return launch_sum_w<T, 1>(inputs, out, nvec, tail, c, s);
-    case 2: return launch_sum_w<T, 2>(inputs, out, nvec, tail, c, s);
-    case 4: return launch_sum_w<T, 4>(inputs, out, nvec, tail, c, s);
-    case 8: return launch_sum_w<T, 8>(inputs, out, nvec, tail, c, s);
-    case 16: return launch_sum_w<T, 16>(inputs, out, nvec, tail, c, s);
-    case 32: return launch_sum_w<T, 32>(inputs, out, nvec, tail, c, s);
-    default: return launch_sum_w<T, 64>(inputs, out, nvec, tail, c, s);
-  }
-}
-
-template <class T, int W, int VPT>
-hipError_t launch_norm_v(const void* const* inputs, const void* residual, const float* gamma,
-                         float eps, void* residual_out, void* norm_out, int64_t M, int64_t H,
-                         const ar_launch_cfg_t& c, hipStream_t s) {
-  RankPtrs<W> p = pack_ptrs<W>(inputs);
-  const u32x4* res = static_cast<const u32x4*>(residual);
-  const f32x4* gam = reinterpret_cast<const f32x4*>(gamma);
-  u32x4* ro = static_cast<u32x4*>(residual_out);
-  u32x4* no = static_cast<u32x4*>(norm_out);
-  int V = static_cast<int>(H / T::kVec);
-  int L = c.lanes_per_row;
-  int R = c.rows_per_block;
-  float count_h = static_cast<float>(H);  // exact: H <= 2^16
-  void* args[] = {&p, &res, &gam, &ro, &no, &M, &V, &L, &R, &eps, &count_h};
-  const void* fn =
-      c.nt_store ? reinterpret_cast<const void*>(&arf::ar_norm_kernel<T, W, VPT, true>)
-                 : reinterpret_cast<const void*>(&arf::ar_norm_kernel<T, W, VPT, false>);
-  return hipLaunchKernel(fn, dim3(c.grid), dim3(c.threads_per_block), args, 0, s);
-}
-
-template <class T, int W>
-hipError_t launch_norm_w(const void* const* inputs, const void* residual, const float* gamma,
-                         float eps, void* residual_out, void* norm_out, int64_t M, int64_t H,
-                         const ar_launch_cfg_t& c, hipStream_t s) {
-  switch (c.vecs_per_thread) {
-    case 1:
-      return launch_norm_v<T, W, 1>(inputs, residual, gamma, eps, residual_out, norm_out, M, H,
-                                    c, s);
-    case 2:
-      return launch_norm_v<T, W, 2>(inputs, residual, gamma, eps, residual_out, norm_out, M, H,
-                                    c, s);
-    case 4:
-      return launch_norm_v<T, W, 4>(inputs, residual, gamma, eps, residual_out, norm_out, M, H,
-                                    c, s);
-    default:
-      return launch_norm_v<T, W, 8>(inputs, residual, gamma, eps, residual_out, norm_out, M, H,
-                                    c, s);
-  }
-}
-
-template <class T>
-hipError_t launch_norm_t(const void* const* inputs, int W, const void* residual,
-                         const float* gamma, float eps, void* residual_out, void* norm_out,
-                         int64_t M, int64_t H, const ar_launch_cfg_t& c, hipStream_t s) {
-#define AR_NORM_W(w)                                                                        \
-  case w:                                                                                   \
-    return launch_norm_w<T, w>(inputs, residual, gamma, eps, residual_out, norm_out, M, H, \
-                               c, s);
-  switch (W) {
-    AR_NORM_W(1)
-    AR_NORM_W(2)
-    AR_NORM_W(4)
-    AR_NORM_W(8)
-    AR_NORM_W(16)
-    AR_NORM_W(32)
-    default:
-      return launch_norm_w<T, 64>(inputs, residual, gamma, eps, residual_out, norm_out, M, H, c,
-                                  s);
-  }
-#undef AR_NORM_W
-}
-
 // ---- argument validation shared by the entry points ----------------------------------------------
 
 int validate_sum(const void* const* inputs, int W, int64_t M, int64_t H, int dtype,
@@ -373,9 +266,9 @@ int run_sum(const void* const* inputs, int W, int64_t M, int64_t H, int dtype, v
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   switch (dtype) {
-    case AR_DTYPE_FP32: e = launch_sum_t<F32>(inputs, W, out, nvec, tail, cfg, s); break;
-    case AR_DTYPE_FP16: e = launch_sum_t<F16>(inputs, W, out, nvec, tail, cfg, s); break;
-    default: e = launch_sum_t<Bf16>(inputs, W, out, nvec, tail, cfg, s); break;
+    case AR_DTYPE_FP32: e = arfh::launch_sum_f32(inputs, W, out, nvec, tail, cfg, s); break;
+    case AR_DTYPE_FP16: e = arfh::launch_sum_f16(inputs, W, out, nvec, tail, cfg, s); break;
+    default: e = arfh::launch_sum_bf16(inputs, W, out, nvec, tail, cfg, s); break;
   }
   return e == hipSuccess ? AR_OK : AR_ERR_LAUNCH;
 }
@@ -403,16 +296,16 @@ int run_norm(const void* const* inputs, int W, int64_t M, int64_t H, int dtype,
   hipError_t e;
   switch (dtype) {
     case AR_DTYPE_FP32:
-      e = launch_norm_t<F32>(inputs, W, residual, gamma, eps, residual_out, norm_out, M, H, cfg,
-                             s);
+      e = arfh::launch_norm_f32(inputs, W, residual, gamma, eps, residual_out, norm_out, M, H,
+                                cfg, s);
       break;
     case AR_DTYPE_FP16:
-      e = launch_norm_t<F16>(inputs, W, residual, gamma, eps, residual_out, norm_out, M, H, cfg,
-                             s);
+      e = arfh::launch_norm_f16(inputs, W, residual, gamma, eps, residual_out, norm_out, M, H,
+                                cfg, s);
       break;
     default:
-      e = launch_norm_t<Bf16>(inputs, W, residual, gamma, eps, residual_out, norm_out, M, H,
-                              cfg, s);
+      e = arfh::launch_norm_bf16(inputs, W, residual, gamma, eps, residual_out, norm_out, M, H,
+                                 cfg, s);
       break;
   }
   return e == hipSuccess ? AR_OK : AR_ERR_LAUNCH;
@@ -483,6 +376,172 @@ int run_gather(const void* const* slices, int W, int64_t M, int64_t H, int dtype
   return e == hipSuccess ? AR_OK : AR_ERR_LAUNCH;
 }
 
+// ---- Lamport-style exchange ----------------------------------------------------------------------
+
+constexpr uint32_t kDefaultSpinLimit = 1u << 16;
+// Rows the Lamport fused kernel takes: up to 1024 lanes x 2 vectors.
+constexpr int64_t kLamportMaxRowVecs = 2048;
+
+int check_lamport_shape(int pattern, int W, int64_t M, int64_t H, int dtype) {
+  int st = check_shape(AR_PATTERN_ALLREDUCE, W, M, H, dtype);
+  if (st != AR_OK) return st;
+  const int64_t vec = kVecBytes / elem_size(dtype);
+  if (H % vec != 0) return AR_ERR_UNSUPPORTED;
+  if (pattern == AR_PATTERN_AR_RESIDUAL_RMSNORM && H / vec > kLamportMaxRowVecs)
+    return AR_ERR_UNSUPPORTED;
+  return AR_OK;
+}
+
+int lamport_grid(int64_t items, int cu) {
+  return static_cast<int>(std::max<int64_t>(1, std::min(ceil_div(items, 256), int64_t(cu) * 16)));
+}
+
+int run_lamport_arm(void* rbuf, int W, int64_t M, int64_t H, int dtype, void* stream) {
+  int st = check_lamport_shape(AR_PATTERN_ALLREDUCE, W, M, H, dtype);
+  if (st != AR_OK) return st;
+  if (M == 0) return AR_OK;
+  if (!rbuf) return AR_ERR_INVALID_ARG;
+  if (!aligned16(rbuf)) return AR_ERR_MISALIGNED;
+  int cu = 0;
+  st = query_cu_count(&cu);
+  if (st != AR_OK) return st;
+  uint64_t* buf = static_cast<uint64_t*>(rbuf);
+  int64_t nwords = int64_t(W) * M * H * elem_size(dtype) / 8;
+  void* args[] = {&buf, &nwords};
+  const hipError_t e =
+      hipLaunchKernel(reinterpret_cast<const void*>(&arf::ar_lamport_arm_kernel<uint64_t>),
+                      dim3(lamport_grid(nwords, cu)), dim3(256), args, 0,
+                      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? AR_OK : AR_ERR_LAUNCH;
+}
+
+int run_lamport_push(const void* partial, int rank, void* rbuf, int W, int64_t M, int64_t H,
+                     int dtype, void* stream) {
+  int st = check_lamport_shape(AR_PATTERN_ALLREDUCE, W, M, H, dtype);
+  if (st != AR_OK) return st;
+  if (rank < 0 || rank >= W) return AR_ERR_INVALID_ARG;
+  if (M == 0) return AR_OK;
+  if (!partial || !rbuf) return AR_ERR_INVALID_ARG;
+  if (!aligned16(partial) || !aligned16(rbuf)) return AR_ERR_MISALIGNED;
+  const int64_t slot_bytes = M * H * elem_size(dtype);
+  if (overlap(range_of(partial, slot_bytes), range_of(rbuf, slot_bytes * W))) return AR_ERR_ALIAS;
+  int cu = 0;
+  st = query_cu_count(&cu);
+  if (st != AR_OK) return st;
+  void* slot = static_cast<char*>(rbuf) + rank * slot_bytes;
+  const int64_t nvec = slot_bytes / kVecBytes;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int grid = lamport_grid(nvec, cu);
+  hipError_t e;
+  switch (dtype) {
+    case AR_DTYPE_FP32: e = arfh::launch_lamport_push_f32(partial, slot, nvec, grid, s); break;
+    case AR_DTYPE_FP16: e = arfh::launch_lamport_push_f16(partial, slot, nvec, grid, s); break;
+    default: e = arfh::launch_lamport_push_bf16(partial, slot, nvec, grid, s); break;
+  }
+  return e == hipSuccess ? AR_OK : AR_ERR_LAUNCH;
+}
+
+// Pointer checks shared by the two Lamport consumers: nothing the kernel writes may overlap the
+// receive buffer or the status word except as allowed for the plain entry points.
+int check_lamport_buffers(void* rbuf, int W, int64_t M, int64_t H, int dtype, const int* status) {
+  if (!rbuf || !status) return AR_ERR_INVALID_ARG;
+  if (!aligned16(rbuf)) return AR_ERR_MISALIGNED;
+  if ((reinterpret_cast<uintptr_t>(status) & 3u) != 0) return AR_ERR_MISALIGNED;
+  const int64_t slot_bytes = M * H * elem_size(dtype);
+  if (overlap(range_of(status, 4), range_of(rbuf, slot_bytes * W))) return AR_ERR_ALIAS;
+  return AR_OK;
+}
+
+int run_lamport_sum(void* rbuf, int W, int64_t M, int64_t H, int dtype, void* out, int* status,
+                    uint32_t spin_limit, void* stream) {
+  int st = check_lamport_shape(AR_PATTERN_ALLREDUCE, W, M, H, dtype);
+  if (st != AR_OK) return st;
+  if (M == 0) return AR_OK;
+  if (!out) return AR_ERR_INVALID_ARG;
+  st = check_lamport_buffers(rbuf, W, M, H, dtype, status);
+  if (st != AR_OK) return st;
+  if (!aligned16(out)) return AR_ERR_MISALIGNED;
+  const int64_t bytes = M * H * elem_size(dtype);
+  const Range o = range_of(out, bytes);
+  if (overlap(o, range_of(rbuf, bytes * W)) || overlap(o, range_of(status, 4)))
+    return AR_ERR_ALIAS;
+  int cu = 0;
+  st = query_cu_count(&cu);
+  if (st != AR_OK) return st;
+  ar_launch_cfg_t cfg;
+  plan_sum(W, M * H, dtype, cu, &cfg);
+  cfg.vecs_per_thread = 1;  // the Lamport consumer is instantiated for one vector per thread
+  cfg.grid = cap_grid(ceil_div(M * H / (kVecBytes / elem_size(dtype)), cfg.threads_per_block));
+  cfg.nt_store = 1;
+  arf::LamportSource src{status, spin_limit ? spin_limit : kDefaultSpinLimit};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  switch (dtype) {
+    case AR_DTYPE_FP32: e = arfh::launch_lamport_sum_f32(rbuf, W, M, H, out, cfg, src, s); break;
+    case AR_DTYPE_FP16: e = arfh::launch_lamport_sum_f16(rbuf, W, M, H, out, cfg, src, s); break;
+    default: e = arfh::launch_lamport_sum_bf16(rbuf, W, M, H, out, cfg, src, s); break;
+  }
+  return e == hipSuccess ? AR_OK : AR_ERR_LAUNCH;
+}
+
+int run_lamport_norm(void* rbuf, int W, int64_t M, int64_t H, int dtype, const void* residual,
+                     const float* gamma, float eps, void* residual_out, void* norm_out,
+                     int* status, uint32_t spin_limit, void* stream) {
+  int st = check_lamport_shape(AR_PATTERN_AR_RESIDUAL_RMSNORM, W, M, H, dtype);
+  if (st != AR_OK) return st;
+  if (!std::isfinite(eps) || eps < 0.0f) return AR_ERR_INVALID_ARG;
+  if (M == 0) return AR_OK;
+  if (!residual || !gamma || !residual_out || !norm_out) return AR_ERR_INVALID_ARG;
+  st = check_lamport_buffers(rbuf, W, M, H, dtype, status);
+  if (st != AR_OK) return st;
+  if (!aligned16(residual) || !aligned16(gamma) || !aligned16(residual_out) ||
+      !aligned16(norm_out))
+    return AR_ERR_MISALIGNED;
+  const int64_t bytes = M * H * elem_size(dtype);
+  const Range rb = range_of(rbuf, bytes * W);
+  const Range ro = range_of(residual_out, bytes);
+  const Range no = range_of(norm_out, bytes);
+  const Range res = range_of(residual, bytes);
+  const Range g = range_of(gamma, H * int64_t(sizeof(float)));
+  const Range stw = range_of(status, 4);
+  if (overlap(ro, no) || overlap(ro, g) || overlap(no, g)) return AR_ERR_ALIAS;
+  if (overlap(ro, rb) || overlap(no, rb) || overlap(res, rb) || overlap(g, rb)) return AR_ERR_ALIAS;
+  if (overlap(ro, stw) || overlap(no, stw)) return AR_ERR_ALIAS;
+  if (bad_alias_with_input(ro, res) || bad_alias_with_input(no, res)) return AR_ERR_ALIAS;
+  int cu = 0;
+  st = query_cu_count(&cu);
+  if (st != AR_OK) return st;
+  ar_launch_cfg_t cfg;
+  plan_norm(W, M, H, dtype, cu, &cfg);
+  if (cfg.vecs_per_thread > 2) {  // the Lamport consumer is instantiated for 1 or 2 vectors
+    const int64_t V = H / (kVecBytes / elem_size(dtype));
+    cfg.vecs_per_thread = 2;
+    cfg.lanes_per_row = static_cast<int>(round_up(ceil_div(V, 2), 64));
+    cfg.threads_per_block = cfg.lanes_per_row;
+    cfg.rows_per_block = 1;
+    cfg.grid = cap_grid(M);
+  }
+  cfg.nt_store = 1;
+  arf::LamportSource src{status, spin_limit ? spin_limit : kDefaultSpinLimit};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  switch (dtype) {
+    case AR_DTYPE_FP32:
+      e = arfh::launch_lamport_norm_f32(rbuf, W, residual, gamma, eps, residual_out, norm_out, M,
+                                        H, cfg, src, s);
+      break;
+    case AR_DTYPE_FP16:
+      e = arfh::launch_lamport_norm_f16(rbuf, W, residual, gamma, eps, residual_out, norm_out, M,
+                                        H, cfg, src, s);
+      break;
+    default:
+      e = arfh::launch_lamport_norm_bf16(rbuf, W, residual, gamma, eps, residual_out, norm_out,
+                                         M, H, cfg, src, s);
+      break;
+  }
+  return e == hipSuccess ? AR_OK : AR_ERR_LAUNCH;
+}
+
 }  // namespace
 
 // ---- C ABI ----------------------------------------------------------------------------------------
@@ -548,6 +607,28 @@ int ar_row_partition(int W, int64_t M, int rank, int64_t* row_begin, int64_t* ro
 int ar_all_gather(const void* const* slices, int W, int64_t M, int64_t H, int dtype, void* out,
                   void* stream) {
   return run_gather(slices, W, M, H, dtype, out, stream);
+}
+
+int ar_lamport_arm(void* rbuf, int W, int64_t M, int64_t H, int dtype, void* stream) {
+  return run_lamport_arm(rbuf, W, M, H, dtype, stream);
+}
+
+int ar_lamport_push(const void* partial, int rank, void* rbuf, int W, int64_t M, int64_t H,
+                    int dtype, void* stream) {
+  return run_lamport_push(partial, rank, rbuf, W, M, H, dtype, stream);
+}
+
+int ar_lamport_sum(void* rbuf, int W, int64_t M, int64_t H, int dtype, void* out, int* status,
+                   uint32_t spin_limit, void* stream) {
+  return run_lamport_sum(rbuf, W, M, H, dtype, out, status, spin_limit, stream);
+}
+
+int ar_lamport_residual_rmsnorm(void* rbuf, int W, int64_t M, int64_t H, int dtype,
+                                const void* residual, const float* gamma, float eps,
+                                void* residual_out, void* norm_out, int* status,
+                                uint32_t spin_limit, void* stream) {
+  return run_lamport_norm(rbuf, W, M, H, dtype, residual, gamma, eps, residual_out, norm_out,
+                          status, spin_limit, stream);
 }
 
 const char* ar_status_string(int status) {

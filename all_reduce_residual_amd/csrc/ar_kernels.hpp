@@ -247,14 +247,31 @@ __device__ inline void rank_sum(const RankPtrs<W>& in, int64_t base, const uint3
   rank_sum_range<T, W, N, 0, kMaxLoads>(in, base, boff, acc);
 }
 
+// ---- input sources ------------------------------------------------------------------------------
+//
+// The kernels read the W partials through a source policy.  StreamSource reads ordinary device
+// buffers (the one-shot path).  LamportSource reads the slots of a receive buffer that producers
+// fill concurrently (see the Lamport section below).
+
+// `ok[k]` says whether vector slot k is a real one; slots that are not re-read a valid vector
+// (their offsets are clamped) and their result is discarded.
+struct StreamSource {
+  template <class T, int W, int N, int kMaxLoads = (N * T::kVec >= 32 ? 8 : 16)>
+  __device__ inline void sum(const RankPtrs<W>& in, int64_t base, const uint32_t (&boff)[N],
+                             const bool (&ok)[N], float (&acc)[N][T::kVec]) const {
+    (void)ok;
+    rank_sum<T, W, N, kMaxLoads>(in, base, boff, acc);
+  }
+};
+
 // ---- kAllReduce -----------------------------------------------------------------------------
 
 // out = RN_T(x_0 + ... + x_{W-1}) over n elements: nvec full 16-byte vectors, then a tail of
 // fewer than one vector handled element by element by block 0.  Blocks walk chunks of
 // blockDim.x * U vectors with a grid stride; lane t of a chunk owns vectors t + u * blockDim.x.
-template <class T, int W, int U, bool kNtStore>
+template <class T, int W, int U, bool kNtStore, class Src = StreamSource>
 __global__ __launch_bounds__(kMaxThreads) void ar_sum_kernel(RankPtrs<W> in, u32x4* out,
-                                                             int64_t nvec, int tail) {
+                                                             int64_t nvec, int tail, Src src) {
   constexpr int kVec = T::kVec;
   const int64_t chunk = static_cast<int64_t>(blockDim.x) * U;
   for (int64_t cbase = blockIdx.x * chunk; cbase < nvec; cbase += gridDim.x * chunk) {
@@ -262,25 +279,30 @@ __global__ __launch_bounds__(kMaxThreads) void ar_sum_kernel(RankPtrs<W> in, u32
     float acc[U][kVec];
     if (cbase + chunk <= nvec) {
       // Whole chunk in range (uniform branch): no predicate anywhere near the loads.
+      bool ok[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) boff[u] = (threadIdx.x + u * blockDim.x) * 16u;
-      rank_sum<T, W, U>(in, cbase, boff, acc);
+      for (int u = 0; u < U; ++u) {
+        boff[u] = (threadIdx.x + u * blockDim.x) * 16u;
+        ok[u] = true;
+      }
+      src.template sum<T, W, U>(in, cbase, boff, ok, acc);
 #pragma unroll
       for (int u = 0; u < U; ++u) store_vec<kNtStore>(at(out + cbase, boff[u]), T::narrow(acc[u]));
     } else {
       // Last, partial chunk: slots past the end re-read the last vector (a clamp, not a
       // branch, so the loads stay unconditional) and are not stored.
       const uint32_t last = static_cast<uint32_t>(nvec - cbase - 1);
+      bool ok[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const uint32_t i = threadIdx.x + u * blockDim.x;
         boff[u] = (i < last ? i : last) * 16u;
+        ok[u] = i <= last;
       }
-      rank_sum<T, W, U>(in, cbase, boff, acc);
+      src.template sum<T, W, U>(in, cbase, boff, ok, acc);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        if (threadIdx.x + u * blockDim.x <= last)
-          store_vec<kNtStore>(at(out + cbase, boff[u]), T::narrow(acc[u]));
+        if (ok[u]) store_vec<kNtStore>(at(out + cbase, boff[u]), T::narrow(acc[u]));
       }
     }
   }
@@ -320,10 +342,10 @@ __device__ inline void load_gamma(const f32x4* gamma, uint32_t vec, float (&g)[k
 // One row = V vectors of 16 bytes.  Thread t of a block serves row slot t / L (R slots per
 // block) and, within the row, vectors lane + k * L for k < VPT.  L * VPT >= V.  Blocks walk
 // groups of R rows with a grid stride.
-template <class T, int W, int VPT, bool kNtStore>
+template <class T, int W, int VPT, bool kNtStore, class Src = StreamSource>
 __global__ __launch_bounds__(kMaxThreads) void ar_norm_kernel(
     RankPtrs<W> in, const u32x4* residual, const f32x4* gamma, u32x4* residual_out,
-    u32x4* norm_out, int64_t M, int V, int L, int R, float eps, float count_h) {
+    u32x4* norm_out, int64_t M, int V, int L, int R, float eps, float count_h, Src src) {
   constexpr int kVec = T::kVec;
   __shared__ float red[2][kMaxWavesPerBlock];
 
@@ -366,12 +388,16 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_kernel(
     uint32_t boff[VPT];
     group_offsets(grp, boff);
 
+    bool ok[VPT];
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) ok[k] = row_ok && col_ok[k];
+
     // Sum of the W partials and the residual, binary32 in rank order, rounded once to T.
     u32x4 rounded[VPT];
     if constexpr (VPT <= 2) {
       // All vectors' chains together: the most independent loads per batch.
       float acc[VPT][kVec];
-      rank_sum<T, W, VPT>(in, base, boff, acc);
+      src.template sum<T, W, VPT>(in, base, boff, ok, acc);
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {
         accumulate<T>(acc[k], load_stream(at(residual + base, boff[k])));
@@ -382,8 +408,9 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_kernel(
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {
         const uint32_t boff_k[1] = {boff[k]};
+        const bool ok_k[1] = {ok[k]};
         float acc[1][kVec];
-        rank_sum<T, W, 1, 8>(in, base, boff_k, acc);
+        src.template sum<T, W, 1, 8>(in, base, boff_k, ok_k, acc);
         accumulate<T>(acc[0], load_stream(at(residual + base, boff[k])));
         rounded[k] = T::narrow(acc[0]);
         batch_fence(acc);
@@ -392,7 +419,7 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_kernel(
     float ss = 0.0f;
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
-      if (row_ok && col_ok[k]) {
+      if (ok[k]) {
         store_vec<kNtStore>(at(residual_out + base, boff[k]), rounded[k]);
         float v[kVec];
         T::widen(rounded[k], v);
@@ -417,7 +444,7 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_kernel(
 
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
-      if (row_ok && col_ok[k]) {
+      if (ok[k]) {
         float v[kVec];
         T::widen(rounded[k], v);
         float g[kVec];
@@ -438,6 +465,158 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_kernel(
       }
     }
   }
+}
+
+// ---- Lamport-style one-shot exchange (receive side) ---------------------------------------------
+//
+// The one-shot exchange of the MNNVL all-reduce (flashinfer pull request "Optimizations for
+// TRTLLM MNNVL Allreduce", Description and Summary: Lamport polling with vectorized loads, flags
+// kept in the data) needs no separate flag: a receive buffer holds one slot per rank, every
+// element of an empty slot holds a sentinel bit pattern (all ones: a NaN in every element type),
+// and a producer's data can never equal it because the producer replaces an all-ones element by
+// the same value with its lowest bit cleared (still a NaN).  The consumer polls each element until
+// it is not the sentinel, reduces, and writes the sentinel back so the slot is empty for the next
+// round.  Words are moved with 64-bit relaxed atomics at agent scope, so a producer kernel and a
+// consumer kernel running at the same time on different XCDs see each other's words.  Every wait
+// is bounded: after `spin_limit` polls of one word the consumer gives up, sets bit 0 of `*status`
+// and continues with what it read (the affected outputs are then meaningless; the caller checks
+// the status).
+
+template <class T>
+struct LaneMask;
+template <>
+struct LaneMask<Bf16> {
+  static constexpr uint64_t kLow = 0x0001000100010001ull, kHigh = 0x8000800080008000ull;
+};
+template <>
+struct LaneMask<F16> : LaneMask<Bf16> {};
+template <>
+struct LaneMask<F32> {
+  static constexpr uint64_t kLow = 0x0000000100000001ull, kHigh = 0x8000000080000000ull;
+};
+
+// Per element lane of w: the lane's high bit set iff the element is the all-ones sentinel
+// (classic "lane is zero" test applied to ~w).
+template <class T>
+__device__ inline uint64_t sentinel_lanes(uint64_t w) {
+  const uint64_t x = ~w;
+  return (x - LaneMask<T>::kLow) & ~x & LaneMask<T>::kHigh;
+}
+
+template <class T>
+__device__ inline uint64_t canonicalize(uint64_t w) {
+  // An all-ones element becomes all ones with the lowest bit cleared.
+  const uint64_t high = sentinel_lanes<T>(w);
+  const int shift = (LaneMask<T>::kHigh == 0x8000800080008000ull) ? 15 : 31;
+  return w & ~(high >> shift);
+}
+
+__device__ inline uint64_t load_agent(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void store_agent(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+struct LamportSource {
+  int* status;          // bit 0 set on a poll timeout
+  uint32_t spin_limit;  // polls per word before giving up
+
+  // Polls *p until no element of w is empty.  After its first timeout a thread stops waiting
+  // (`gave_up`), so a missing producer costs each thread at most one spin limit.
+  template <class T>
+  __device__ inline uint64_t wait_word(const uint64_t* p, uint64_t w, bool& gave_up) const {
+    uint32_t n = 0;
+    while (!gave_up && sentinel_lanes<T>(w) != 0) {
+      if (n++ >= spin_limit) {
+        __hip_atomic_fetch_or(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        gave_up = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+      w = load_agent(p);
+    }
+    return w;
+  }
+
+  // acc[k] = -0 + slot_0[k] + ... + slot_{W-1}[k], each 16-byte vector read as two words: all
+  // words of a batch are loaded first, then only words still empty are polled again, then the
+  // batch is accumulated in rank order and its words are re-armed with the sentinel.
+  // Slots that are not real (ok[k] false) neither read nor re-arm anything: their clamped
+  // offset points at another lane's vector, which they must not empty.
+  template <class T, int W, int N, int kMaxLoads = (N * T::kVec >= 32 ? 8 : 16)>
+  __device__ inline void sum(const RankPtrs<W>& in, int64_t base, const uint32_t (&boff)[N],
+                             const bool (&ok)[N], float (&acc)[N][T::kVec]) const {
+    // Polled words stay live until accumulated: half the stream source's batch.
+    constexpr int kBatch = rank_batch<W, N, (kMaxLoads / 2 > 0 ? kMaxLoads / 2 : 1)>();
+    bool gave_up = false;
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+#pragma unroll
+      for (int e = 0; e < T::kVec; ++e) acc[k][e] = -0.0f;
+    }
+#pragma unroll
+    for (int r0 = 0; r0 < W; r0 += kBatch) {
+      uint64_t w[kBatch][N][2];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        if (r0 + j >= W) break;
+#pragma unroll
+        for (int k = 0; k < N; ++k) {
+          const uint64_t* p = reinterpret_cast<const uint64_t*>(at(in.p[r0 + j] + base, boff[k]));
+          w[j][k][0] = ok[k] ? load_agent(p) : 0;
+          w[j][k][1] = ok[k] ? load_agent(p + 1) : 0;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        if (r0 + j >= W) break;
+#pragma unroll
+        for (int k = 0; k < N; ++k) {
+          const uint64_t* p = reinterpret_cast<const uint64_t*>(at(in.p[r0 + j] + base, boff[k]));
+          w[j][k][0] = wait_word<T>(p, w[j][k][0], gave_up);
+          w[j][k][1] = wait_word<T>(p + 1, w[j][k][1], gave_up);
+          u32x4 v;
+          v.x = static_cast<uint32_t>(w[j][k][0]);
+          v.y = static_cast<uint32_t>(w[j][k][0] >> 32);
+          v.z = static_cast<uint32_t>(w[j][k][1]);
+          v.w = static_cast<uint32_t>(w[j][k][1] >> 32);
+          float x[T::kVec];
+          T::widen(v, x);
+#pragma unroll
+          for (int e = 0; e < T::kVec; ++e) acc[k][e] = acc[k][e] + x[e];
+          if (ok[k]) {
+            uint64_t* q = const_cast<uint64_t*>(p);
+            store_agent(q, ~0ull);
+            store_agent(q + 1, ~0ull);
+          }
+        }
+      }
+      if (r0 + kBatch < W) batch_fence(acc);
+    }
+  }
+};
+
+// Producer: slot[i] = canonicalize(src[i]) for nvec 16-byte vectors, as 64-bit agent-scope words.
+template <class T>
+__global__ __launch_bounds__(kMaxThreads) void ar_lamport_push_kernel(const u32x4* src,
+                                                                      u32x4* slot, int64_t nvec) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < nvec;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const u32x4 v = load_stream(src + i);
+    uint64_t* q = reinterpret_cast<uint64_t*>(slot + i);
+    store_agent(q, canonicalize<T>(v.x | (static_cast<uint64_t>(v.y) << 32)));
+    store_agent(q + 1, canonicalize<T>(v.z | (static_cast<uint64_t>(v.w) << 32)));
+  }
+}
+
+// Arms (empties) nwords 64-bit words of a receive buffer.  (A template so that the header
+// defines no kernel by itself: it is instantiated in one translation unit only.)
+template <class Word>
+__global__ __launch_bounds__(kMaxThreads) void ar_lamport_arm_kernel(Word* buf, int64_t nwords) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < nwords;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    store_agent(buf + i, ~0ull);
 }
 
 // ---- all-gather share (two-shot) ----------------------------------------------------------------

@@ -1,0 +1,37 @@
+// inst_bf16.hip -- kernel instantiations and launchers for one element type (Bf16).
+#include "ar_dispatch.hpp"
+
+namespace arfh {
+
+hipError_t launch_sum_bf16(const void* const* inputs, int W, void* out, int64_t nvec, int tail,
+                          const ar_launch_cfg_t& c, hipStream_t s) {
+  return launch_sum_t<Bf16>(inputs, W, out, nvec, tail, c, s);
+}
+
+hipError_t launch_norm_bf16(const void* const* inputs, int W, const void* residual,
+                           const float* gamma, float eps, void* residual_out, void* norm_out,
+                           int64_t M, int64_t H, const ar_launch_cfg_t& c, hipStream_t s) {
+  return launch_norm_t<Bf16>(inputs, W, residual, gamma, eps, residual_out, norm_out, M, H, c,
+                              s);
+}
+
+hipError_t launch_lamport_sum_bf16(void* rbuf, int W, int64_t M, int64_t H, void* out,
+                                  const ar_launch_cfg_t& c, arf::LamportSource src,
+                                  hipStream_t s) {
+  return launch_lamport_sum_t<Bf16>(rbuf, W, M, H, out, c, src, s);
+}
+
+hipError_t launch_lamport_norm_bf16(void* rbuf, int W, const void* residual, const float* gamma,
+                                   float eps, void* residual_out, void* norm_out, int64_t M,
+                                   int64_t H, const ar_launch_cfg_t& c, arf::LamportSource src,
+                                   hipStream_t s) {
+  return launch_lamport_norm_t<Bf16>(rbuf, W, residual, gamma, eps, residual_out, norm_out, M,
+                                      H, c, src, s);
+}
+
+hipError_t launch_lamport_push_bf16(const void* partial, void* slot, int64_t nvec, int grid,
+                                   hipStream_t s) {
+  return launch_lamport_push_t<Bf16>(partial, slot, nvec, grid, s);
+}
+
+}  // namespace arfh

@@ -175,6 +175,42 @@ int ar_row_partition(int W, int64_t M, int rank, int64_t* row_begin, int64_t* ro
 int ar_all_gather(const void* const* slices, int W, int64_t M, int64_t H, int dtype, void* out,
                   void* stream);
 
+/* ---- Lamport-style one-shot exchange ------------------------------------------------------------
+ *
+ * The one-shot exchange of the MNNVL all-reduce (flashinfer pull request "Optimizations for
+ * TRTLLM MNNVL Allreduce", Description and Summary: Lamport polling with vectorized loads,
+ * buffer state kept in the data) carries no separate flag: a receive buffer `rbuf` holds W slots
+ * of [M, H] elements of type `dtype` (slot r at byte offset r * M * H * sizeof(T)); an empty
+ * element holds the all-ones bit pattern (a NaN in every type).  Producers write their partial
+ * into their slot; consumers poll each element until it is not all ones, reduce exactly as
+ * ar_sum / ar_residual_rmsnorm, and write all ones back, leaving the buffer empty for the next
+ * round.  A partial element that is itself all ones is delivered with its lowest bit cleared (a
+ * NaN either way).  Producers and the consumer may run concurrently (on other streams, or, with
+ * peer-mapped memory, other GPUs): words move as 64-bit relaxed atomics at agent scope.
+ * Every wait is bounded: after `spin_limit` polls of one 8-byte word (0 = 65536) the consumer
+ * gives up on it, sets bit 0 of *status (a device int the caller clears) and carries on; the
+ * outputs are then meaningless and the buffer is not left empty.  H must be a multiple of
+ * 16 / sizeof(T); the fused consumer takes rows of at most 2048 16-byte vectors. */
+
+/* Empties all W slots (every element all ones).  Call once before the first round. */
+int ar_lamport_arm(void* rbuf, int W, int64_t M, int64_t H, int dtype, void* stream);
+
+/* Producer of rank `rank`: copies `partial` ([M, H], must not overlap rbuf) into slot `rank`. */
+int ar_lamport_push(const void* partial, int rank, void* rbuf, int W, int64_t M, int64_t H,
+                    int dtype, void* stream);
+
+/* Consumer, kAllReduce: out = sum of the W slots (as ar_sum); re-empties the slots.
+ * out must not overlap rbuf or *status. */
+int ar_lamport_sum(void* rbuf, int W, int64_t M, int64_t H, int dtype, void* out, int* status,
+                   uint32_t spin_limit, void* stream);
+
+/* Consumer, kARResidualRMSNorm (as ar_residual_rmsnorm); re-empties the slots.  residual,
+ * gamma and both outputs must not overlap rbuf; outputs must not overlap *status. */
+int ar_lamport_residual_rmsnorm(void* rbuf, int W, int64_t M, int64_t H, int dtype,
+                                const void* residual, const float* gamma, float eps,
+                                void* residual_out, void* norm_out, int* status,
+                                uint32_t spin_limit, void* stream);
+
 /* Static, human-readable name of a status code ("unknown status" for anything else). */
 const char* ar_status_string(int status);
 

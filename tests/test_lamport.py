@@ -1,0 +1,48 @@
+"""Lamport-style exchange, host side: argument validation of the producer and the consumers.
+Every call here is invalid and must be rejected before any device access (the pointers are
+fake and never dereferenced)."""
+import ctypes
+
+import all_reduce_residual_amd as ar
+
+BF16 = ar.DTYPE_BF16
+
+
+def test_lamport_validation():
+    L = ar.lib()
+    rbuf, part, out, status = 0x1000000, 0x4000000, 0x5000000, 0x6000000
+    res, gam, ro, no = 0x7000000, 0x8000000, 0x9000000, 0xA000000
+    W, M, H = 4, 8, 256               # slot = 4096 bytes, rbuf = 16 KiB
+    # Producer.
+    assert L.ar_lamport_push(part, 4, rbuf, W, M, H, BF16, None) == ar.AR_ERR_INVALID_ARG
+    assert L.ar_lamport_push(part, -1, rbuf, W, M, H, BF16, None) == ar.AR_ERR_INVALID_ARG
+    assert L.ar_lamport_push(part, 0, rbuf, 12, M, H, BF16, None) == ar.AR_ERR_UNSUPPORTED
+    assert L.ar_lamport_push(part, 0, rbuf, W, M, 260, BF16, None) == ar.AR_ERR_UNSUPPORTED
+    assert L.ar_lamport_push(rbuf + 4096, 0, rbuf, W, M, H, BF16, None) == ar.AR_ERR_ALIAS
+    assert L.ar_lamport_push(part + 2, 0, rbuf, W, M, H, BF16, None) == ar.AR_ERR_MISALIGNED
+    assert L.ar_lamport_push(None, 0, rbuf, W, M, H, BF16, None) == ar.AR_ERR_INVALID_ARG
+    # Sum consumer.
+    assert L.ar_lamport_sum(rbuf, W, M, H, BF16, out, None, 0, None) == ar.AR_ERR_INVALID_ARG
+    assert L.ar_lamport_sum(rbuf, W, M, H, BF16, out, status + 2, 0, None) == ar.AR_ERR_MISALIGNED
+    assert L.ar_lamport_sum(rbuf, W, M, H, BF16, rbuf + 8192, status, 0, None) == ar.AR_ERR_ALIAS
+    assert L.ar_lamport_sum(rbuf, W, M, H, BF16, out, rbuf + 64, 0, None) == ar.AR_ERR_ALIAS
+    assert L.ar_lamport_sum(rbuf, W, M, H, BF16, out, out + 64, 0, None) == ar.AR_ERR_ALIAS
+    assert L.ar_lamport_sum(rbuf + 8, W, M, H, BF16, out, status, 0, None) == ar.AR_ERR_MISALIGNED
+    assert L.ar_lamport_sum(rbuf, 3, M, H, BF16, out, status, 0, None) == ar.AR_ERR_UNSUPPORTED
+    # Fused consumer.
+    args = (rbuf, W, M, H, BF16)
+    assert L.ar_lamport_residual_rmsnorm(*args, res, gam, -1.0, ro, no, status, 0, None) == \
+        ar.AR_ERR_INVALID_ARG
+    assert L.ar_lamport_residual_rmsnorm(*args, rbuf + 4096, gam, 1e-6, ro, no, status, 0,
+                                         None) == ar.AR_ERR_ALIAS
+    assert L.ar_lamport_residual_rmsnorm(*args, res, gam, 1e-6, ro, ro, status, 0, None) == \
+        ar.AR_ERR_ALIAS
+    assert L.ar_lamport_residual_rmsnorm(*args, res, gam, 1e-6, ro, no, ro + 16, 0, None) == \
+        ar.AR_ERR_ALIAS
+    assert L.ar_lamport_residual_rmsnorm(rbuf, W, M, 32768, BF16, res, gam, 1e-6, ro, no,
+                                         status, 0, None) == ar.AR_ERR_UNSUPPORTED
+    assert L.ar_lamport_residual_rmsnorm(*args, None, gam, 1e-6, ro, no, status, 0, None) == \
+        ar.AR_ERR_INVALID_ARG
+    # Zero rows: nothing to do.
+    assert L.ar_lamport_sum(None, W, 0, H, BF16, None, None, 0, None) == ar.AR_OK
+    assert L.ar_lamport_arm(None, W, 0, H, BF16, None) == ar.AR_OK
