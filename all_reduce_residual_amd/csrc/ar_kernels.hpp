@@ -218,6 +218,38 @@ template <class T, int W, int N, int R0 = 0, int kMaxLoads = (N * T::kVec >= 32 
 __device__ inline void rank_sum_range(const RankPtrs<W>& in, int64_t base,
                                       const uint32_t (&boff)[N], float (&acc)[N][T::kVec]) {
   constexpr int kBatch = rank_batch<W - R0 < 1 ? 1 : W - R0, N, kMaxLoads>();
+  if constexpr (W > 32 && R0 == 0 && 16 % kBatch == 0) {
+    // More rank pointers than scalar registers (2 per pointer): left to itself the compiler
+    // spills them to VGPR lanes and, reloading them one at a time, issues one load per DRAM
+    // round trip.  Instead walk groups of 16 ranks in a loop that is not unrolled, so each
+    // group's pointers are read from the kernel arguments when the group is reached, and stage
+    // every batch in registers (all loads first, then the adds in rank order).
+#pragma unroll 1
+    for (int g = 0; g < W; g += 16) {
+#pragma unroll
+      for (int r0 = 0; r0 < 16; r0 += kBatch) {
+        u32x4 raw[kBatch][N];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const u32x4* src = in.p[g + r0 + j] + base;
+#pragma unroll
+          for (int k = 0; k < N; ++k) raw[j][k] = load_stream(at(src, boff[k]));
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+#pragma unroll
+          for (int k = 0; k < N; ++k) {
+            float x[T::kVec];
+            T::widen(raw[j][k], x);
+#pragma unroll
+            for (int e = 0; e < T::kVec; ++e) acc[k][e] = acc[k][e] + x[e];
+          }
+        }
+        batch_fence(acc);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int r0 = R0; r0 < W; r0 += kBatch) {
 #pragma unroll
