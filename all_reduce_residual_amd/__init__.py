@@ -43,6 +43,17 @@ class ArError(RuntimeError):
         super().__init__("%s: %s (status %d)" % (where, status_string(status), status))
 
 
+ROUTE_ONE_SHOT, ROUTE_TWO_SHOT, ROUTE_FALLBACK = 0, 1, 2
+
+
+class Policy(ctypes.Structure):
+    _fields_ = [("min_tokens", ctypes.c_int64), ("two_shot_min_bytes", ctypes.c_int64),
+                ("max_payload_bytes", ctypes.c_int64)]
+
+    def as_dict(self) -> Dict[str, int]:
+        return {name: int(getattr(self, name)) for name, _ in self._fields_}
+
+
 class LaunchConfig(ctypes.Structure):
     _fields_ = [("threads_per_block", ctypes.c_int32), ("vecs_per_thread", ctypes.c_int32),
                 ("lanes_per_row", ctypes.c_int32), ("rows_per_block", ctypes.c_int32),
@@ -82,6 +93,9 @@ def lib():
             "ar_lamport_sum": [vp, i32, i64, i64, i32, vp, vp, ctypes.c_uint32, vp],
             "ar_lamport_residual_rmsnorm": [vp, i32, i64, i64, i32, vp, vp, f32, vp, vp, vp,
                                             ctypes.c_uint32, vp],
+            "ar_policy_default": [i32, ctypes.POINTER(Policy)],
+            "ar_route": [i32, i32, i64, i64, i32, ctypes.POINTER(Policy),
+                         ctypes.POINTER(ctypes.c_int)],
             "ar_row_partition": [i32, i64, i32, ctypes.POINTER(ctypes.c_int64),
                                  ctypes.POINTER(ctypes.c_int64)],
             "ar_all_gather": [vp, i32, i64, i64, i32, vp, vp],
@@ -265,6 +279,21 @@ def ar_lamport_residual_rmsnorm(rbuf, residual, gamma, eps: float, residual_out,
         residual_out.data_ptr(), norm_out.data_ptr(), status.data_ptr(), spin_limit,
         _stream_handle(stream, rbuf.device))
     _check(st, "ar_lamport_residual_rmsnorm")
+
+
+def ar_policy_default(W: int) -> Dict[str, int]:
+    p = Policy()
+    _check(lib().ar_policy_default(W, ctypes.byref(p)), "ar_policy_default")
+    return p.as_dict()
+
+
+def ar_route(pattern: int, W: int, M: int, H: int, dtype: int,
+             policy: Optional[Dict[str, int]] = None) -> int:
+    """ROUTE_ONE_SHOT, ROUTE_TWO_SHOT or ROUTE_FALLBACK for this call (default policy if None)."""
+    p = Policy(**(policy if policy is not None else ar_policy_default(W if W >= 1 else 1)))
+    r = ctypes.c_int(-1)
+    _check(lib().ar_route(pattern, W, M, H, dtype, ctypes.byref(p), ctypes.byref(r)), "ar_route")
+    return int(r.value)
 
 
 def ar_supports(pattern: int, W: int, M: int, H: int, dtype: int) -> int:

@@ -631,6 +631,43 @@ int ar_lamport_residual_rmsnorm(void* rbuf, int W, int64_t M, int64_t H, int dty
                           status, spin_limit, stream);
 }
 
+int ar_policy_default(int W, ar_policy_t* policy) {
+  if (!policy || W < 1) return AR_ERR_INVALID_ARG;
+  // Two-shot beats one-shot once S (1 - 2/W) / link_bw > t_exchange (see the header).
+  constexpr double kLinkBytesPerSec = 153e9;
+  constexpr double kExchangeSec = 5e-6;
+  policy->min_tokens = 32;
+  policy->two_shot_min_bytes =
+      W <= 2 ? INT64_MAX
+             : static_cast<int64_t>(kExchangeSec * kLinkBytesPerSec / (1.0 - 2.0 / W));
+  policy->max_payload_bytes = 0;
+  return AR_OK;
+}
+
+int ar_route(int pattern, int W, int64_t M, int64_t H, int dtype, const ar_policy_t* policy,
+             int* route) {
+  if (!policy || !route) return AR_ERR_INVALID_ARG;
+  if (pattern != AR_PATTERN_ALLREDUCE && pattern != AR_PATTERN_AR_RESIDUAL_RMSNORM)
+    return AR_ERR_INVALID_ARG;
+  if (policy->min_tokens < 0 || policy->two_shot_min_bytes < 0 || policy->max_payload_bytes < 0)
+    return AR_ERR_INVALID_ARG;
+  if (check_shape(pattern, W, M, H, dtype) != AR_OK) {
+    *route = AR_ROUTE_FALLBACK;
+    return AR_OK;
+  }
+  const int64_t payload = M * H * elem_size(dtype);
+  if (policy->max_payload_bytes > 0 && payload > policy->max_payload_bytes) {
+    *route = AR_ROUTE_FALLBACK;
+  } else if (M < policy->min_tokens || payload < policy->two_shot_min_bytes) {
+    *route = AR_ROUTE_ONE_SHOT;
+  } else {
+    // Two-shot needs whole vectors per row for the gather; otherwise stay on one-shot.
+    const bool gatherable = H % (kVecBytes / elem_size(dtype)) == 0;
+    *route = gatherable ? AR_ROUTE_TWO_SHOT : AR_ROUTE_ONE_SHOT;
+  }
+  return AR_OK;
+}
+
 const char* ar_status_string(int status) {
   switch (status) {
     case AR_OK: return "ok";

@@ -211,6 +211,43 @@ int ar_lamport_residual_rmsnorm(void* rbuf, int W, int64_t M, int64_t H, int dty
                                 void* residual_out, void* norm_out, int* status,
                                 uint32_t spin_limit, void* stream);
 
+/* ---- routing policy ------------------------------------------------------------------------------
+ *
+ * The policy layer that picks a path per call, after the pages: the tokenspeed pull request
+ * (Body, Routing) splits by token count (32 by default: decode sizes stay on the latency path)
+ * and treats an unsupported shape as a reason to take the other path; the vLLM pull request
+ * (Scope, Performance) keys strict per-rank payload cutoffs by topology and sends world size 12
+ * to the fallback.  ar_route is pure host arithmetic. */
+typedef enum {
+  AR_ROUTE_ONE_SHOT = 0,  /* ar_sum / ar_residual_rmsnorm over all W peers' buffers */
+  AR_ROUTE_TWO_SHOT = 1,  /* reduce-scatter share on the rank's rows, then ar_all_gather */
+  AR_ROUTE_FALLBACK = 2   /* not this library: the caller's collective (e.g. RCCL) */
+} ar_route_t;
+
+typedef struct {
+  int64_t min_tokens;          /* M below this always takes one-shot (latency-bound sizes) */
+  int64_t two_shot_min_bytes;  /* from this per-rank payload (M * H * sizeof(T)) on, and with
+                                  M >= min_tokens, two-shot */
+  int64_t max_payload_bytes;   /* per-rank payload above this goes to the fallback (the
+                                  workspace capacity); 0 = no limit */
+} ar_policy_t;
+
+/* Default policy for W ranks of one MI355X node (all-to-all xGMI: one ~153 GB/s link per peer
+ * pair).  min_tokens = 32 (the tokenspeed default).  two_shot_min_bytes comes from a link model:
+ * one-shot moves the whole payload S over each peer link, two-shot 2 S / W but pays a second
+ * exchange (~5 us); two-shot wins once S (1 - 2 / W) / 153 GB/s exceeds 5 us, i.e. from
+ * 5 us * 153 GB/s / (1 - 2 / W) (W = 8: 1.02 MB); for W <= 2 two-shot never wins (INT64_MAX).
+ * max_payload_bytes = 0: the library needs no workspace.  A model, not a measurement: the
+ * crossover needs two GPUs to measure. */
+int ar_policy_default(int W, ar_policy_t* policy);
+
+/* Route for one call: AR_ROUTE_FALLBACK if ar_supports rejects the shape (e.g. W = 12) or the
+ * payload exceeds max_payload_bytes; otherwise AR_ROUTE_ONE_SHOT below min_tokens or below
+ * two_shot_min_bytes, else AR_ROUTE_TWO_SHOT.  Returns AR_OK and sets *route, or
+ * AR_ERR_INVALID_ARG for a null pointer, a negative threshold or a bad pattern. */
+int ar_route(int pattern, int W, int64_t M, int64_t H, int dtype, const ar_policy_t* policy,
+             int* route);
+
 /* Static, human-readable name of a status code ("unknown status" for anything else). */
 const char* ar_status_string(int status);
 

@@ -25,7 +25,8 @@ def test_exports_every_declared_function(L):
                           "ar_sum_with_config", "ar_residual_rmsnorm_with_config",
                           "ar_status_string", "ar_device_cu_count", "ar_row_partition",
                           "ar_all_gather", "ar_lamport_arm", "ar_lamport_push",
-                          "ar_lamport_sum", "ar_lamport_residual_rmsnorm"}
+                          "ar_lamport_sum", "ar_lamport_residual_rmsnorm",
+                          "ar_policy_default", "ar_route"}
     for n in names:
         assert hasattr(L, n), n
 

@@ -1,0 +1,74 @@
+"""Routing policy (host only): the pages' decision rules as the library implements them.
+
+* unsupported world sizes (12, 3, ...) and unsupported shapes go to the caller's fallback;
+* below the token threshold (32 by default) every call stays one-shot;
+* from the two-shot payload threshold on, two-shot; a per-rank payload cutoff sends larger
+  calls to the fallback;
+* the decision is monotone in M for a fixed policy (one-shot, then two-shot, then fallback).
+"""
+import pytest
+
+import all_reduce_residual_amd as ar
+
+ONE, TWO, FB = ar.ROUTE_ONE_SHOT, ar.ROUTE_TWO_SHOT, ar.ROUTE_FALLBACK
+RMS, SUM, BF16 = ar.PATTERN_AR_RESIDUAL_RMSNORM, ar.PATTERN_ALLREDUCE, ar.DTYPE_BF16
+
+
+def test_default_policy_values():
+    p8 = ar.ar_policy_default(8)
+    assert p8["min_tokens"] == 32 and p8["max_payload_bytes"] == 0
+    # 5 us * 153 GB/s / (1 - 2/8) = 1.02 MB
+    assert abs(p8["two_shot_min_bytes"] - 1_020_000) <= 1
+    assert ar.ar_policy_default(2)["two_shot_min_bytes"] == 2 ** 63 - 1
+    # Larger worlds cross over earlier.
+    t = [ar.ar_policy_default(w)["two_shot_min_bytes"] for w in (4, 8, 16, 64)]
+    assert t == sorted(t, reverse=True)
+
+
+def test_world_size_twelve_falls_back():
+    for pat in (SUM, RMS):
+        assert ar.ar_route(pat, 12, 256, 7168, BF16) == FB
+        assert ar.ar_route(pat, 3, 256, 7168, BF16) == FB
+        assert ar.ar_route(pat, 8, 256, 7168, BF16) != FB
+
+
+def test_unsupported_shape_falls_back():
+    assert ar.ar_route(RMS, 8, 64, 7170, BF16) == FB       # norm rows need whole vectors
+    assert ar.ar_route(SUM, 8, 64, 7170, BF16) == ONE      # the sum takes any H
+
+
+def test_token_threshold_and_payload():
+    # Decode sizes: one-shot regardless of bytes.
+    for M in (1, 8, 31):
+        assert ar.ar_route(RMS, 8, M, 65536, BF16) == ONE
+    # M >= 32 with a large payload: two-shot.
+    assert ar.ar_route(RMS, 8, 2048, 7168, BF16) == TWO
+    # M >= 32 but a small payload (32 x 256 x 2 = 16 KiB): one-shot.
+    assert ar.ar_route(RMS, 8, 32, 256, BF16) == ONE
+    # W = 2 never takes two-shot by default.
+    assert ar.ar_route(RMS, 2, 4096, 8192, BF16) == ONE
+
+
+def test_payload_cutoff_sends_to_fallback():
+    pol = dict(min_tokens=32, two_shot_min_bytes=1 << 20, max_payload_bytes=80 << 20)
+    assert ar.ar_route(SUM, 4, 5120, 8192, BF16, pol) == TWO      # 80 MiB: at the cutoff
+    assert ar.ar_route(SUM, 4, 5121, 8192, BF16, pol) == FB       # one row more: above it
+
+
+def test_monotone_in_tokens():
+    pol = dict(min_tokens=32, two_shot_min_bytes=1 << 20, max_payload_bytes=64 << 20)
+    order = {ONE: 0, TWO: 1, FB: 2}
+    for W in ar.SUPPORTED_W:
+        prev = 0
+        for M in range(0, 6000, 37):
+            r = order[ar.ar_route(RMS, W, M, 7168, BF16, pol)]
+            assert r >= prev
+            prev = r
+
+
+def test_route_rejects_bad_arguments():
+    with pytest.raises(ar.ArError):
+        ar.ar_route(7, 8, 32, 256, BF16)
+    with pytest.raises(ar.ArError):
+        ar.ar_route(RMS, 8, 32, 256, BF16, dict(min_tokens=-1, two_shot_min_bytes=0,
+                                                max_payload_bytes=0))
