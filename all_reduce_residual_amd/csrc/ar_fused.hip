@@ -48,8 +48,8 @@ int check_shape(int pattern, int W, int64_t M, int64_t H, int dtype) {
   if (W < 1 || M < 0 || H < 1 || !valid_dtype(dtype)) return AR_ERR_INVALID_ARG;
   if (W > AR_MAX_W || !is_pow2(W)) return AR_ERR_UNSUPPORTED;
   const int64_t es = elem_size(dtype);
-  // Keep every byte offset far from int64 overflow.
-  if (M > 0 && H > (int64_t(1) << 60) / (M * es)) return AR_ERR_UNSUPPORTED;
+  // Keep every byte offset far from int64 overflow (M * H * es <= 2^60, computed by division).
+  if (M > 0 && H > ((int64_t(1) << 60) / es) / M) return AR_ERR_UNSUPPORTED;
   if (pattern == AR_PATTERN_AR_RESIDUAL_RMSNORM) {
     const int64_t vec = kVecBytes / es;
     if (H % vec != 0) return AR_ERR_UNSUPPORTED;
@@ -385,6 +385,9 @@ constexpr int64_t kLamportMaxRowVecs = 2048;
 int check_lamport_shape(int pattern, int W, int64_t M, int64_t H, int dtype) {
   int st = check_shape(AR_PATTERN_ALLREDUCE, W, M, H, dtype);
   if (st != AR_OK) return st;
+  // The receive buffer is W slots: keep W * M * H * es <= 2^60 as well.
+  if (M > 0 && H > ((int64_t(1) << 60) / (int64_t(W) * elem_size(dtype))) / M)
+    return AR_ERR_UNSUPPORTED;
   const int64_t vec = kVecBytes / elem_size(dtype);
   if (H % vec != 0) return AR_ERR_UNSUPPORTED;
   if (pattern == AR_PATTERN_AR_RESIDUAL_RMSNORM && H / vec > kLamportMaxRowVecs)

@@ -67,6 +67,10 @@ def test_supports_shapes():
     assert ar.ar_supports(RMS, 8, 4, 32768, FP32) == ar.AR_OK
     assert ar.ar_supports(RMS, 8, 4, 32772, FP32) == ar.AR_ERR_UNSUPPORTED
     assert ar.ar_supports(SUM, 8, 1 << 40, 1 << 30, BF16) == ar.AR_ERR_UNSUPPORTED
+    # Huge M alone must not overflow the size check.
+    assert ar.ar_supports(SUM, 8, (1 << 62) + 5, 1, FP32) == ar.AR_ERR_UNSUPPORTED
+    assert ar.ar_supports(SUM, 8, 2 ** 63 - 1, 1, FP32) == ar.AR_ERR_UNSUPPORTED
+    assert ar.ar_supports(SUM, 8, 1 << 59, 1, BF16) == ar.AR_OK           # 2^60 bytes exactly
 
 
 SHAPES = list(itertools.product(

@@ -43,6 +43,10 @@ def test_lamport_validation():
                                          status, 0, None) == ar.AR_ERR_UNSUPPORTED
     assert L.ar_lamport_residual_rmsnorm(*args, None, gam, 1e-6, ro, no, status, 0, None) == \
         ar.AR_ERR_INVALID_ARG
+    # A receive buffer of W slots past 2^60 bytes is refused before any size arithmetic wraps.
+    assert L.ar_lamport_arm(rbuf, 64, 1 << 50, 1 << 5, BF16, None) == ar.AR_ERR_UNSUPPORTED
+    assert L.ar_lamport_push(part, 0, rbuf, 64, 1 << 50, 1 << 5, BF16, None) == \
+        ar.AR_ERR_UNSUPPORTED
     # Zero rows: nothing to do.
     assert L.ar_lamport_sum(None, W, 0, H, BF16, None, None, 0, None) == ar.AR_OK
     assert L.ar_lamport_arm(None, W, 0, H, BF16, None) == ar.AR_OK
