@@ -53,11 +53,16 @@ PMC_SUMMARY = os.path.join(PROFILE_DIR, "norm_kernel_wide_hidden_M2048_pmc.md")
 
 
 def kernel_source_hash() -> str:
+    """Hash of every source the library is built from (kernels, launch planning, build flags):
+    counter figures taken on another build are not reported as this one's traffic."""
     h = hashlib.sha256()
-    for rel in ("all_reduce_residual_amd/csrc/ar_kernels.hpp",
-                "all_reduce_residual_amd/csrc/ar_fused.hip",
-                "all_reduce_residual_amd/_build.py"):
-        with open(os.path.join(ROOT, rel), "rb") as f:
+    csrc = os.path.join(ROOT, "all_reduce_residual_amd", "csrc")
+    paths = sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.hpp"))
+                   + glob.glob(os.path.join(ROOT, "include", "*.h")))
+    paths.append(os.path.join(ROOT, "all_reduce_residual_amd", "_build.py"))
+    for path in paths:
+        h.update(os.path.relpath(path, ROOT).encode())
+        with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
