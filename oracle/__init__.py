@@ -70,6 +70,9 @@ def _load():
         lib.oracle_ar_residual_rmsnorm_rows.argtypes = [
             vp, i32, i64, i64, i32, vp, vp, ctypes.c_float, vp, vp, vp, vp, i64, i64]
         lib.oracle_ar_residual_rmsnorm_rows.restype = i32
+        lib.oracle_rmsnorm_rows.argtypes = [vp, i64, i64, i32, vp, ctypes.c_float, vp, vp, vp,
+                                            i64, i64]
+        lib.oracle_rmsnorm_rows.restype = i32
         _lib = lib
         return lib
 
@@ -181,6 +184,32 @@ def ar_residual_rmsnorm(inputs, residual, gamma, eps: float, dtype: str, rows=No
     if debug:
         return residual_out, norm_out, y, rstd
     return residual_out, norm_out
+
+
+def rmsnorm(x, gamma, eps: float, dtype: str, rows=None, out=None, debug: bool = False):
+    """RMSNorm of a stored [M, H] tensor (the normalisation step of kARResidualRMSNorm alone).
+
+    Returns ``out``, or ``(out, y, rstd)`` with ``debug=True``.
+    """
+    M, H = x.shape
+    _check_array(x, dtype, (M, H))
+    gamma = np.ascontiguousarray(gamma, dtype=np.float32)
+    if gamma.shape != (H,):
+        raise ValueError("gamma must be [H] float32")
+    if out is None:
+        out = np.zeros((M, H), dtype=_storage_np(dtype))
+    _check_array(out, dtype, (M, H))
+    y = np.full((M, H), np.nan) if debug else None
+    rstd = np.full((M,), np.nan) if debug else None
+    r0, r1 = (0, M) if rows is None else rows
+    rc = _load().oracle_rmsnorm_rows(
+        x.ctypes.data, M, H, DTYPE_CODES[dtype], gamma.ctypes.data, float(eps), out.ctypes.data,
+        y.ctypes.data if debug else None, rstd.ctypes.data if debug else None, r0, r1)
+    if rc != 0:
+        raise ValueError("oracle_rmsnorm rejected its arguments")
+    if debug:
+        return out, y, rstd
+    return out
 
 
 # ---- two-shot share --------------------------------------------------------------------------

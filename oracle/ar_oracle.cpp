@@ -216,6 +216,32 @@ int oracle_ar_sum(const void* const* inputs, int W, int64_t M, int64_t H, int dt
   return oracle_ar_sum_rows(inputs, W, M, H, dtype, out, 0, M);
 }
 
+// ---- RMSNorm of one stored row ---------------------------------------------------------------------
+//
+// Row m of x ([M, H], storage type T):
+//   v_i   = x_i widened exactly, then to binary64
+//   rstd  = 1 / sqrt( (sum_i v_i^2) / H + eps )       (binary64, sequential sum over i = 0..H-1)
+//   y_i   = v_i * rstd * gamma_i                       (binary64)
+//   out_i = RN_T( RN_binary32(y_i) )
+static void rmsnorm_row(const void* x, int64_t m, int64_t H, int dtype, const float* gamma,
+                        float eps, void* out, double* y_dbg, double* rstd_dbg) {
+  double sum_sq = 0.0;
+  for (int64_t i = 0; i < H; ++i) {
+    const double v = static_cast<double>(load_widened(x, m * H + i, dtype));
+    sum_sq += v * v;
+  }
+  const double mean_sq = sum_sq / static_cast<double>(H);
+  const double rstd = 1.0 / std::sqrt(mean_sq + static_cast<double>(eps));
+  if (rstd_dbg) rstd_dbg[m] = rstd;
+  for (int64_t i = 0; i < H; ++i) {
+    const int64_t idx = m * H + i;
+    const double v = static_cast<double>(load_widened(x, idx, dtype));
+    const double y = v * rstd * static_cast<double>(gamma[i]);
+    if (y_dbg) y_dbg[idx] = y;
+    store_rounded(out, idx, dtype, static_cast<float>(y));
+  }
+}
+
 // ---- kARResidualRMSNorm ------------------------------------------------------------------------
 //
 // For every row m in [row0, row1):
@@ -245,21 +271,7 @@ int oracle_ar_residual_rmsnorm_rows(const void* const* inputs, int W, int64_t M,
       store_rounded(residual_out, idx, dtype, a);
     }
     // RMSNorm of the stored residual_out row.
-    double sum_sq = 0.0;
-    for (int64_t i = 0; i < H; ++i) {
-      const double v = static_cast<double>(load_widened(residual_out, m * H + i, dtype));
-      sum_sq += v * v;
-    }
-    const double mean_sq = sum_sq / static_cast<double>(H);
-    const double rstd = 1.0 / std::sqrt(mean_sq + static_cast<double>(eps));
-    if (rstd_dbg) rstd_dbg[m] = rstd;
-    for (int64_t i = 0; i < H; ++i) {
-      const int64_t idx = m * H + i;
-      const double v = static_cast<double>(load_widened(residual_out, idx, dtype));
-      const double y = v * rstd * static_cast<double>(gamma[i]);
-      if (y_dbg) y_dbg[idx] = y;
-      store_rounded(norm_out, idx, dtype, static_cast<float>(y));
-    }
+    rmsnorm_row(residual_out, m, H, dtype, gamma, eps, norm_out, y_dbg, rstd_dbg);
   }
   return 0;
 }
@@ -270,6 +282,22 @@ int oracle_ar_residual_rmsnorm(const void* const* inputs, int W, int64_t M, int6
                                double* rstd_dbg) {
   return oracle_ar_residual_rmsnorm_rows(inputs, W, M, H, dtype, residual, gamma, eps,
                                          residual_out, norm_out, y_dbg, rstd_dbg, 0, M);
+}
+
+// ---- RMSNorm of a stored tensor -----------------------------------------------------------------
+//
+// The normalisation step of kARResidualRMSNorm applied to a tensor x that is already stored in T:
+// out = RMSNorm(x) * gamma row by row, exactly as rmsnorm_row defines it (this is what an unfused
+// caller runs after a separate sum-and-residual step).  Rows [row0, row1) only; y_dbg / rstd_dbg
+// as above.  Returns 0, or -1 on a bad argument.
+int oracle_rmsnorm_rows(const void* x, int64_t M, int64_t H, int dtype, const float* gamma,
+                        float eps, void* out, double* y_dbg, double* rstd_dbg, int64_t row0,
+                        int64_t row1) {
+  if (!x || M < 0 || H < 1 || !valid_dtype(dtype) || !gamma || !out) return -1;
+  if (row0 < 0 || row1 > M || row0 > row1) return -1;
+  if (std::fegetround() != FE_TONEAREST) return -1;
+  for (int64_t m = row0; m < row1; ++m) rmsnorm_row(x, m, H, dtype, gamma, eps, out, y_dbg, rstd_dbg);
+  return 0;
 }
 
 }  // extern "C"
