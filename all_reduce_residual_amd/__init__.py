@@ -43,7 +43,7 @@ class ArError(RuntimeError):
         super().__init__("%s: %s (status %d)" % (where, status_string(status), status))
 
 
-ROUTE_ONE_SHOT, ROUTE_TWO_SHOT, ROUTE_FALLBACK = 0, 1, 2
+ROUTE_ONE_SHOT, ROUTE_TWO_SHOT, ROUTE_FALLBACK, ROUTE_UNFUSED = 0, 1, 2, 3
 
 
 class Policy(ctypes.Structure):
@@ -100,6 +100,8 @@ def lib():
                                  ctypes.POINTER(ctypes.c_int64)],
             "ar_all_gather": [vp, i32, i64, i64, i32, vp, vp],
             "ar_device_cu_count": [ctypes.POINTER(ctypes.c_int)],
+            "ar_rmsnorm": [vp, i64, i64, i32, vp, f32, vp, vp],
+            "ar_residual_rmsnorm_unfused": [vp, i32, i64, i64, i32, vp, vp, f32, vp, vp, vp],
         }
         for name, argtypes in sig.items():
             fn = getattr(L, name)
@@ -191,6 +193,39 @@ def ar_residual_rmsnorm(inputs, residual, gamma, eps: float, residual_out, norm_
         cfg = LaunchConfig.from_dict(config)
         st = lib().ar_residual_rmsnorm_with_config(*args, ctypes.byref(cfg))
     _check(st, "ar_residual_rmsnorm")
+
+
+def _check_gamma(gamma, H, device):
+    import torch
+    if gamma.dtype != torch.float32 or tuple(gamma.shape) != (H,) or not gamma.is_contiguous():
+        raise ValueError("gamma must be a contiguous float32 [%d] tensor" % H)
+    if gamma.device != device:
+        raise ValueError("gamma must be on %s" % device)
+
+
+def ar_residual_rmsnorm_unfused(inputs, residual, gamma, eps: float, residual_out, norm_out,
+                                stream=None) -> None:
+    """kARResidualRMSNorm as two kernels (sum with the residual as last addend, then RMSNorm of
+    residual_out): the fallback for rows of any width, with the fused path's results."""
+    ptrs, W, M, H, dt = _marshal_inputs(inputs, residual_out)
+    _marshal_inputs([residual], norm_out)
+    _marshal_inputs([residual], residual_out)
+    _check_gamma(gamma, H, residual_out.device)
+    s = _stream_handle(stream, residual_out.device)
+    _check(lib().ar_residual_rmsnorm_unfused(ptrs, W, M, H, dt, residual.data_ptr(),
+                                             gamma.data_ptr(), float(eps),
+                                             residual_out.data_ptr(), norm_out.data_ptr(), s),
+           "ar_residual_rmsnorm_unfused")
+
+
+def ar_rmsnorm(x, gamma, eps: float, y, stream=None) -> None:
+    """y = RMSNorm(x) * gamma row by row (the normalisation step alone); any row width."""
+    _marshal_inputs([x], y)
+    M, H = y.shape
+    _check_gamma(gamma, H, y.device)
+    s = _stream_handle(stream, y.device)
+    _check(lib().ar_rmsnorm(x.data_ptr(), M, H, dtype_code(y.dtype), gamma.data_ptr(),
+                            float(eps), y.data_ptr(), s), "ar_rmsnorm")
 
 
 def ar_row_partition(W: int, M: int, rank: int):
@@ -289,7 +324,8 @@ def ar_policy_default(W: int) -> Dict[str, int]:
 
 def ar_route(pattern: int, W: int, M: int, H: int, dtype: int,
              policy: Optional[Dict[str, int]] = None) -> int:
-    """ROUTE_ONE_SHOT, ROUTE_TWO_SHOT or ROUTE_FALLBACK for this call (default policy if None)."""
+    """ROUTE_ONE_SHOT, ROUTE_TWO_SHOT, ROUTE_FALLBACK or ROUTE_UNFUSED for this call (default
+    policy if None)."""
     p = Policy(**(policy if policy is not None else ar_policy_default(W if W >= 1 else 1)))
     r = ctypes.c_int(-1)
     _check(lib().ar_route(pattern, W, M, H, dtype, ctypes.byref(p), ctypes.byref(r)), "ar_route")

@@ -220,6 +220,82 @@ inline hipError_t launch_lamport_push_t(const void* partial, void* slot, int64_t
                          dim3(grid), dim3(256), args, 0, s);
 }
 
+// ---- two-kernel (unfused) path -------------------------------------------------------------------
+
+template <class T, int W, int U>
+hipError_t launch_sum_residual_u(const void* const* inputs, const void* residual, void* out,
+                                 int64_t nvec, int tail, const ar_launch_cfg_t& c, hipStream_t s) {
+  RankPtrs<W> p = pack_ptrs<W>(inputs);
+  u32x4* o = static_cast<u32x4*>(out);
+  arf::ResidualSource src{static_cast<const u32x4*>(residual)};
+  void* args[] = {&p, &o, &nvec, &tail, &src};
+  const void* fn =
+      c.nt_store
+          ? reinterpret_cast<const void*>(&arf::ar_sum_kernel<T, W, U, true, arf::ResidualSource>)
+          : reinterpret_cast<const void*>(&arf::ar_sum_kernel<T, W, U, false, arf::ResidualSource>);
+  return hipLaunchKernel(fn, dim3(c.grid), dim3(c.threads_per_block), args, 0, s);
+}
+
+// vecs_per_thread 1 or 2 (the values plan_sum picks).
+template <class T>
+inline hipError_t launch_sum_residual_t(const void* const* inputs, int W, const void* residual,
+                                        void* out, int64_t nvec, int tail,
+                                        const ar_launch_cfg_t& c, hipStream_t s) {
+  if (c.vecs_per_thread == 1) {
+#define AR_CALL(w) launch_sum_residual_u<T, w, 1>(inputs, residual, out, nvec, tail, c, s)
+    AR_W_SWITCH(W, AR_CALL)
+#undef AR_CALL
+  }
+#define AR_CALL(w) launch_sum_residual_u<T, w, 2>(inputs, residual, out, nvec, tail, c, s)
+  AR_W_SWITCH(W, AR_CALL)
+#undef AR_CALL
+}
+
+template <class T, int VPT>
+hipError_t launch_rmsnorm_v(const void* x, const float* gamma, float eps, void* y, int64_t M,
+                            int64_t H, const ar_launch_cfg_t& c, hipStream_t s) {
+  RankPtrs<1> p;
+  p.p[0] = static_cast<const u32x4*>(x);
+  const u32x4* res = nullptr;
+  const f32x4* gam = reinterpret_cast<const f32x4*>(gamma);
+  u32x4* ro = nullptr;
+  u32x4* no = static_cast<u32x4*>(y);
+  int V = static_cast<int>(H / T::kVec);
+  int L = c.lanes_per_row;
+  int R = c.rows_per_block;
+  float count_h = static_cast<float>(H);  // exact: H <= 2^16
+  arf::StreamSource src;
+  void* args[] = {&p, &res, &gam, &ro, &no, &M, &V, &L, &R, &eps, &count_h, &src};
+  const void* fn =
+      c.nt_store
+          ? reinterpret_cast<const void*>(
+                &arf::ar_norm_kernel<T, 1, VPT, true, arf::StreamSource, true>)
+          : reinterpret_cast<const void*>(
+                &arf::ar_norm_kernel<T, 1, VPT, false, arf::StreamSource, true>);
+  return hipLaunchKernel(fn, dim3(c.grid), dim3(c.threads_per_block), args, 0, s);
+}
+
+template <class T>
+inline hipError_t launch_rmsnorm_t(const void* x, const float* gamma, float eps, void* y,
+                                   int64_t M, int64_t H, const ar_launch_cfg_t& c, hipStream_t s) {
+  switch (c.vecs_per_thread) {
+    case 1: return launch_rmsnorm_v<T, 1>(x, gamma, eps, y, M, H, c, s);
+    case 2: return launch_rmsnorm_v<T, 2>(x, gamma, eps, y, M, H, c, s);
+    case 4: return launch_rmsnorm_v<T, 4>(x, gamma, eps, y, M, H, c, s);
+    default: return launch_rmsnorm_v<T, 8>(x, gamma, eps, y, M, H, c, s);
+  }
+}
+
+template <class T>
+inline hipError_t launch_rmsnorm_rows_t(const void* x, const float* gamma, float eps, void* y,
+                                        int64_t M, int64_t H, int grid, int threads,
+                                        hipStream_t s) {
+  float count_h = static_cast<float>(H);
+  void* args[] = {&x, &gamma, &y, &M, &H, &eps, &count_h};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&arf::ar_rmsnorm_rows_kernel<T>),
+                         dim3(grid), dim3(threads), args, 0, s);
+}
+
 // ---- per-element-type entry points (defined in inst_bf16.hip, inst_f16.hip, inst_f32.hip) ----
 
 #define AR_DECLARE_LAUNCHERS(suffix)                                                         \
@@ -238,7 +314,16 @@ inline hipError_t launch_lamport_push_t(const void* partial, void* slot, int64_t
                                           const ar_launch_cfg_t& c, arf::LamportSource src,   \
                                           hipStream_t s);                                     \
   hipError_t launch_lamport_push_##suffix(const void* partial, void* slot, int64_t nvec,      \
-                                          int grid, hipStream_t s);
+                                          int grid, hipStream_t s);                           \
+  hipError_t launch_sum_residual_##suffix(const void* const* inputs, int W,                   \
+                                          const void* residual, void* out, int64_t nvec,      \
+                                          int tail, const ar_launch_cfg_t& c, hipStream_t s); \
+  hipError_t launch_rmsnorm_##suffix(const void* x, const float* gamma, float eps, void* y,   \
+                                     int64_t M, int64_t H, const ar_launch_cfg_t& c,          \
+                                     hipStream_t s);                                          \
+  hipError_t launch_rmsnorm_rows_##suffix(const void* x, const float* gamma, float eps,       \
+                                          void* y, int64_t M, int64_t H, int grid,            \
+                                          int threads, hipStream_t s);
 AR_DECLARE_LAUNCHERS(bf16)
 AR_DECLARE_LAUNCHERS(f16)
 AR_DECLARE_LAUNCHERS(f32)

@@ -212,10 +212,12 @@ int validate_sum(const void* const* inputs, int W, int64_t M, int64_t H, int dty
   return AR_OK;
 }
 
+// shape_pattern: AR_PATTERN_AR_RESIDUAL_RMSNORM for the fused kernel (whole vectors per row,
+// register-resident rows); AR_PATTERN_ALLREDUCE for the two-kernel path (any row width).
 int validate_norm(const void* const* inputs, int W, int64_t M, int64_t H, int dtype,
                   const void* residual, const float* gamma, float eps, const void* residual_out,
-                  const void* norm_out) {
-  const int st = check_shape(AR_PATTERN_AR_RESIDUAL_RMSNORM, W, M, H, dtype);
+                  const void* norm_out, int shape_pattern = AR_PATTERN_AR_RESIDUAL_RMSNORM) {
+  const int st = check_shape(shape_pattern, W, M, H, dtype);
   if (st != AR_OK) return st;
   if (!std::isfinite(eps) || eps < 0.0f) return AR_ERR_INVALID_ARG;
   if (M == 0) return AR_OK;
@@ -309,6 +311,105 @@ int run_norm(const void* const* inputs, int W, int64_t M, int64_t H, int dtype,
       break;
   }
   return e == hipSuccess ? AR_OK : AR_ERR_LAUNCH;
+}
+
+// ---- two-kernel (unfused) path and the stand-alone RMSNorm ----------------------------------------
+//
+// The route for kARResidualRMSNorm shapes the fused kernel does not take (rows that are not whole
+// 16-byte vectors, or wider than a block keeps in registers): the pages' policy layer sends such
+// calls to an unfused fallback (tokenspeed pull request, Body / Routing; vLLM pull request,
+// Scope).  Kernel 1 is the flat sum kernel with the residual as one more addend, so residual_out
+// is bit-identical to the fused kernel's; kernel 2 is RMSNorm of residual_out.
+
+bool norm_fits_fused(int64_t H, int dtype) {
+  return check_shape(AR_PATTERN_AR_RESIDUAL_RMSNORM, 1, 0, H, dtype) == AR_OK;
+}
+
+int validate_rmsnorm(const void* x, int64_t M, int64_t H, int dtype, const float* gamma,
+                     float eps, const void* y) {
+  int st = check_shape(AR_PATTERN_ALLREDUCE, 1, M, H, dtype);
+  if (st != AR_OK) return st;
+  if (!std::isfinite(eps) || eps < 0.0f) return AR_ERR_INVALID_ARG;
+  if (M == 0) return AR_OK;
+  if (!x || !gamma || !y) return AR_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(gamma) || !aligned16(y)) return AR_ERR_MISALIGNED;
+  const int64_t bytes = M * H * elem_size(dtype);
+  const Range yr = range_of(y, bytes);
+  if (bad_alias_with_input(yr, range_of(x, bytes))) return AR_ERR_ALIAS;
+  if (overlap(yr, range_of(gamma, H * int64_t(sizeof(float))))) return AR_ERR_ALIAS;
+  return AR_OK;
+}
+
+// Launches RMSNorm of x into y (validated arguments, M > 0): the row kernel in norm-only mode
+// when rows fit it, else the two-pass kernel for rows of any width.
+int launch_rmsnorm(const void* x, int64_t M, int64_t H, int dtype, const float* gamma, float eps,
+                   void* y, hipStream_t s) {
+  int cu = 0;
+  const int st = query_cu_count(&cu);
+  if (st != AR_OK) return st;
+  hipError_t e;
+  if (norm_fits_fused(H, dtype)) {
+    ar_launch_cfg_t cfg;
+    plan_norm(1, M, H, dtype, cu, &cfg);
+    switch (dtype) {
+      case AR_DTYPE_FP32: e = arfh::launch_rmsnorm_f32(x, gamma, eps, y, M, H, cfg, s); break;
+      case AR_DTYPE_FP16: e = arfh::launch_rmsnorm_f16(x, gamma, eps, y, M, H, cfg, s); break;
+      default: e = arfh::launch_rmsnorm_bf16(x, gamma, eps, y, M, H, cfg, s); break;
+    }
+  } else {
+    // One block per row: enough threads for ~8 elements each (whole waves, at most 1024), and
+    // at most 8 blocks per CU with a grid stride over further rows.
+    const int threads = static_cast<int>(std::min<int64_t>(1024, round_up(ceil_div(H, 8), 64)));
+    const int grid = cap_grid(std::min<int64_t>(M, int64_t(cu) * 8));
+    switch (dtype) {
+      case AR_DTYPE_FP32:
+        e = arfh::launch_rmsnorm_rows_f32(x, gamma, eps, y, M, H, grid, threads, s);
+        break;
+      case AR_DTYPE_FP16:
+        e = arfh::launch_rmsnorm_rows_f16(x, gamma, eps, y, M, H, grid, threads, s);
+        break;
+      default: e = arfh::launch_rmsnorm_rows_bf16(x, gamma, eps, y, M, H, grid, threads, s); break;
+    }
+  }
+  return e == hipSuccess ? AR_OK : AR_ERR_LAUNCH;
+}
+
+int run_rmsnorm(const void* x, int64_t M, int64_t H, int dtype, const float* gamma, float eps,
+                void* y, void* stream) {
+  const int st = validate_rmsnorm(x, M, H, dtype, gamma, eps, y);
+  if (st != AR_OK || M == 0) return st;
+  return launch_rmsnorm(x, M, H, dtype, gamma, eps, y, static_cast<hipStream_t>(stream));
+}
+
+int run_unfused(const void* const* inputs, int W, int64_t M, int64_t H, int dtype,
+                const void* residual, const float* gamma, float eps, void* residual_out,
+                void* norm_out, void* stream) {
+  int st = validate_norm(inputs, W, M, H, dtype, residual, gamma, eps, residual_out, norm_out,
+                         AR_PATTERN_ALLREDUCE);
+  if (st != AR_OK || M == 0) return st;
+  int cu = 0;
+  st = query_cu_count(&cu);
+  if (st != AR_OK) return st;
+  ar_launch_cfg_t cfg;
+  plan_sum(W + 1, M * H, dtype, cu, &cfg);
+  const int64_t vec = kVecBytes / elem_size(dtype);
+  const int64_t nvec = M * H / vec;
+  const int tail = static_cast<int>(M * H - nvec * vec);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  switch (dtype) {
+    case AR_DTYPE_FP32:
+      e = arfh::launch_sum_residual_f32(inputs, W, residual, residual_out, nvec, tail, cfg, s);
+      break;
+    case AR_DTYPE_FP16:
+      e = arfh::launch_sum_residual_f16(inputs, W, residual, residual_out, nvec, tail, cfg, s);
+      break;
+    default:
+      e = arfh::launch_sum_residual_bf16(inputs, W, residual, residual_out, nvec, tail, cfg, s);
+      break;
+  }
+  if (e != hipSuccess) return AR_ERR_LAUNCH;
+  return launch_rmsnorm(residual_out, M, H, dtype, gamma, eps, norm_out, s);
 }
 
 // ---- two-shot share ------------------------------------------------------------------------------
@@ -578,6 +679,17 @@ int ar_residual_rmsnorm_with_config(const void* const* inputs, int W, int64_t M,
                   cfg);
 }
 
+int ar_rmsnorm(const void* x, int64_t M, int64_t H, int dtype, const float* gamma, float eps,
+               void* y, void* stream) {
+  return run_rmsnorm(x, M, H, dtype, gamma, eps, y, stream);
+}
+
+int ar_residual_rmsnorm_unfused(const void* const* inputs, int W, int64_t M, int64_t H,
+                                int dtype, const void* residual, const float* gamma, float eps,
+                                void* residual_out, void* norm_out, void* stream) {
+  return run_unfused(inputs, W, M, H, dtype, residual, gamma, eps, residual_out, norm_out, stream);
+}
+
 int ar_supports(int pattern, int W, int64_t M, int64_t H, int dtype) {
   return check_shape(pattern, W, M, H, dtype);
 }
@@ -654,13 +766,19 @@ int ar_route(int pattern, int W, int64_t M, int64_t H, int dtype, const ar_polic
     return AR_ERR_INVALID_ARG;
   if (policy->min_tokens < 0 || policy->two_shot_min_bytes < 0 || policy->max_payload_bytes < 0)
     return AR_ERR_INVALID_ARG;
-  if (check_shape(pattern, W, M, H, dtype) != AR_OK) {
+  const bool fused_ok = check_shape(pattern, W, M, H, dtype) == AR_OK;
+  // A norm row the fused kernel does not take still has the two-kernel path.
+  const bool unfused_ok = !fused_ok && pattern == AR_PATTERN_AR_RESIDUAL_RMSNORM &&
+                          check_shape(AR_PATTERN_ALLREDUCE, W, M, H, dtype) == AR_OK;
+  if (!fused_ok && !unfused_ok) {
     *route = AR_ROUTE_FALLBACK;
     return AR_OK;
   }
   const int64_t payload = M * H * elem_size(dtype);
   if (policy->max_payload_bytes > 0 && payload > policy->max_payload_bytes) {
     *route = AR_ROUTE_FALLBACK;
+  } else if (unfused_ok) {
+    *route = AR_ROUTE_UNFUSED;
   } else if (M < policy->min_tokens || payload < policy->two_shot_min_bytes) {
     *route = AR_ROUTE_ONE_SHOT;
   } else {

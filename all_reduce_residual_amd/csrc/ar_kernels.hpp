@@ -294,6 +294,9 @@ struct StreamSource {
     (void)ok;
     rank_sum<T, W, N, kMaxLoads>(in, base, boff, acc);
   }
+  // Terms after the W partials for the element-wise tail of the flat sum: none.
+  template <class T>
+  __device__ inline float tail_extra(float a, int64_t) const { return a; }
 };
 
 // ---- kAllReduce -----------------------------------------------------------------------------
@@ -343,7 +346,7 @@ __global__ __launch_bounds__(kMaxThreads) void ar_sum_kernel(RankPtrs<W> in, u32
     float a = -0.0f;
 #pragma unroll
     for (int r = 0; r < W; ++r) a = a + T::widen1(in.p[r], i);
-    T::store1(out, i, a);
+    T::store1(out, i, src.template tail_extra<T>(a, i));
   }
 }
 
@@ -357,6 +360,25 @@ __device__ inline void accumulate(float (&acc)[T::kVec], u32x4 v) {
 #pragma unroll
   for (int e = 0; e < T::kVec; ++e) acc[e] = acc[e] + x[e];
 }
+
+// The W partials and then the residual as one more addend, so the flat sum kernel computes
+// residual_out = RN_T(x_0 + ... + x_{W-1} + residual) with the same binary32 chain as the fused
+// kernel: the first kernel of the two-kernel (unfused) path, which accepts rows of any width.
+struct ResidualSource {
+  const u32x4* residual;
+  template <class T, int W, int N, int kMaxLoads = (N * T::kVec >= 32 ? 8 : 16)>
+  __device__ inline void sum(const RankPtrs<W>& in, int64_t base, const uint32_t (&boff)[N],
+                             const bool (&ok)[N], float (&acc)[N][T::kVec]) const {
+    (void)ok;
+    rank_sum<T, W, N, kMaxLoads>(in, base, boff, acc);
+#pragma unroll
+    for (int k = 0; k < N; ++k) accumulate<T>(acc[k], load_stream(at(residual + base, boff[k])));
+  }
+  template <class T>
+  __device__ inline float tail_extra(float a, int64_t i) const {
+    return a + T::widen1(residual, i);
+  }
+};
 
 // The kVec gamma values of element vector `vec` (gamma is binary32 [H], 16-byte aligned).
 template <int kVec>
@@ -374,7 +396,11 @@ __device__ inline void load_gamma(const f32x4* gamma, uint32_t vec, float (&g)[k
 // One row = V vectors of 16 bytes.  Thread t of a block serves row slot t / L (R slots per
 // block) and, within the row, vectors lane + k * L for k < VPT.  L * VPT >= V.  Blocks walk
 // groups of R rows with a grid stride.
-template <class T, int W, int VPT, bool kNtStore, class Src = StreamSource>
+//
+// kNormOnly: the RMSNorm step alone on a stored tensor x = in.p[0] (W = 1; residual and
+// residual_out are unused): norm_out = RMSNorm(x) * gamma.  The second kernel of the two-kernel
+// path, and a stand-alone RMSNorm.
+template <class T, int W, int VPT, bool kNtStore, class Src = StreamSource, bool kNormOnly = false>
 __global__ __launch_bounds__(kMaxThreads) void ar_norm_kernel(
     RankPtrs<W> in, const u32x4* residual, const f32x4* gamma, u32x4* residual_out,
     u32x4* norm_out, int64_t M, int V, int L, int R, float eps, float count_h, Src src) {
@@ -426,7 +452,11 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_kernel(
 
     // Sum of the W partials and the residual, binary32 in rank order, rounded once to T.
     u32x4 rounded[VPT];
-    if constexpr (VPT <= 2) {
+    if constexpr (kNormOnly) {
+      static_assert(W == 1, "the norm-only mode reads one tensor");
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) rounded[k] = load_stream(at(in.p[0] + base, boff[k]));
+    } else if constexpr (VPT <= 2) {
       // All vectors' chains together: the most independent loads per batch.
       float acc[VPT][kVec];
       src.template sum<T, W, VPT>(in, base, boff, ok, acc);
@@ -452,7 +482,7 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_kernel(
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
       if (ok[k]) {
-        store_vec<kNtStore>(at(residual_out + base, boff[k]), rounded[k]);
+        if constexpr (!kNormOnly) store_vec<kNtStore>(at(residual_out + base, boff[k]), rounded[k]);
         float v[kVec];
         T::widen(rounded[k], v);
 #pragma unroll
@@ -495,6 +525,42 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_kernel(
         for (int e = 0; e < kVec; ++e) y[e] = (v[e] * rstd) * g[e];
         store_vec<kNtStore>(at(norm_out + base, boff[k]), T::narrow(y));
       }
+    }
+  }
+}
+
+// RMSNorm of rows of any width and any element alignment: the second kernel of the two-kernel
+// path when a row is not a whole number of 16-byte vectors or is too wide to keep in registers.
+// One block per row (grid stride over rows).  Pass 1 sums the squares of the row's elements
+// (ordinary loads, so the row stays in cache); pass 2 reads the row again and writes
+// y = RN_T((x * rstd) * gamma).  y may be x itself: each element is read and then written by the
+// same thread, after every read of pass 1.
+template <class T>
+__global__ __launch_bounds__(kMaxThreads) void ar_rmsnorm_rows_kernel(const void* x,
+                                                                      const float* gamma,
+                                                                      void* y, int64_t M,
+                                                                      int64_t H, float eps,
+                                                                      float count_h) {
+  __shared__ float red[kMaxWavesPerBlock];
+  const int tid = threadIdx.x;
+  const int waves = blockDim.x >> 6;
+  for (int64_t m = blockIdx.x; m < M; m += gridDim.x) {
+    const int64_t row = m * H;
+    float ss = 0.0f;
+    for (int64_t i = tid; i < H; i += blockDim.x) {
+      const float v = T::widen1(x, row + i);
+      ss += v * v;
+    }
+    ss = segment_sum(ss, 64);
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    float t = red[0];
+    for (int j = 1; j < waves; ++j) t += red[j];
+    __syncthreads();  // every wave has read red before the next row overwrites it
+    const float rstd = rsqrtf(t / count_h + eps);
+    for (int64_t i = tid; i < H; i += blockDim.x) {
+      const float v = T::widen1(x, row + i);
+      T::store1(y, row + i, (v * rstd) * gamma[i]);
     }
   }
 }
@@ -627,6 +693,9 @@ struct LamportSource {
       if (r0 + kBatch < W) batch_fence(acc);
     }
   }
+  // The exchange moves whole vectors only: no element-wise tail.
+  template <class T>
+  __device__ inline float tail_extra(float a, int64_t) const { return a; }
 };
 
 // Producer: slot[i] = canonicalize(src[i]) for nvec 16-byte vectors, as 64-bit agent-scope words.

@@ -34,4 +34,20 @@ hipError_t launch_lamport_push_bf16(const void* partial, void* slot, int64_t nve
   return launch_lamport_push_t<Bf16>(partial, slot, nvec, grid, s);
 }
 
+hipError_t launch_sum_residual_bf16(const void* const* inputs, int W, const void* residual,
+                                  void* out, int64_t nvec, int tail, const ar_launch_cfg_t& c,
+                                  hipStream_t s) {
+  return launch_sum_residual_t<Bf16>(inputs, W, residual, out, nvec, tail, c, s);
+}
+
+hipError_t launch_rmsnorm_bf16(const void* x, const float* gamma, float eps, void* y,
+                             int64_t M, int64_t H, const ar_launch_cfg_t& c, hipStream_t s) {
+  return launch_rmsnorm_t<Bf16>(x, gamma, eps, y, M, H, c, s);
+}
+
+hipError_t launch_rmsnorm_rows_bf16(const void* x, const float* gamma, float eps, void* y,
+                                  int64_t M, int64_t H, int grid, int threads, hipStream_t s) {
+  return launch_rmsnorm_rows_t<Bf16>(x, gamma, eps, y, M, H, grid, threads, s);
+}
+
 }  // namespace arfh

@@ -34,4 +34,20 @@ hipError_t launch_lamport_push_f16(const void* partial, void* slot, int64_t nvec
   return launch_lamport_push_t<F16>(partial, slot, nvec, grid, s);
 }
 
+hipError_t launch_sum_residual_f16(const void* const* inputs, int W, const void* residual,
+                                  void* out, int64_t nvec, int tail, const ar_launch_cfg_t& c,
+                                  hipStream_t s) {
+  return launch_sum_residual_t<F16>(inputs, W, residual, out, nvec, tail, c, s);
+}
+
+hipError_t launch_rmsnorm_f16(const void* x, const float* gamma, float eps, void* y,
+                             int64_t M, int64_t H, const ar_launch_cfg_t& c, hipStream_t s) {
+  return launch_rmsnorm_t<F16>(x, gamma, eps, y, M, H, c, s);
+}
+
+hipError_t launch_rmsnorm_rows_f16(const void* x, const float* gamma, float eps, void* y,
+                                  int64_t M, int64_t H, int grid, int threads, hipStream_t s) {
+  return launch_rmsnorm_rows_t<F16>(x, gamma, eps, y, M, H, grid, threads, s);
+}
+
 }  // namespace arfh

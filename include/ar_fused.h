@@ -31,8 +31,9 @@
  * workspace and retains no pointer, so calls are safe to capture in a hipGraph and replay.  The
  * only state is a per-device cache of the compute-unit count.
  *
- * Streams: `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue one kernel and
- * return without synchronising; the return code reports argument validation and the launch only.
+ * Streams: `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue one kernel (two
+ * for ar_residual_rmsnorm_unfused) and return without synchronising; the return code reports
+ * argument validation and the launch only.
  * Device faults surface on the stream as usual.
  *
  * Errors: every entry point returns an ar_status_t.  On any non-zero status nothing was launched
@@ -211,6 +212,38 @@ int ar_lamport_residual_rmsnorm(void* rbuf, int W, int64_t M, int64_t H, int dty
                                 void* residual_out, void* norm_out, int* status,
                                 uint32_t spin_limit, void* stream);
 
+/* ---- two-kernel (unfused) path and the stand-alone RMSNorm -------------------------------------------
+ *
+ * The pages' policy layer sends calls the fused kernel cannot take to an unfused fallback (the
+ * tokenspeed pull request, Body and Routing, uses each path as the other's shape fallback; the
+ * vLLM pull request, Scope, routes unsupported cases to the fallback).  This library's own
+ * fallback for kARResidualRMSNorm is two kernels on the stream: the flat sum kernel with the
+ * residual as the last addend (residual_out), then RMSNorm of residual_out (norm_out).  It takes
+ * rows of any width H >= 1 (the fused kernel needs whole 16-byte vectors per row and at most
+ * AR_MAX_H_16BIT / AR_MAX_H_FP32 elements), with the same results: residual_out bit-identical,
+ * norm_out within one unit in the last place of T of the exact expression. */
+
+/* RMSNorm of a stored tensor, the normalisation step of kARResidualRMSNorm alone:
+ *   y[m, i] = RN_T( x[m, i] * rsqrt(mean_i(x[m, i]^2) + eps) * gamma[i] )
+ *   x     : device [M, H] of type `dtype`, 16-byte aligned; any H >= 1
+ *   gamma : device [H] binary32, 16-byte aligned
+ *   eps   : finite, >= 0
+ *   y     : device [M, H]; may be exactly x (in place); must not partially overlap x or overlap
+ *           gamma
+ * Rows of whole 16-byte vectors up to AR_MAX_H_16BIT / AR_MAX_H_FP32 elements run the fused
+ * kernel's row machinery (one read, values kept in registers); other rows run a two-pass kernel
+ * (the second pass re-reads the row, normally from cache).  M = 0 returns AR_OK. */
+int ar_rmsnorm(const void* x, int64_t M, int64_t H, int dtype, const float* gamma, float eps,
+               void* y, void* stream);
+
+/* kARResidualRMSNorm as two kernels, for any H >= 1.  Arguments, aliasing rules and results as
+ * ar_residual_rmsnorm; W in the same supported set.  Enqueues two kernels on `stream`.  The one
+ * exception to "nothing launched on error": if the second launch fails, AR_ERR_LAUNCH is
+ * returned after the first (residual_out) was enqueued; norm_out is then not written. */
+int ar_residual_rmsnorm_unfused(const void* const* inputs, int W, int64_t M, int64_t H,
+                                int dtype, const void* residual, const float* gamma, float eps,
+                                void* residual_out, void* norm_out, void* stream);
+
 /* ---- routing policy ------------------------------------------------------------------------------
  *
  * The policy layer that picks a path per call, after the pages: the tokenspeed pull request
@@ -221,7 +254,9 @@ int ar_lamport_residual_rmsnorm(void* rbuf, int W, int64_t M, int64_t H, int dty
 typedef enum {
   AR_ROUTE_ONE_SHOT = 0,  /* ar_sum / ar_residual_rmsnorm over all W peers' buffers */
   AR_ROUTE_TWO_SHOT = 1,  /* reduce-scatter share on the rank's rows, then ar_all_gather */
-  AR_ROUTE_FALLBACK = 2   /* not this library: the caller's collective (e.g. RCCL) */
+  AR_ROUTE_FALLBACK = 2,  /* not this library: the caller's collective (e.g. RCCL) */
+  AR_ROUTE_UNFUSED = 3    /* kARResidualRMSNorm rows the fused kernel does not take:
+                             ar_residual_rmsnorm_unfused */
 } ar_route_t;
 
 typedef struct {
@@ -241,9 +276,11 @@ typedef struct {
  * crossover needs two GPUs to measure. */
 int ar_policy_default(int W, ar_policy_t* policy);
 
-/* Route for one call: AR_ROUTE_FALLBACK if ar_supports rejects the shape (e.g. W = 12) or the
- * payload exceeds max_payload_bytes; otherwise AR_ROUTE_ONE_SHOT below min_tokens or below
- * two_shot_min_bytes, else AR_ROUTE_TWO_SHOT.  Returns AR_OK and sets *route, or
+/* Route for one call: AR_ROUTE_FALLBACK if neither the fused kernel nor the two-kernel path
+ * takes the shape (e.g. W = 12) or the payload exceeds max_payload_bytes; AR_ROUTE_UNFUSED for a
+ * norm row only the two-kernel path takes (H not a multiple of 16 / sizeof(T), or above the
+ * fused limit); otherwise AR_ROUTE_ONE_SHOT below min_tokens or below two_shot_min_bytes, else
+ * AR_ROUTE_TWO_SHOT.  Returns AR_OK and sets *route, or
  * AR_ERR_INVALID_ARG for a null pointer, a negative threshold or a bad pattern. */
 int ar_route(int pattern, int W, int64_t M, int64_t H, int dtype, const ar_policy_t* policy,
              int* route);

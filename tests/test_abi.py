@@ -26,7 +26,8 @@ def test_exports_every_declared_function(L):
                           "ar_status_string", "ar_device_cu_count", "ar_row_partition",
                           "ar_all_gather", "ar_lamport_arm", "ar_lamport_push",
                           "ar_lamport_sum", "ar_lamport_residual_rmsnorm",
-                          "ar_policy_default", "ar_route"}
+                          "ar_policy_default", "ar_route", "ar_rmsnorm",
+                          "ar_residual_rmsnorm_unfused"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -173,3 +174,33 @@ def test_zero_rows_returns_ok_without_device(L):
     assert L.ar_sum(None, 2, 0, 256, BF16, None, None) == ar.AR_OK
     assert L.ar_residual_rmsnorm(None, 2, 0, 256, BF16, None, None, 1e-6, None, None,
                                  None) == ar.AR_OK
+
+
+def test_unfused_and_rmsnorm_validation(L):
+    """The two-kernel path takes any row width but the same world sizes, pointers and alias
+    rules; the stand-alone RMSNorm rejects null, misaligned and overlapping buffers."""
+    p = [0x10000 * (i + 1) for i in range(16)]
+    args = (2, 4, 7170, BF16, 0xA00000, 0xB00000, 1e-6, 0xC00000, 0xD00000, None)
+    assert L.ar_residual_rmsnorm_unfused(_ptrs(p[:12]), 12, 4, 7170, BF16, 0xA00000, 0xB00000,
+                                         1e-6, 0xC00000, 0xD00000, None) == ar.AR_ERR_UNSUPPORTED
+    assert L.ar_residual_rmsnorm_unfused(None, *args) == ar.AR_ERR_INVALID_ARG
+    assert L.ar_residual_rmsnorm_unfused(_ptrs([p[0] + 2, p[1]]), *args) == ar.AR_ERR_MISALIGNED
+    assert L.ar_residual_rmsnorm_unfused(_ptrs(p[:2]), 2, 4, 7170, BF16, 0xA00000, 0xB00000,
+                                         -1.0, 0xC00000, 0xD00000, None) == ar.AR_ERR_INVALID_ARG
+    # norm_out overlapping residual_out.
+    assert L.ar_residual_rmsnorm_unfused(_ptrs(p[:2]), 2, 4, 7170, BF16, 0xA00000, 0xB00000,
+                                         1e-6, 0xC00000, 0xC00000 + 4096, None) == ar.AR_ERR_ALIAS
+    assert L.ar_residual_rmsnorm_unfused(None, 2, 0, 7170, BF16, None, None, 1e-6, None, None,
+                                         None) == ar.AR_OK
+    # Stand-alone RMSNorm.
+    x, g, y = 0x100000, 0x200000, 0x300000
+    assert L.ar_rmsnorm(None, 4, 7, BF16, g, 1e-6, y, None) == ar.AR_ERR_INVALID_ARG
+    assert L.ar_rmsnorm(x, 4, 0, BF16, g, 1e-6, y, None) == ar.AR_ERR_INVALID_ARG
+    assert L.ar_rmsnorm(x, 4, 7, 5, g, 1e-6, y, None) == ar.AR_ERR_INVALID_ARG
+    assert L.ar_rmsnorm(x, 4, 7, BF16, g, float("nan"), y, None) == ar.AR_ERR_INVALID_ARG
+    assert L.ar_rmsnorm(x + 2, 4, 7, BF16, g, 1e-6, y, None) == ar.AR_ERR_MISALIGNED
+    assert L.ar_rmsnorm(x, 4, 7, BF16, g + 4, 1e-6, y, None) == ar.AR_ERR_MISALIGNED
+    assert L.ar_rmsnorm(x, 4, 7, BF16, g, 1e-6, x + 16, None) == ar.AR_ERR_ALIAS
+    assert L.ar_rmsnorm(x, 4, 7, BF16, y + 16, 1e-6, y, None) == ar.AR_ERR_ALIAS
+    assert L.ar_rmsnorm(x, 1 << 40, 1 << 30, BF16, g, 1e-6, y, None) == ar.AR_ERR_UNSUPPORTED
+    assert L.ar_rmsnorm(None, 0, 7, BF16, None, 1e-6, None, None) == ar.AR_OK

@@ -1,6 +1,7 @@
 """Routing policy (host only): the pages' decision rules as the library implements them.
 
-* unsupported world sizes (12, 3, ...) and unsupported shapes go to the caller's fallback;
+* unsupported world sizes (12, 3, ...) go to the caller's fallback; norm rows the fused kernel
+  does not take (odd widths, rows past its limit) go to the library's two-kernel path;
 * below the token threshold (32 by default) every call stays one-shot;
 * from the two-shot payload threshold on, two-shot; a per-rank payload cutoff sends larger
   calls to the fallback;
@@ -10,7 +11,7 @@ import pytest
 
 import all_reduce_residual_amd as ar
 
-ONE, TWO, FB = ar.ROUTE_ONE_SHOT, ar.ROUTE_TWO_SHOT, ar.ROUTE_FALLBACK
+ONE, TWO, FB, UNF = ar.ROUTE_ONE_SHOT, ar.ROUTE_TWO_SHOT, ar.ROUTE_FALLBACK, ar.ROUTE_UNFUSED
 RMS, SUM, BF16 = ar.PATTERN_AR_RESIDUAL_RMSNORM, ar.PATTERN_ALLREDUCE, ar.DTYPE_BF16
 
 
@@ -32,9 +33,15 @@ def test_world_size_twelve_falls_back():
         assert ar.ar_route(pat, 8, 256, 7168, BF16) != FB
 
 
-def test_unsupported_shape_falls_back():
-    assert ar.ar_route(RMS, 8, 64, 7170, BF16) == FB       # norm rows need whole vectors
-    assert ar.ar_route(SUM, 8, 64, 7170, BF16) == ONE      # the sum takes any H
+def test_norm_rows_the_fused_kernel_rejects_take_the_two_kernel_path():
+    assert ar.ar_route(RMS, 8, 64, 7170, BF16) == UNF      # not whole 16-byte vectors
+    assert ar.ar_route(RMS, 8, 1, 7170, BF16) == UNF       # at any token count
+    assert ar.ar_route(RMS, 8, 4, 65544, BF16) == UNF      # wider than the fused limit
+    assert ar.ar_route(RMS, 8, 4, 32772, ar.DTYPE_FP32) == UNF
+    assert ar.ar_route(SUM, 8, 64, 7170, BF16) == ONE      # the sum kernel takes any H
+    assert ar.ar_route(RMS, 12, 64, 7170, BF16) == FB      # world size still decides first
+    pol = dict(min_tokens=32, two_shot_min_bytes=1 << 20, max_payload_bytes=1 << 20)
+    assert ar.ar_route(RMS, 8, 1024, 7170, BF16, pol) == FB   # payload cutoff applies too
 
 
 def test_token_threshold_and_payload():
