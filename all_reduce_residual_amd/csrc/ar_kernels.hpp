@@ -301,45 +301,61 @@ struct StreamSource {
 
 // ---- kAllReduce -----------------------------------------------------------------------------
 
+// out = RN_T(x_0 + ... + x_{W-1}) for one chunk of blockDim.x * U vectors starting at vector
+// `cbase` (uniform); lane t owns vectors cbase + t + u * blockDim.x.
+template <class T, int W, int U, bool kNtStore, class Src>
+__device__ inline void sum_chunk(const RankPtrs<W>& in, u32x4* out, int64_t nvec, int64_t cbase,
+                                 int64_t chunk, const Src& src) {
+  uint32_t boff[U];
+  float acc[U][T::kVec];
+  if (cbase + chunk <= nvec) {
+    // Whole chunk in range (uniform branch): no predicate anywhere near the loads.
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      boff[u] = (threadIdx.x + u * blockDim.x) * 16u;
+      ok[u] = true;
+    }
+    src.template sum<T, W, U>(in, cbase, boff, ok, acc);
+#pragma unroll
+    for (int u = 0; u < U; ++u) store_vec<kNtStore>(at(out + cbase, boff[u]), T::narrow(acc[u]));
+  } else {
+    // Last, partial chunk: slots past the end re-read the last vector (a clamp, not a branch,
+    // so the loads stay unconditional) and are not stored.
+    const uint32_t last = static_cast<uint32_t>(nvec - cbase - 1);
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t i = threadIdx.x + u * blockDim.x;
+      boff[u] = (i < last ? i : last) * 16u;
+      ok[u] = i <= last;
+    }
+    src.template sum<T, W, U>(in, cbase, boff, ok, acc);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (ok[u]) store_vec<kNtStore>(at(out + cbase, boff[u]), T::narrow(acc[u]));
+    }
+  }
+}
+
 // out = RN_T(x_0 + ... + x_{W-1}) over n elements: nvec full 16-byte vectors, then a tail of
-// fewer than one vector handled element by element by block 0.  Blocks walk chunks of
-// blockDim.x * U vectors with a grid stride; lane t of a chunk owns vectors t + u * blockDim.x.
+// fewer than one vector handled element by element by block 0.  When the grid covers every
+// chunk (the launch heuristic always sizes it so) each block sums its one chunk with no loop;
+// a smaller grid walks the chunks with a grid stride.  The loop-free form matters: inside a
+// loop the compiler hoists each tensor's per-lane address out as a 64-bit pointer stepped per
+// iteration (instead of the scalar base + 32-bit offset form) and, for some (W, U), then issues
+// the loads a round trip apart.
 template <class T, int W, int U, bool kNtStore, class Src = StreamSource>
 __global__ __launch_bounds__(kMaxThreads) void ar_sum_kernel(RankPtrs<W> in, u32x4* out,
                                                              int64_t nvec, int tail, Src src) {
   constexpr int kVec = T::kVec;
   const int64_t chunk = static_cast<int64_t>(blockDim.x) * U;
-  for (int64_t cbase = blockIdx.x * chunk; cbase < nvec; cbase += gridDim.x * chunk) {
-    uint32_t boff[U];
-    float acc[U][kVec];
-    if (cbase + chunk <= nvec) {
-      // Whole chunk in range (uniform branch): no predicate anywhere near the loads.
-      bool ok[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        boff[u] = (threadIdx.x + u * blockDim.x) * 16u;
-        ok[u] = true;
-      }
-      src.template sum<T, W, U>(in, cbase, boff, ok, acc);
-#pragma unroll
-      for (int u = 0; u < U; ++u) store_vec<kNtStore>(at(out + cbase, boff[u]), T::narrow(acc[u]));
-    } else {
-      // Last, partial chunk: slots past the end re-read the last vector (a clamp, not a
-      // branch, so the loads stay unconditional) and are not stored.
-      const uint32_t last = static_cast<uint32_t>(nvec - cbase - 1);
-      bool ok[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const uint32_t i = threadIdx.x + u * blockDim.x;
-        boff[u] = (i < last ? i : last) * 16u;
-        ok[u] = i <= last;
-      }
-      src.template sum<T, W, U>(in, cbase, boff, ok, acc);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (ok[u]) store_vec<kNtStore>(at(out + cbase, boff[u]), T::narrow(acc[u]));
-      }
-    }
+  if (static_cast<int64_t>(gridDim.x) * chunk >= nvec) {
+    const int64_t cbase = blockIdx.x * chunk;
+    if (cbase < nvec) sum_chunk<T, W, U, kNtStore>(in, out, nvec, cbase, chunk, src);
+  } else {
+    for (int64_t cbase = blockIdx.x * chunk; cbase < nvec; cbase += gridDim.x * chunk)
+      sum_chunk<T, W, U, kNtStore>(in, out, nvec, cbase, chunk, src);
   }
   if (tail > 0 && blockIdx.x == 0 && static_cast<int>(threadIdx.x) < tail) {
     const int64_t i = nvec * kVec + threadIdx.x;
