@@ -68,7 +68,12 @@ def kernel_source_hash() -> str:
 
 
 def metric_bytes(pattern: str, W: int, M: int, H: int, esize: int) -> int:
-    extra = 3 if pattern == "rms" else 1
+    """Algorithmic bytes of one call: W partials (+ residual) read, outputs written.  The
+    two-kernel path is charged the fused op's bytes (same result, so the same metric); the
+    stand-alone RMSNorm reads x and writes y."""
+    if pattern == "rmsnorm":
+        return 2 * M * H * esize
+    extra = 3 if pattern in ("rms", "unfused") else 1
     return (W + extra) * M * H * esize
 
 
@@ -97,13 +102,15 @@ class Case:
             return t.to(tdt)
 
         self.parts = [randn(*dist) for _ in range(W)]
-        if pattern == "rms":
+        if pattern in ("rms", "unfused", "rmsnorm"):
             self.res = randn(0.0, 1.0)
             self.gamma = torch.empty(H, dtype=torch.float32, device="cuda").uniform_(
                 0.8, 1.2, generator=g)
             self.ro = torch.empty_like(self.res)
             self.no = torch.empty_like(self.res)
-            self.fn = ar.lib().ar_residual_rmsnorm
+            self.fn = {"rms": ar.lib().ar_residual_rmsnorm,
+                       "unfused": ar.lib().ar_residual_rmsnorm_unfused,
+                       "rmsnorm": ar.lib().ar_rmsnorm}[pattern]
         else:
             self.out = torch.empty_like(self.parts[0])
             self.fn = ar.lib().ar_sum
@@ -118,7 +125,10 @@ class Case:
     def _args_for(self, r):
         ptrs = (ctypes.c_void_p * self.W)(*[self._sl(p, r) for p in self.parts])
         self._keep.append(ptrs)
-        if self.pattern == "rms":
+        if self.pattern == "rmsnorm":
+            return (self._sl(self.res, r), self.M, self.H, self.dt, self.gamma.data_ptr(),
+                    ctypes.c_float(self.eps), self._sl(self.no, r))
+        if self.pattern in ("rms", "unfused"):
             return (ptrs, self.W, self.M, self.H, self.dt, self._sl(self.res, r),
                     self.gamma.data_ptr(), ctypes.c_float(self.eps), self._sl(self.ro, r),
                     self._sl(self.no, r))
@@ -229,6 +239,38 @@ def two_shot_lines(ar, torch, W=8, H=7168, Ms=(128, 512, 2048)) -> list:
             del rs
             torch.cuda.empty_cache()
             print("# two-shot %s" % json.dumps(lines[-1]), file=sys.stderr, flush=True)
+    return lines
+
+
+# The other workloads the metric is quoted on (configs besides the wide-hidden sweep), and the
+# routing fallback: (label, pattern, W, M, H, dtype).
+CONFIG_LINES = [
+    ("tiny W=2 M=4 H=256", "rms", 2, 4, 256, "bf16"),
+    ("Llama-3 decode W=2 M=128 H=4096", "rms", 2, 128, 4096, "bf16"),
+    ("TP4 80 MiB W=4 M=5120 H=8192", "sum", 4, 5120, 8192, "bf16"),
+    ("TP16 8 MiB fp16 W=16 M=512 H=8192", "rms", 16, 512, 8192, "fp16"),
+    ("two-kernel path, W=8 M=2048 H=7168", "unfused", 8, 2048, 7168, "bf16"),
+    ("two-kernel path, odd width W=8 M=2048 H=7170", "unfused", 8, 2048, 7170, "bf16"),
+    ("stand-alone RMSNorm M=2048 H=7168", "rmsnorm", 1, 2048, 7168, "bf16"),
+    ("stand-alone RMSNorm, odd width M=2048 H=7170", "rmsnorm", 1, 2048, 7170, "bf16"),
+]
+
+
+def config_lines(ar, torch) -> list:
+    """hipGraph-replayed µs/call (rotated buffers) of CONFIG_LINES."""
+    lines = []
+    names = {"rms": "kARResidualRMSNorm", "sum": "kAllReduce",
+             "unfused": "kARResidualRMSNorm (two kernels)", "rmsnorm": "RMSNorm"}
+    for label, pattern, W, M, H, dt in CONFIG_LINES:
+        c = Case(ar, torch, pattern, W, M, H, dtype=dt)
+        us = c.time_graph(c.calls_per_batch(50 if c.bytes >= (64 << 20) else 200))
+        gbs = c.bytes / (us * 1e-6) / 1e9
+        lines.append({"config": label, "pattern": names[pattern], "W": W, "M": M, "H": H,
+                      "element_type": dt, "bytes": c.bytes, "us_graph": round(us, 3),
+                      "GBs": round(gbs, 1), "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2)})
+        print("# config %s" % json.dumps(lines[-1]), file=sys.stderr, flush=True)
+        del c
+        torch.cuda.empty_cache()
     return lines
 
 
@@ -585,6 +627,7 @@ def main():
                 torch.cuda.empty_cache()
         result["sweep"] = sweep
         result["two_shot_share"] = two_shot_lines(ar, torch)
+        result["configs"] = config_lines(ar, torch)
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline()
