@@ -286,14 +286,22 @@ inline hipError_t launch_rmsnorm_t(const void* x, const float* gamma, float eps,
   }
 }
 
+// vecs_per_thread: 1, 2, 4 or 8 (row values kept in registers) or 0 (two passes over memory).
 template <class T>
 inline hipError_t launch_rmsnorm_rows_t(const void* x, const float* gamma, float eps, void* y,
                                         int64_t M, int64_t H, int grid, int threads,
-                                        hipStream_t s) {
+                                        int vecs_per_thread, hipStream_t s) {
   float count_h = static_cast<float>(H);
   void* args[] = {&x, &gamma, &y, &M, &H, &eps, &count_h};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&arf::ar_rmsnorm_rows_kernel<T>),
-                         dim3(grid), dim3(threads), args, 0, s);
+  const void* fn;
+  switch (vecs_per_thread) {
+    case 1: fn = reinterpret_cast<const void*>(&arf::ar_rmsnorm_rows_kernel<T, 1>); break;
+    case 2: fn = reinterpret_cast<const void*>(&arf::ar_rmsnorm_rows_kernel<T, 2>); break;
+    case 4: fn = reinterpret_cast<const void*>(&arf::ar_rmsnorm_rows_kernel<T, 4>); break;
+    case 8: fn = reinterpret_cast<const void*>(&arf::ar_rmsnorm_rows_kernel<T, 8>); break;
+    default: fn = reinterpret_cast<const void*>(&arf::ar_rmsnorm_rows_kernel<T, 0>); break;
+  }
+  return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, 0, s);
 }
 
 // ---- per-element-type entry points (defined in inst_bf16.hip, inst_f16.hip, inst_f32.hip) ----
@@ -323,7 +331,7 @@ inline hipError_t launch_rmsnorm_rows_t(const void* x, const float* gamma, float
                                      hipStream_t s);                                          \
   hipError_t launch_rmsnorm_rows_##suffix(const void* x, const float* gamma, float eps,       \
                                           void* y, int64_t M, int64_t H, int grid,            \
-                                          int threads, hipStream_t s);
+                                          int threads, int vecs_per_thread, hipStream_t s);
 AR_DECLARE_LAUNCHERS(bf16)
 AR_DECLARE_LAUNCHERS(f16)
 AR_DECLARE_LAUNCHERS(f32)

@@ -357,18 +357,30 @@ int launch_rmsnorm(const void* x, int64_t M, int64_t H, int dtype, const float* 
       default: e = arfh::launch_rmsnorm_bf16(x, gamma, eps, y, M, H, cfg, s); break;
     }
   } else {
-    // One block per row: enough threads for ~8 elements each (whole waves, at most 1024), and
-    // at most 8 blocks per CU with a grid stride over further rows.
-    const int threads = static_cast<int>(std::min<int64_t>(1024, round_up(ceil_div(H, 8), 64)));
+    // One block per row, grid stride over rows (at most 8 blocks per CU).  A row spans at most
+    // H / vec + 2 aligned vectors; the fewest vectors per thread (1, 2, 4 or 8) that keep the
+    // block at <= 512 threads (1024 for 8) hold the row in registers, else two passes.
+    const int vec = kVecBytes / elem_size(dtype);
+    const int64_t nv = H / vec + 2;
+    int vpt = 0;
+    int64_t threads = 1024;
+    for (int k = 1; k <= 8; k *= 2) {
+      if (ceil_div(nv, k) <= (k == 8 ? 1024 : 512)) {
+        vpt = k;
+        threads = round_up(ceil_div(nv, k), 64);
+        break;
+      }
+    }
+    const int t = static_cast<int>(threads);
     const int grid = cap_grid(std::min<int64_t>(M, int64_t(cu) * 8));
     switch (dtype) {
       case AR_DTYPE_FP32:
-        e = arfh::launch_rmsnorm_rows_f32(x, gamma, eps, y, M, H, grid, threads, s);
+        e = arfh::launch_rmsnorm_rows_f32(x, gamma, eps, y, M, H, grid, t, vpt, s);
         break;
       case AR_DTYPE_FP16:
-        e = arfh::launch_rmsnorm_rows_f16(x, gamma, eps, y, M, H, grid, threads, s);
+        e = arfh::launch_rmsnorm_rows_f16(x, gamma, eps, y, M, H, grid, t, vpt, s);
         break;
-      default: e = arfh::launch_rmsnorm_rows_bf16(x, gamma, eps, y, M, H, grid, threads, s); break;
+      default: e = arfh::launch_rmsnorm_rows_bf16(x, gamma, eps, y, M, H, grid, t, vpt, s); break;
     }
   }
   return e == hipSuccess ? AR_OK : AR_ERR_LAUNCH;

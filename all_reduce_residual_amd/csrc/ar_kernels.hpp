@@ -545,38 +545,117 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_kernel(
   }
 }
 
-// RMSNorm of rows of any width and any element alignment: the second kernel of the two-kernel
-// path when a row is not a whole number of 16-byte vectors or is too wide to keep in registers.
-// One block per row (grid stride over rows).  Pass 1 sums the squares of the row's elements
-// (ordinary loads, so the row stays in cache); pass 2 reads the row again and writes
-// y = RN_T((x * rstd) * gamma).  y may be x itself: each element is read and then written by the
-// same thread, after every read of pass 1.
+// ---- RMSNorm of rows of any width ----------------------------------------------------------------
+//
+// The second kernel of the two-kernel path when a row is not a whole number of 16-byte vectors
+// (or too wide for the row kernel).  Row m spans elements [e0, e1) = [m H, m H + H) of a
+// 16-byte-aligned tensor; the row is walked as the aligned 16-byte vectors v0 .. v0 + nv - 1 that
+// cover it.  Vectors wholly inside the row are loaded and stored whole; the (at most two)
+// vectors the row shares with its neighbours are read and written element by element, only the
+// row's own elements, so no access leaves the tensor and no block writes another row's data.
+
+// The kVec values of vector v restricted to [e0, e1) (zeros elsewhere).
+template <class T, bool kStream>
+__device__ inline void load_row_vec(const void* x, int64_t e0, int64_t e1, int64_t v,
+                                    float (&f)[T::kVec]) {
+  const int64_t a = v * T::kVec;
+  if (a >= e0 && a + T::kVec <= e1) {
+    const u32x4* p = static_cast<const u32x4*>(x) + v;
+    T::widen(kStream ? load_stream(p) : *p, f);
+  } else {
+#pragma unroll
+    for (int e = 0; e < T::kVec; ++e) {
+      const int64_t idx = a + e;
+      f[e] = (idx >= e0 && idx < e1) ? T::widen1(x, idx) : 0.0f;
+    }
+  }
+}
+
+// y = RN_T((f * rstd) * gamma) for the row's elements of vector v.
 template <class T>
+__device__ inline void store_row_vec(void* y, const float* gamma, int64_t e0, int64_t e1,
+                                     int64_t v, const float (&f)[T::kVec], float rstd) {
+  const int64_t a = v * T::kVec;
+  if (a >= e0 && a + T::kVec <= e1) {
+    const float* g = gamma + (a - e0);
+    float o[T::kVec];
+#pragma unroll
+    for (int e = 0; e < T::kVec; ++e) o[e] = (f[e] * rstd) * g[e];
+    store_vec<true>(static_cast<u32x4*>(y) + v, T::narrow(o));
+  } else {
+#pragma unroll
+    for (int e = 0; e < T::kVec; ++e) {
+      const int64_t idx = a + e;
+      if (idx >= e0 && idx < e1) T::store1(y, idx, (f[e] * rstd) * gamma[idx - e0]);
+    }
+  }
+}
+
+// Block-wide sum of one value per thread (every thread gets the total); `red` holds one float
+// per wave and is free again when this returns.
+__device__ inline float block_sum(float v, float* red) {
+  v = segment_sum(v, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float t = red[0];
+  for (int j = 1; j < static_cast<int>(blockDim.x >> 6); ++j) t += red[j];
+  __syncthreads();  // every wave has read red before it is written again
+  return t;
+}
+
+// One block per row (grid stride over rows).  K > 0: thread t owns vectors t + k * blockDim.x
+// (k < K) and keeps their values in registers between the sum of squares and the scaling, so x
+// is read once.  K = 0 (rows longer than 8 vectors per thread of a 1024-thread block): the row is
+// read twice, the second time normally from cache.  y may be x itself: every element is read
+// (pass 1) before the barrier and written afterwards by the thread that read it.
+template <class T, int K>
 __global__ __launch_bounds__(kMaxThreads) void ar_rmsnorm_rows_kernel(const void* x,
                                                                       const float* gamma,
                                                                       void* y, int64_t M,
                                                                       int64_t H, float eps,
                                                                       float count_h) {
+  constexpr int kVec = T::kVec;
   __shared__ float red[kMaxWavesPerBlock];
-  const int tid = threadIdx.x;
-  const int waves = blockDim.x >> 6;
+  const int64_t nthreads = blockDim.x;
   for (int64_t m = blockIdx.x; m < M; m += gridDim.x) {
-    const int64_t row = m * H;
+    const int64_t e0 = m * H;
+    const int64_t e1 = e0 + H;
+    const int64_t v0 = e0 / kVec;
+    const int64_t nv = (e1 + kVec - 1) / kVec - v0;
     float ss = 0.0f;
-    for (int64_t i = tid; i < H; i += blockDim.x) {
-      const float v = T::widen1(x, row + i);
-      ss += v * v;
-    }
-    ss = segment_sum(ss, 64);
-    if ((tid & 63) == 0) red[tid >> 6] = ss;
-    __syncthreads();
-    float t = red[0];
-    for (int j = 1; j < waves; ++j) t += red[j];
-    __syncthreads();  // every wave has read red before the next row overwrites it
-    const float rstd = rsqrtf(t / count_h + eps);
-    for (int64_t i = tid; i < H; i += blockDim.x) {
-      const float v = T::widen1(x, row + i);
-      T::store1(y, row + i, (v * rstd) * gamma[i]);
+    if constexpr (K > 0) {
+      float f[K][kVec];
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int64_t j = threadIdx.x + k * nthreads;
+        if (j < nv) {
+          load_row_vec<T, true>(x, e0, e1, v0 + j, f[k]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < kVec; ++e) f[k][e] = 0.0f;
+        }
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) ss += f[k][e] * f[k][e];
+      }
+      const float rstd = rsqrtf(block_sum(ss, red) / count_h + eps);
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int64_t j = threadIdx.x + k * nthreads;
+        if (j < nv) store_row_vec<T>(y, gamma, e0, e1, v0 + j, f[k], rstd);
+      }
+    } else {
+      for (int64_t j = threadIdx.x; j < nv; j += nthreads) {
+        float f[kVec];
+        load_row_vec<T, false>(x, e0, e1, v0 + j, f);
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) ss += f[e] * f[e];
+      }
+      const float rstd = rsqrtf(block_sum(ss, red) / count_h + eps);
+      for (int64_t j = threadIdx.x; j < nv; j += nthreads) {
+        float f[kVec];
+        load_row_vec<T, false>(x, e0, e1, v0 + j, f);
+        store_row_vec<T>(y, gamma, e0, e1, v0 + j, f, rstd);
+      }
     }
   }
 }

@@ -46,8 +46,9 @@ hipError_t launch_rmsnorm_bf16(const void* x, const float* gamma, float eps, voi
 }
 
 hipError_t launch_rmsnorm_rows_bf16(const void* x, const float* gamma, float eps, void* y,
-                                  int64_t M, int64_t H, int grid, int threads, hipStream_t s) {
-  return launch_rmsnorm_rows_t<Bf16>(x, gamma, eps, y, M, H, grid, threads, s);
+                                  int64_t M, int64_t H, int grid, int threads, int vecs_per_thread,
+                                  hipStream_t s) {
+  return launch_rmsnorm_rows_t<Bf16>(x, gamma, eps, y, M, H, grid, threads, vecs_per_thread, s);
 }
 
 }  // namespace arfh

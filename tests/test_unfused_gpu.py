@@ -126,8 +126,11 @@ def test_unfused_zero_rows():
 
 # ---- stand-alone RMSNorm ---------------------------------------------------------------------------
 
+# Odd widths reach every vectors-per-thread choice of the any-width kernel (1, 2, 4, 8 and the
+# two-pass form): 1001, 7170, 12345, 40001, 65544 / 200003 at 16 bits.
 RMS_SHAPES = [(1, 1), (4, 7), (3, 64), (9, 256), (5, 1001), (17, 7168), (2, 8192), (3, 65536),
-              (2, 65544), (1, 200003), (300, 128)]
+              (2, 65544), (1, 200003), (300, 128), (3, 7170), (3, 12345), (2, 40001),
+              (600, 13)]
 
 
 @pytest.mark.parametrize("M,H", RMS_SHAPES, ids=["M%d-H%d" % s for s in RMS_SHAPES])
@@ -143,7 +146,7 @@ def test_rmsnorm_matches_oracle(oracle_mod, M, H, dtype):
     assert_norm_close(host_np(y.cpu()), want, dtype)
 
 
-@pytest.mark.parametrize("H", [7168, 1001])
+@pytest.mark.parametrize("H", [7168, 1001, 40001, 70001])
 def test_rmsnorm_in_place(oracle_mod, H):
     parts, _, gam = synth.custom(1, 6, H, "fp16", seed=H)
     want = oracle_mod.rmsnorm(host_np(parts[0]), gam.numpy(), 1e-5, "fp16")
