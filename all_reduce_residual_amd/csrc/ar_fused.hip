@@ -118,7 +118,9 @@ void plan_sum(int W, int64_t n, int dtype, int cu, ar_launch_cfg_t* c) {
   // independent waves for the dispatcher to spread over the 256 CUs.  Small payloads (fewer
   // than 16 such blocks per CU) do better with two vectors per thread and half the blocks.
   const int threads = 64;
-  const int u = ceil_div(nvec, threads) < int64_t(cu) * 16 ? 2 : 1;
+  // (Two vectors per thread only for W <= 8: beyond that the doubled loads and rank pointers no
+  // longer fit the registers and spill.)
+  const int u = (W <= 8 && ceil_div(nvec, threads) < int64_t(cu) * 16) ? 2 : 1;
   c->threads_per_block = threads;
   c->vecs_per_thread = u;
   c->lanes_per_row = 0;
@@ -132,7 +134,6 @@ void plan_sum(int W, int64_t n, int dtype, int cu, ar_launch_cfg_t* c) {
 }
 
 void plan_norm(int W, int64_t M, int64_t H, int dtype, int cu, ar_launch_cfg_t* c) {
-  (void)W;
   const int64_t vec = kVecBytes / elem_size(dtype);
   const int64_t V = H / vec;
   int vpt, lanes, threads;
@@ -144,8 +145,14 @@ void plan_norm(int W, int64_t M, int64_t H, int dtype, int cu, ar_launch_cfg_t* 
     threads = (M >= int64_t(cu) * rows_per_wave * 4 * 4) ? 256 : 64;
   } else {
     // Wide rows: one row per block of up to 512 threads (two 16-byte vectors per thread at
-    // H = 7168 bf16: 7 waves), the shape that measured fastest from decode to prefill sizes.
-    const int64_t target = 512;
+    // H = 7168 bf16: 7 waves), the shape that measured fastest from decode to prefill sizes
+    // for W >= 4.  With one or two partials a row is few bytes, and once there are more rows
+    // than CUs the block per row shrinks in proportion (512 lanes / rows per CU, at least one
+    // wave) with more vectors per thread: more rows in flight per CU (W = 2, M = 2048,
+    // H = 4096: one wave of 8 vectors per thread per row, 13 % faster than 512 lanes; at
+    // W = 4 the 512-lane shape stays ahead, measured).
+    int64_t target = 512;
+    if (W <= 2) target = std::max<int64_t>(64, 512 / std::max<int64_t>(1, M / cu));
     vpt = 1;
     while (vpt < 8 && ceil_div(V, vpt) > target) vpt *= 2;
     while (vpt < 8 && round_up(ceil_div(V, vpt), 64) > 1024) vpt *= 2;

@@ -218,8 +218,12 @@ template <class T, int W, int N, int R0 = 0, int kMaxLoads = (N * T::kVec >= 32 
 __device__ inline void rank_sum_range(const RankPtrs<W>& in, int64_t base,
                                       const uint32_t (&boff)[N], float (&acc)[N][T::kVec]) {
   constexpr int kBatch = rank_batch<W - R0 < 1 ? 1 : W - R0, N, kMaxLoads>();
-  if constexpr (W > 32 && R0 == 0 && 16 % kBatch == 0) {
-    // More rank pointers than scalar registers (2 per pointer): left to itself the compiler
+  // At W = 32 the grouped walk below pays only with small batches (the norm kernel's
+  // one-vector-at-a-time chains for very wide rows: 2x faster); with 16-load batches the
+  // unrolled form is faster (measured).
+  constexpr bool kGrouped = W > 32 || (W == 32 && kBatch <= 8);
+  if constexpr (kGrouped && R0 == 0 && 16 % kBatch == 0) {
+    // About as many rank pointers as scalar registers (2 per pointer): left to itself the compiler
     // spills them to VGPR lanes and, reloading them one at a time, issues one load per DRAM
     // round trip.  Instead walk groups of 16 ranks in a loop that is not unrolled, so each
     // group's pointers are read from the kernel arguments when the group is reached, and stage
@@ -472,8 +476,9 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_kernel(
       static_assert(W == 1, "the norm-only mode reads one tensor");
 #pragma unroll
       for (int k = 0; k < VPT; ++k) rounded[k] = load_stream(at(in.p[0] + base, boff[k]));
-    } else if constexpr (VPT <= 2) {
-      // All vectors' chains together: the most independent loads per batch.
+    } else if constexpr (VPT <= 2 || (W + 1) * VPT <= 20) {
+      // All vectors' chains together: the most independent loads per batch (with few
+      // partials even 4-8 vectors' accumulators fit beside a batch of loads, no spill).
       float acc[VPT][kVec];
       src.template sum<T, W, VPT>(in, base, boff, ok, acc);
 #pragma unroll
