@@ -528,12 +528,12 @@ int run_lamport_arm(void* rbuf, int W, int64_t M, int64_t H, int dtype, void* st
   int cu = 0;
   st = query_cu_count(&cu);
   if (st != AR_OK) return st;
-  uint64_t* buf = static_cast<uint64_t*>(rbuf);
-  int64_t nwords = int64_t(W) * M * H * elem_size(dtype) / 8;
-  void* args[] = {&buf, &nwords};
+  u32x4* buf = static_cast<u32x4*>(rbuf);
+  int64_t nvec = int64_t(W) * M * H * elem_size(dtype) / kVecBytes;
+  void* args[] = {&buf, &nvec};
   const hipError_t e =
-      hipLaunchKernel(reinterpret_cast<const void*>(&arf::ar_lamport_arm_kernel<uint64_t>),
-                      dim3(lamport_grid(nwords, cu)), dim3(256), args, 0,
+      hipLaunchKernel(reinterpret_cast<const void*>(&arf::ar_lamport_arm_kernel<u32x4>),
+                      dim3(lamport_grid(nvec, cu)), dim3(256), args, 0,
                       static_cast<hipStream_t>(stream));
   return e == hipSuccess ? AR_OK : AR_ERR_LAUNCH;
 }
@@ -554,7 +554,9 @@ int run_lamport_push(const void* partial, int rank, void* rbuf, int W, int64_t M
   void* slot = static_cast<char*>(rbuf) + rank * slot_bytes;
   const int64_t nvec = slot_bytes / kVecBytes;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int grid = lamport_grid(nvec, cu);
+  // One vector per thread and a grid that covers the slot: the kernel runs no loop.
+  (void)cu;
+  const int grid = cap_grid(ceil_div(nvec, 256));
   hipError_t e;
   switch (dtype) {
     case AR_DTYPE_FP32: e = arfh::launch_lamport_push_f32(partial, slot, nvec, grid, s); break;

@@ -674,11 +674,17 @@ __global__ __launch_bounds__(kMaxThreads) void ar_rmsnorm_rows_kernel(const void
 // and a producer's data can never equal it because the producer replaces an all-ones element by
 // the same value with its lowest bit cleared (still a NaN).  The consumer polls each element until
 // it is not the sentinel, reduces, and writes the sentinel back so the slot is empty for the next
-// round.  Words are moved with 64-bit relaxed atomics at agent scope, so a producer kernel and a
-// consumer kernel running at the same time on different XCDs see each other's words.  Every wait
-// is bounded: after `spin_limit` polls of one word the consumer gives up, sets bit 0 of `*status`
-// and continues with what it read (the affected outputs are then meaningless; the caller checks
-// the status).
+// round.
+//
+// Slots are moved as 16-byte buffer loads and stores carrying the device-coherence cache bit
+// (sc1, the form of a relaxed agent-scope atomic on this architecture) and the streaming hint:
+// a producer kernel and a consumer kernel running at the same time on different XCDs see each
+// other's data.  A 16-byte access is not atomic as a whole, but each naturally aligned dword of
+// it is, and an element (2 or 4 bytes) never straddles a dword, so every element the consumer
+// reads is either the sentinel or the producer's complete value; the consumer checks elements,
+// not vectors.  Every wait is bounded: after `spin_limit` polls of one vector the consumer gives
+// up, sets bit 0 of `*status` and continues with what it read (the affected outputs are then
+// meaningless; the caller checks the status).
 
 template <class T>
 struct LaneMask;
@@ -709,44 +715,64 @@ __device__ inline uint64_t canonicalize(uint64_t w) {
   return w & ~(high >> shift);
 }
 
-__device__ inline uint64_t load_agent(const uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ inline uint64_t lo64(u32x4 v) { return v.x | (static_cast<uint64_t>(v.y) << 32); }
+__device__ inline uint64_t hi64(u32x4 v) { return v.z | (static_cast<uint64_t>(v.w) << 32); }
+
+template <class T>
+__device__ inline bool has_sentinel(u32x4 v) {
+  return (sentinel_lanes<T>(lo64(v)) | sentinel_lanes<T>(hi64(v))) != 0;
 }
-__device__ inline void store_agent(uint64_t* p, uint64_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+// Cache-policy bits of a buffer access: sc1 (device coherence) | nt (streaming).
+constexpr int kCoherentNt = 16 | 2;
+// Raw buffer over [base, base + 4 GiB): word 3 selects 32-bit data format, no swizzle.
+__device__ inline __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, -1, 0x00020000);
+}
+// The 16 bytes at byte offset boff of a uniform base, device-coherent.
+__device__ inline u32x4 load_coherent(const u32x4* base, uint32_t boff) {
+  return __builtin_bit_cast(
+      u32x4, __builtin_amdgcn_raw_buffer_load_b128(coherent_rsrc(base), boff, 0, kCoherentNt));
+}
+__device__ inline void store_coherent(u32x4* base, uint32_t boff, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, coherent_rsrc(base), boff, 0, kCoherentNt);
 }
 
 struct LamportSource {
   int* status;          // bit 0 set on a poll timeout
-  uint32_t spin_limit;  // polls per word before giving up
+  uint32_t spin_limit;  // polls per vector before giving up
 
-  // Polls *p until no element of w is empty.  After its first timeout a thread stops waiting
-  // (`gave_up`), so a missing producer costs each thread at most one spin limit.
+  // Polls the vector at base + boff until no element is empty.  After its first timeout a
+  // thread stops waiting (`gave_up`), so a missing producer costs each thread at most one spin
+  // limit.  The empty asm with a memory clobber keeps the reload inside the loop.
   template <class T>
-  __device__ inline uint64_t wait_word(const uint64_t* p, uint64_t w, bool& gave_up) const {
+  __device__ inline u32x4 wait_vec(const u32x4* base, uint32_t boff, u32x4 v,
+                                   bool& gave_up) const {
     uint32_t n = 0;
-    while (!gave_up && sentinel_lanes<T>(w) != 0) {
+    while (!gave_up && has_sentinel<T>(v)) {
       if (n++ >= spin_limit) {
         __hip_atomic_fetch_or(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         gave_up = true;
         break;
       }
       __builtin_amdgcn_s_sleep(2);
-      w = load_agent(p);
+      asm volatile("" : : : "memory");
+      v = load_coherent(base, boff);
     }
-    return w;
+    return v;
   }
 
-  // acc[k] = -0 + slot_0[k] + ... + slot_{W-1}[k], each 16-byte vector read as two words: all
-  // words of a batch are loaded first, then only words still empty are polled again, then the
-  // batch is accumulated in rank order and its words are re-armed with the sentinel.
-  // Slots that are not real (ok[k] false) neither read nor re-arm anything: their clamped
-  // offset points at another lane's vector, which they must not empty.
+  // acc[k] = -0 + slot_0[k] + ... + slot_{W-1}[k]: all vectors of a batch are loaded first, then
+  // only vectors still holding an empty element are polled again, then the batch is accumulated
+  // in rank order and re-armed with the sentinel.  Slots that are not real (ok[k] false) neither
+  // read nor re-arm anything: their clamped offset points at another lane's vector, which they
+  // must not empty.
   template <class T, int W, int N, int kMaxLoads = (N * T::kVec >= 32 ? 8 : 16)>
   __device__ inline void sum(const RankPtrs<W>& in, int64_t base, const uint32_t (&boff)[N],
                              const bool (&ok)[N], float (&acc)[N][T::kVec]) const {
-    // Polled words stay live until accumulated: half the stream source's batch.
+    // Polled vectors stay live until accumulated: half the stream source's batch.
     constexpr int kBatch = rank_batch<W, N, (kMaxLoads / 2 > 0 ? kMaxLoads / 2 : 1)>();
+    const u32x4 empty = {~0u, ~0u, ~0u, ~0u};
     bool gave_up = false;
 #pragma unroll
     for (int k = 0; k < N; ++k) {
@@ -755,69 +781,81 @@ struct LamportSource {
     }
 #pragma unroll
     for (int r0 = 0; r0 < W; r0 += kBatch) {
-      uint64_t w[kBatch][N][2];
+      u32x4 w[kBatch][N];
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
         if (r0 + j >= W) break;
 #pragma unroll
         for (int k = 0; k < N; ++k) {
-          const uint64_t* p = reinterpret_cast<const uint64_t*>(at(in.p[r0 + j] + base, boff[k]));
-          w[j][k][0] = ok[k] ? load_agent(p) : 0;
-          w[j][k][1] = ok[k] ? load_agent(p + 1) : 0;
+          w[j][k] = ok[k] ? load_coherent(in.p[r0 + j] + base, boff[k]) : u32x4{0, 0, 0, 0};
         }
       }
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
         if (r0 + j >= W) break;
+        const u32x4* slot = in.p[r0 + j] + base;
 #pragma unroll
         for (int k = 0; k < N; ++k) {
-          const uint64_t* p = reinterpret_cast<const uint64_t*>(at(in.p[r0 + j] + base, boff[k]));
-          w[j][k][0] = wait_word<T>(p, w[j][k][0], gave_up);
-          w[j][k][1] = wait_word<T>(p + 1, w[j][k][1], gave_up);
-          u32x4 v;
-          v.x = static_cast<uint32_t>(w[j][k][0]);
-          v.y = static_cast<uint32_t>(w[j][k][0] >> 32);
-          v.z = static_cast<uint32_t>(w[j][k][1]);
-          v.w = static_cast<uint32_t>(w[j][k][1] >> 32);
+          const u32x4 v = wait_vec<T>(slot, boff[k], w[j][k], gave_up);
           float x[T::kVec];
           T::widen(v, x);
 #pragma unroll
           for (int e = 0; e < T::kVec; ++e) acc[k][e] = acc[k][e] + x[e];
-          if (ok[k]) {
-            uint64_t* q = const_cast<uint64_t*>(p);
-            store_agent(q, ~0ull);
-            store_agent(q + 1, ~0ull);
-          }
+        }
+      }
+      // Re-arm the batch only after all of it is read: a store between two polls would make
+      // every later check wait for that store's round trip.
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        if (r0 + j >= W) break;
+        u32x4* slot = const_cast<u32x4*>(in.p[r0 + j] + base);
+#pragma unroll
+        for (int k = 0; k < N; ++k) {
+          if (ok[k]) store_coherent(slot, boff[k], empty);
         }
       }
       if (r0 + kBatch < W) batch_fence(acc);
     }
   }
+
   // The exchange moves whole vectors only: no element-wise tail.
   template <class T>
   __device__ inline float tail_extra(float a, int64_t) const { return a; }
 };
 
-// Producer: slot[i] = canonicalize(src[i]) for nvec 16-byte vectors, as 64-bit agent-scope words.
+// Producer: slot[i] = canonicalize(src[i]) for nvec 16-byte vectors, device-coherent stores.
+// One 16-byte vector per thread; a grid that covers every vector runs no loop.
 template <class T>
 __global__ __launch_bounds__(kMaxThreads) void ar_lamport_push_kernel(const u32x4* src,
                                                                       u32x4* slot, int64_t nvec) {
-  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < nvec;
-       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const u32x4 v = load_stream(src + i);
-    uint64_t* q = reinterpret_cast<uint64_t*>(slot + i);
-    store_agent(q, canonicalize<T>(v.x | (static_cast<uint64_t>(v.y) << 32)));
-    store_agent(q + 1, canonicalize<T>(v.z | (static_cast<uint64_t>(v.w) << 32)));
+  const int64_t chunk = blockDim.x;
+  const uint32_t boff = threadIdx.x * 16u;
+  auto one = [&](int64_t cbase) {
+    if (cbase + threadIdx.x < nvec) {
+      const u32x4 v = load_stream(at(src + cbase, boff));
+      const uint64_t lo = canonicalize<T>(lo64(v)), hi = canonicalize<T>(hi64(v));
+      const u32x4 c = {static_cast<uint32_t>(lo), static_cast<uint32_t>(lo >> 32),
+                       static_cast<uint32_t>(hi), static_cast<uint32_t>(hi >> 32)};
+      store_coherent(slot + cbase, boff, c);
+    }
+  };
+  if (static_cast<int64_t>(gridDim.x) * chunk >= nvec) {
+    one(blockIdx.x * chunk);
+  } else {
+    for (int64_t cbase = blockIdx.x * chunk; cbase < nvec; cbase += gridDim.x * chunk) one(cbase);
   }
 }
 
-// Arms (empties) nwords 64-bit words of a receive buffer.  (A template so that the header
+// Arms (empties) nvec 16-byte vectors of a receive buffer.  (A template so that the header
 // defines no kernel by itself: it is instantiated in one translation unit only.)
-template <class Word>
-__global__ __launch_bounds__(kMaxThreads) void ar_lamport_arm_kernel(Word* buf, int64_t nwords) {
-  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < nwords;
-       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
-    store_agent(buf + i, ~0ull);
+template <class V>
+__global__ __launch_bounds__(kMaxThreads) void ar_lamport_arm_kernel(V* buf, int64_t nvec) {
+  const int64_t chunk = blockDim.x;
+  const uint32_t boff = threadIdx.x * 16u;
+  const V empty = {~0u, ~0u, ~0u, ~0u};
+  for (int64_t cbase = blockIdx.x * chunk; cbase < nvec; cbase += gridDim.x * chunk) {
+    if (cbase + threadIdx.x < nvec) store_coherent(buf + cbase, boff, empty);
+  }
 }
 
 // ---- all-gather share (two-shot) ----------------------------------------------------------------

@@ -219,6 +219,91 @@ class GatherCase(Case):
         torch.cuda.synchronize()
 
 
+class LamportCase(Case):
+    """Lamport-style one-shot exchange on one GPU: per step, W producer pushes into the sentinel-
+    armed receive slots, then the polling consumer (which re-arms the slots).  `mode` "push"
+    times the W pushes alone, "step" pushes + consumer; the consumer's share is the difference.
+    One buffer set (the receive buffer is state), so small shapes are cache-warm."""
+
+    def __init__(self, ar, torch, pattern, W, M, H, dtype="bf16", eps=1e-6):
+        self.ar, self.torch = ar, torch
+        self.pattern, self.W, self.M, self.H, self.dtype, self.eps = pattern, W, M, H, dtype, eps
+        tdt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[dtype]
+        self.esize = 4 if dtype == "fp32" else 2
+        self.bytes = metric_bytes(pattern, W, M, H, self.esize)
+        self.R = 1
+        self.mode = "step"
+        g = torch.Generator(device="cuda")
+        g.manual_seed(99)
+        self.parts = [torch.empty((M, H), dtype=torch.float32, device="cuda")
+                      .normal_(0.0, 0.05, generator=g).to(tdt) for _ in range(W)]
+        self.rbuf = torch.empty((W, M, H), dtype=tdt, device="cuda")
+        self.status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        self.dt = ar.dtype_code(tdt)
+        L = ar.lib()
+        self.L = L
+        self.push_args = [(p.data_ptr(), r, self.rbuf.data_ptr(), W, M, H, self.dt)
+                          for r, p in enumerate(self.parts)]
+        if pattern == "rms":
+            self.res = torch.empty((M, H), dtype=torch.float32, device="cuda").normal_(
+                generator=g).to(tdt)
+            self.gamma = torch.empty(H, dtype=torch.float32, device="cuda").uniform_(
+                0.8, 1.2, generator=g)
+            self.ro, self.no = torch.empty_like(self.res), torch.empty_like(self.res)
+            self.consume = lambda h: L.ar_lamport_residual_rmsnorm(
+                self.rbuf.data_ptr(), W, M, H, self.dt, self.res.data_ptr(),
+                self.gamma.data_ptr(), ctypes.c_float(eps), self.ro.data_ptr(),
+                self.no.data_ptr(), self.status.data_ptr(), 0, ctypes.c_void_p(h))
+        else:
+            self.out = torch.empty((M, H), dtype=tdt, device="cuda")
+            self.consume = lambda h: L.ar_lamport_sum(
+                self.rbuf.data_ptr(), W, M, H, self.dt, self.out.data_ptr(),
+                self.status.data_ptr(), 0, ctypes.c_void_p(h))
+        st = L.ar_lamport_arm(self.rbuf.data_ptr(), W, M, H, self.dt,
+                              ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if st != 0:
+            raise RuntimeError("ar_lamport_arm failed: %s" % ar.status_string(st))
+        torch.cuda.synchronize()
+
+    def call(self, i: int, stream_handle: int) -> None:
+        h = ctypes.c_void_p(stream_handle)
+        for a in self.push_args:
+            st = self.L.ar_lamport_push(*a, h)
+            if st != 0:
+                raise RuntimeError("ar_lamport_push failed: %s" % self.ar.status_string(st))
+        if self.mode == "step":
+            st = self.consume(stream_handle)
+            if st != 0:
+                raise RuntimeError("Lamport consumer failed: %s" % self.ar.status_string(st))
+
+
+def lamport_lines(ar, torch, W=8, H=7168, Ms=(128, 2048)) -> list:
+    """hipGraph-replayed µs of the Lamport exchange steps (pushes + consumer, pushes alone)."""
+    lines = []
+    for m in Ms:
+        for pattern in ("rms", "sum"):
+            c = LamportCase(ar, torch, pattern, W, m, H)
+            calls = 20 if m >= 1024 else 100
+            c.mode = "step"
+            us_step = c.time_graph(calls)
+            c.mode = "push"
+            us_push = c.time_graph(calls)
+            c.mode = "step"
+            us_step = min(us_step, c.time_graph(calls))
+            torch.cuda.synchronize()
+            status = int(c.status.item())
+            us_cons = us_step - us_push
+            lines.append({"pattern": "kARResidualRMSNorm" if pattern == "rms" else "kAllReduce",
+                          "W": W, "M": m, "H": H, "us_pushes": round(us_push, 3),
+                          "us_step": round(us_step, 3), "us_consumer": round(us_cons, 3),
+                          "consumer_GBs_metric": round(c.bytes / (us_cons * 1e-6) / 1e9, 1),
+                          "status": status})
+            print("# lamport %s" % json.dumps(lines[-1]), file=sys.stderr, flush=True)
+            del c
+            torch.cuda.empty_cache()
+    return lines
+
+
 def two_shot_lines(ar, torch, W=8, H=7168, Ms=(128, 512, 2048)) -> list:
     """One GPU's two-shot share: reduce-scatter of rank 0's row slice with the fused kernels,
     then the all-gather of each output (hipGraph replay, rotated buffers)."""
@@ -628,6 +713,7 @@ def main():
         result["sweep"] = sweep
         result["two_shot_share"] = two_shot_lines(ar, torch)
         result["configs"] = config_lines(ar, torch)
+        result["lamport_exchange"] = lamport_lines(ar, torch)
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline()
