@@ -187,8 +187,9 @@ int ar_all_gather(const void* const* slices, int W, int64_t M, int64_t H, int dt
  * ar_sum / ar_residual_rmsnorm, and write all ones back, leaving the buffer empty for the next
  * round.  A partial element that is itself all ones is delivered with its lowest bit cleared (a
  * NaN either way).  Producers and the consumer may run concurrently (on other streams, or, with
- * peer-mapped memory, other GPUs): words move as 64-bit relaxed atomics at agent scope.
- * Every wait is bounded: after `spin_limit` polls of one 8-byte word (0 = 65536) the consumer
+ * peer-mapped memory, other GPUs): slots move as 16-byte device-coherent accesses (each aligned
+ * dword single-copy atomic; elements are tested one by one).
+ * Every wait is bounded: after `spin_limit` polls of one 16-byte vector (0 = 65536) the consumer
  * gives up on it, sets bit 0 of *status (a device int the caller clears) and carries on; the
  * outputs are then meaningless and the buffer is not left empty.  H must be a multiple of
  * 16 / sizeof(T); the fused consumer takes rows of at most 2048 16-byte vectors. */
