@@ -485,13 +485,14 @@ int run_gather(const void* const* slices, int W, int64_t M, int64_t H, int dtype
   // covering every vector once; smaller ones as 256-thread blocks, at most 16 per CU over all
   // slices.  Non-temporal stores won at every size.
   const bool large = M * V >= int64_t(cu) * 4096;
+  // (Two or four vectors per thread measured 3-7 % slower at every size.)
   const int threads = large ? 64 : 256;
   const int64_t cap = large ? int64_t(INT_MAX) : std::max<int64_t>(1, int64_t(cu) * 16 / W);
   const int gx = static_cast<int>(std::min(ceil_div(max_vecs, threads), cap));
   hipStream_t s = static_cast<hipStream_t>(stream);
   u32x4* dst = static_cast<u32x4*>(out);
   void* args[] = {&a, &dst, &skip};
-  const void* fn = reinterpret_cast<const void*>(&arf::ar_gather_kernel<true>);
+  const void* fn = reinterpret_cast<const void*>(&arf::ar_gather_kernel<true, 1>);
   const hipError_t e = hipLaunchKernel(fn, dim3(std::max(gx, 1), W), dim3(threads), args, 0, s);
   return e == hipSuccess ? AR_OK : AR_ERR_LAUNCH;
 }

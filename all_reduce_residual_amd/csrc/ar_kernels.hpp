@@ -865,9 +865,11 @@ struct GatherArgs {
   int64_t vec_begin[65];    // first vector of slice j in `out`; vec_begin[W] = M * V
 };
 
-// out[vec_begin[j] + i] = src[j][i].  blockIdx.y = slice; blocks of a slice walk its vectors
-// with a grid stride over blockIdx.x; slices whose bit is set in `skip` are already in place.
-template <bool kNtStore>
+// out[vec_begin[j] + i] = src[j][i].  blockIdx.y = slice; the blocks of a slice take chunks of
+// blockDim.x * U vectors (lane t owns t + u * blockDim.x, all U loads issued before the stores),
+// loop-free when the grid covers the largest slice, else with a grid stride.  Slices whose bit
+// is set in `skip` are already in place.
+template <bool kNtStore, int U>
 __global__ __launch_bounds__(kMaxThreads) void ar_gather_kernel(GatherArgs a, u32x4* out,
                                                                 uint64_t skip) {
   const int j = blockIdx.y;
@@ -876,13 +878,29 @@ __global__ __launch_bounds__(kMaxThreads) void ar_gather_kernel(GatherArgs a, u3
   const int64_t n = a.vec_begin[j + 1] - begin;
   const u32x4* src = a.src[j];
   u32x4* dst = out + begin;
-  const int64_t chunk = blockDim.x;
-  for (int64_t cbase = blockIdx.x * chunk; cbase < n; cbase += gridDim.x * chunk) {
-    const uint32_t i = threadIdx.x;
-    if (cbase + i < n) {
-      const uint32_t boff = i * 16u;
-      store_vec<kNtStore>(at(dst + cbase, boff), load_stream(at(src + cbase, boff)));
+  const int64_t chunk = static_cast<int64_t>(blockDim.x) * U;
+  auto one = [&](int64_t cbase) {
+    if (cbase + chunk <= n) {
+      u32x4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        v[u] = load_stream(at(src + cbase, (threadIdx.x + u * blockDim.x) * 16u));
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        store_vec<kNtStore>(at(dst + cbase, (threadIdx.x + u * blockDim.x) * 16u), v[u]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t i = threadIdx.x + u * blockDim.x;
+        if (cbase + i < n) store_vec<kNtStore>(at(dst + cbase, i * 16u), load_stream(at(src + cbase, i * 16u)));
+      }
     }
+  };
+  if (static_cast<int64_t>(gridDim.x) * chunk >= n) {
+    const int64_t cbase = blockIdx.x * chunk;
+    if (cbase < n) one(cbase);
+  } else {
+    for (int64_t cbase = blockIdx.x * chunk; cbase < n; cbase += gridDim.x * chunk) one(cbase);
   }
 }
 
