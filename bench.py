@@ -20,6 +20,10 @@ Modes:
   --summarize-stats DIR  markdown summary of a rocprofv3 --kernel-trace --stats output dir
   --summarize-pmc DIR... markdown summary of rocprofv3 --pmc output dirs (FETCH_SIZE run, then
                          WRITE_SIZE run) scaled by the copy calibration
+  --summarize-sweep-trace DIR BENCH_JSON
+                         per-M median in-kernel duration of the wide-hidden sweep kernels from a
+                         rocprofv3 --kernel-trace dir, beside the per-call graph times of a
+                         bench JSON line
 """
 from __future__ import annotations
 
@@ -474,6 +478,44 @@ def _read_csvs(d: str, pattern: str):
     return rows
 
 
+def summarize_sweep_trace(d: str, bench_json: str) -> str:
+    """In-kernel time (median kernel-trace duration) against the per-call hipGraph time for the
+    wide-hidden sweep (W = 8, H = 7168 bf16): the difference is launch gap and ramp, not kernel."""
+    rows = _read_csvs(d, "*kernel_trace.csv")
+    if not rows:
+        raise SystemExit("no kernel_trace.csv under %s" % d)
+    with open(bench_json) as f:
+        line = json.loads(f.read().strip().splitlines()[-1])
+    per_call = {(e["pattern"], e["M"]): e for e in line.get("sweep", [])}
+    W, H = HEADLINE["W"], HEADLINE["H"]
+    V = H // 8
+    durs = {}
+    for r in rows:
+        name = r["Kernel_Name"]
+        wg, grid = int(r["Workgroup_Size_X"]), int(r["Grid_Size_X"])
+        m = re.search(r"ar_(norm|sum)_kernel<arf::Bf16, (\d+), (\d+), \w+, arf::StreamSource", name)
+        if not m or int(m.group(2)) != W:
+            continue
+        if m.group(1) == "norm":
+            pattern, M = "kARResidualRMSNorm", grid // wg          # one row per block
+        else:
+            pattern, M = "kAllReduce", grid * int(m.group(3)) // V  # U vectors per thread
+        durs.setdefault((pattern, M), []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    out = ["| pattern | M | metric bytes | dispatches | in-kernel µs (median) | in-kernel % of 8 TB/s |"
+           " per-call µs (graph) | per-call % of 8 TB/s |", "|---|---|---|---|---|---|---|---|"]
+    for key in sorted(durs, key=lambda k: (k[0], k[1])):
+        if key not in per_call:
+            continue
+        e = per_call[key]
+        ds = sorted(durs[key])
+        med = ds[len(ds) // 2]
+        out.append("| %s | %d | %d | %d | %.2f | %.1f | %.2f | %.1f |" % (
+            key[0], key[1], e["bytes"], len(ds), med, 100 * e["bytes"] / (med * 1e3) / HBM_PEAK_GBS,
+            e["us_graph"], 100 * e["bytes"] / (e["us_graph"] * 1e3) / HBM_PEAK_GBS))
+    return "\n".join(out)
+
+
 def summarize_stats(d: str) -> str:
     rows = _read_csvs(d, "*kernel_stats.csv")
     if not rows:
@@ -574,8 +616,12 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--summarize-stats", metavar="DIR")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-sweep-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_JSON"))
     args = ap.parse_args()
 
+    if args.summarize_sweep_trace:
+        print(summarize_sweep_trace(*args.summarize_sweep_trace))
+        return 0
     if args.summarize_stats:
         print(summarize_stats(args.summarize_stats))
         return 0
