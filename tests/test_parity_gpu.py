@@ -232,3 +232,30 @@ def test_fp16_outliers_cancel(oracle_mod):
     wl = synth.WORKLOADS["fp16_many_rank"]
     parts = [synth.partial(wl, r, 6) for r in range(wl.W)]
     run_sum_both(oracle_mod, parts, "fp16")
+
+
+# ---- launch shapes the planner picks for one or two partials at large M -------------------------
+
+@pytest.mark.parametrize("W,M,H", [(2, 2048, 4096), (2, 1024, 8192), (1, 2048, 7168), (1, 600, 4096),
+                                   (2, 600, 4096)])
+def test_small_world_planned_shapes(oracle_mod, W, M, H):
+    """More rows than CUs with W <= 2: the planner shrinks the row block (down to one wave with
+    8 vectors per thread); the result is the oracle's."""
+    cfg = ar.ar_launch_config(ar.PATTERN_AR_RESIDUAL_RMSNORM, W, M, H, ar.DTYPE_BF16)
+    print("case", W, M, H, cfg, flush=True)
+    parts, res, gam = synth.custom(W, M, H, "bf16", seed=W * 100 + M + H)
+    run_rms_both(oracle_mod, parts, res, gam, 1e-6, "bf16")
+
+
+@pytest.mark.parametrize("W,vpt", [(1, 4), (1, 8), (2, 4), (2, 8), (4, 4), (4, 8), (8, 4)])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_norm_vectors_per_thread_branches(oracle_mod, W, vpt, dtype):
+    """4 and 8 vectors per thread take the batched-chains branch when (W + 1) x vpt <= 20 and
+    the one-vector-at-a-time branch otherwise; both match the oracle, with ragged rows."""
+    M, H = 37, 4096 - 8 if dtype != "fp32" else 4096 - 4
+    V = H // (8 if dtype != "fp32" else 4)
+    lanes = -(-(-(-V // vpt)) // 64) * 64
+    cfg = dict(threads_per_block=lanes, vecs_per_thread=vpt, lanes_per_row=lanes,
+               rows_per_block=1, grid=M, flat=0, nt_store=1)
+    parts, res, gam = synth.custom(W, M, H, dtype, seed=W * 10 + vpt)
+    run_rms_both(oracle_mod, parts, res, gam, 1e-6, dtype, config=cfg)
