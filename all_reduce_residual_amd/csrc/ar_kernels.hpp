@@ -214,7 +214,19 @@ __device__ inline void batch_fence(float (&acc)[N][K]) {
 
 // acc[k] += x_R0[k] + x_{R0+1}[k] + ... + x_{W-1}[k] (in that order) for the N vectors at
 // element offset `base` (uniform) + byte offset boff[k] (per lane) of every partial.
-template <class T, int W, int N, int R0 = 0, int kMaxLoads = (N * T::kVec >= 32 ? 8 : 16)>
+//
+// kStage: every batch's loads are issued, then made visible to the arithmetic all at once
+// through an empty asm per loaded vector (memory clobber: no load moves past them), then added.
+// Without it the scheduler may, to reach its occupancy target, issue one load and wait for it
+// before the next (seen at W = 8 with 4-8 vectors per thread: 2x slower); with it the batch
+// costs more registers, which the fused kernel's 2-vector rows measured slower for.
+template <class T, int N>
+constexpr int default_max_loads() {
+  return N * T::kVec >= 32 ? 8 : 16;
+}
+
+template <class T, int W, int N, int R0 = 0, int kMaxLoads = default_max_loads<T, N>(),
+          bool kStage = false>
 __device__ inline void rank_sum_range(const RankPtrs<W>& in, int64_t base,
                                       const uint32_t (&boff)[N], float (&acc)[N][T::kVec]) {
   constexpr int kBatch = rank_batch<W - R0 < 1 ? 1 : W - R0, N, kMaxLoads>();
@@ -256,15 +268,40 @@ __device__ inline void rank_sum_range(const RankPtrs<W>& in, int64_t base,
   }
 #pragma unroll
   for (int r0 = R0; r0 < W; r0 += kBatch) {
+    if constexpr (kStage) {
+      u32x4 raw[kBatch][N];
 #pragma unroll
-    for (int r = r0; r < r0 + kBatch && r < W; ++r) {
-      const u32x4* src = in.p[r] + base;
+      for (int r = r0; r < r0 + kBatch && r < W; ++r) {
+        const u32x4* src = in.p[r] + base;
 #pragma unroll
-      for (int k = 0; k < N; ++k) {
-        float x[T::kVec];
-        T::widen(load_stream(at(src, boff[k])), x);
+        for (int k = 0; k < N; ++k) raw[r - r0][k] = load_stream(at(src, boff[k]));
+      }
 #pragma unroll
-        for (int e = 0; e < T::kVec; ++e) acc[k][e] = acc[k][e] + x[e];
+      for (int r = r0; r < r0 + kBatch && r < W; ++r) {
+#pragma unroll
+        for (int k = 0; k < N; ++k) asm volatile("" : "+v"(raw[r - r0][k]) : : "memory");
+      }
+#pragma unroll
+      for (int r = r0; r < r0 + kBatch && r < W; ++r) {
+#pragma unroll
+        for (int k = 0; k < N; ++k) {
+          float x[T::kVec];
+          T::widen(raw[r - r0][k], x);
+#pragma unroll
+          for (int e = 0; e < T::kVec; ++e) acc[k][e] = acc[k][e] + x[e];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int r = r0; r < r0 + kBatch && r < W; ++r) {
+        const u32x4* src = in.p[r] + base;
+#pragma unroll
+        for (int k = 0; k < N; ++k) {
+          float x[T::kVec];
+          T::widen(load_stream(at(src, boff[k])), x);
+#pragma unroll
+          for (int e = 0; e < T::kVec; ++e) acc[k][e] = acc[k][e] + x[e];
+        }
       }
     }
     if (r0 + kBatch < W) batch_fence(acc);
@@ -272,7 +309,7 @@ __device__ inline void rank_sum_range(const RankPtrs<W>& in, int64_t base,
 }
 
 // acc[k] = -0 + x_0[k] + x_1[k] + ... + x_{W-1}[k].
-template <class T, int W, int N, int kMaxLoads = (N * T::kVec >= 32 ? 8 : 16)>
+template <class T, int W, int N, int kMaxLoads = default_max_loads<T, N>(), bool kStage = false>
 __device__ inline void rank_sum(const RankPtrs<W>& in, int64_t base, const uint32_t (&boff)[N],
                                 float (&acc)[N][T::kVec]) {
 #pragma unroll
@@ -280,7 +317,7 @@ __device__ inline void rank_sum(const RankPtrs<W>& in, int64_t base, const uint3
 #pragma unroll
     for (int e = 0; e < T::kVec; ++e) acc[k][e] = -0.0f;
   }
-  rank_sum_range<T, W, N, 0, kMaxLoads>(in, base, boff, acc);
+  rank_sum_range<T, W, N, 0, kMaxLoads, kStage>(in, base, boff, acc);
 }
 
 // ---- input sources ------------------------------------------------------------------------------
@@ -292,11 +329,11 @@ __device__ inline void rank_sum(const RankPtrs<W>& in, int64_t base, const uint3
 // `ok[k]` says whether vector slot k is a real one; slots that are not re-read a valid vector
 // (their offsets are clamped) and their result is discarded.
 struct StreamSource {
-  template <class T, int W, int N, int kMaxLoads = (N * T::kVec >= 32 ? 8 : 16)>
+  template <class T, int W, int N, int kMaxLoads = default_max_loads<T, N>(), bool kStage = false>
   __device__ inline void sum(const RankPtrs<W>& in, int64_t base, const uint32_t (&boff)[N],
                              const bool (&ok)[N], float (&acc)[N][T::kVec]) const {
     (void)ok;
-    rank_sum<T, W, N, kMaxLoads>(in, base, boff, acc);
+    rank_sum<T, W, N, kMaxLoads, kStage>(in, base, boff, acc);
   }
   // Terms after the W partials for the element-wise tail of the flat sum: none.
   template <class T>
@@ -320,7 +357,7 @@ __device__ inline void sum_chunk(const RankPtrs<W>& in, u32x4* out, int64_t nvec
       boff[u] = (threadIdx.x + u * blockDim.x) * 16u;
       ok[u] = true;
     }
-    src.template sum<T, W, U>(in, cbase, boff, ok, acc);
+    src.template sum<T, W, U, default_max_loads<T, U>(), (U >= 2)>(in, cbase, boff, ok, acc);
 #pragma unroll
     for (int u = 0; u < U; ++u) store_vec<kNtStore>(at(out + cbase, boff[u]), T::narrow(acc[u]));
   } else {
@@ -334,7 +371,7 @@ __device__ inline void sum_chunk(const RankPtrs<W>& in, u32x4* out, int64_t nvec
       boff[u] = (i < last ? i : last) * 16u;
       ok[u] = i <= last;
     }
-    src.template sum<T, W, U>(in, cbase, boff, ok, acc);
+    src.template sum<T, W, U, default_max_loads<T, U>(), (U >= 2)>(in, cbase, boff, ok, acc);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (ok[u]) store_vec<kNtStore>(at(out + cbase, boff[u]), T::narrow(acc[u]));
@@ -386,11 +423,11 @@ __device__ inline void accumulate(float (&acc)[T::kVec], u32x4 v) {
 // kernel: the first kernel of the two-kernel (unfused) path, which accepts rows of any width.
 struct ResidualSource {
   const u32x4* residual;
-  template <class T, int W, int N, int kMaxLoads = (N * T::kVec >= 32 ? 8 : 16)>
+  template <class T, int W, int N, int kMaxLoads = default_max_loads<T, N>(), bool kStage = false>
   __device__ inline void sum(const RankPtrs<W>& in, int64_t base, const uint32_t (&boff)[N],
                              const bool (&ok)[N], float (&acc)[N][T::kVec]) const {
     (void)ok;
-    rank_sum<T, W, N, kMaxLoads>(in, base, boff, acc);
+    rank_sum<T, W, N, kMaxLoads, kStage>(in, base, boff, acc);
 #pragma unroll
     for (int k = 0; k < N; ++k) accumulate<T>(acc[k], load_stream(at(residual + base, boff[k])));
   }
@@ -487,15 +524,34 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_kernel(
         rounded[k] = T::narrow(acc[k]);
       }
     } else {
-      // One vector's chain at a time keeps the live accumulators to one vector.
+      // G vectors' chains at a time (G the largest power of two with (W + 1) G <= 20, at least
+      // one) keep the live accumulators and loads in registers; a fence after each group stops
+      // the next group's loads from being hoisted over it.  (One vector at a time cost a round
+      // trip per vector: W = 8 with 8 vectors per thread ran 6x slower at small M.)
+      constexpr int G = (W + 1) * 4 <= 20 ? 4 : (W + 1) * 2 <= 20 ? 2 : 1;
+      // Loads per staged batch: 16 x G (all W ranks at once up to W = 16); 8 with 8 vectors
+      // per thread (the 32 registers of rounded values leave no room for more: it spilled);
+      // 8 for the grouped walk of W >= 32 (its groups of 16 ranks need a batch dividing 16).
+      constexpr int kLoads = (W >= 32 || VPT >= 8) ? 8 : 16 * G;
 #pragma unroll
-      for (int k = 0; k < VPT; ++k) {
-        const uint32_t boff_k[1] = {boff[k]};
-        const bool ok_k[1] = {ok[k]};
-        float acc[1][kVec];
-        src.template sum<T, W, 1, 8>(in, base, boff_k, ok_k, acc);
-        accumulate<T>(acc[0], load_stream(at(residual + base, boff[k])));
-        rounded[k] = T::narrow(acc[0]);
+      for (int k0 = 0; k0 < VPT; k0 += G) {
+        uint32_t boff_g[G];
+        bool ok_g[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          boff_g[g] = boff[k0 + g];
+          ok_g[g] = ok[k0 + g];
+        }
+        float acc[G][kVec];
+        // Staged only for groups of several vectors: that is where the scheduler otherwise
+        // issues the loads one round trip apart (W = 8: 2x); single-vector chains (W >= 16)
+        // measured faster unstaged.
+        src.template sum<T, W, G, kLoads, (G >= 2)>(in, base, boff_g, ok_g, acc);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          accumulate<T>(acc[g], load_stream(at(residual + base, boff_g[g])));
+          rounded[k0 + g] = T::narrow(acc[g]);
+        }
         batch_fence(acc);
       }
     }
@@ -767,7 +823,8 @@ struct LamportSource {
   // in rank order and re-armed with the sentinel.  Slots that are not real (ok[k] false) neither
   // read nor re-arm anything: their clamped offset points at another lane's vector, which they
   // must not empty.
-  template <class T, int W, int N, int kMaxLoads = (N * T::kVec >= 32 ? 8 : 16)>
+  // (kStage is accepted for the common interface; the polled batch is staged already.)
+  template <class T, int W, int N, int kMaxLoads = default_max_loads<T, N>(), bool kStage = false>
   __device__ inline void sum(const RankPtrs<W>& in, int64_t base, const uint32_t (&boff)[N],
                              const bool (&ok)[N], float (&acc)[N][T::kVec]) const {
     // Polled vectors stay live until accumulated: half the stream source's batch.
