@@ -247,11 +247,13 @@ def test_small_world_planned_shapes(oracle_mod, W, M, H):
     run_rms_both(oracle_mod, parts, res, gam, 1e-6, "bf16")
 
 
-@pytest.mark.parametrize("W,vpt", [(1, 4), (1, 8), (2, 4), (2, 8), (4, 4), (4, 8), (8, 4)])
-@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("W", [1, 2, 4, 8, 16, 32, 64])
+@pytest.mark.parametrize("vpt", [4, 8])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
 def test_norm_vectors_per_thread_branches(oracle_mod, W, vpt, dtype):
-    """4 and 8 vectors per thread take the batched-chains branch when (W + 1) x vpt <= 20 and
-    the one-vector-at-a-time branch otherwise; both match the oracle, with ragged rows."""
+    """4 and 8 vectors per thread take the all-chains branch when (W + 1) x vpt <= 20 and the
+    grouped branch otherwise (groups of 4, 2 or 1 vectors, staged for groups of 2 or more,
+    the 16-rank walk at W >= 32); every branch matches the oracle, with ragged rows."""
     M, H = 37, 4096 - 8 if dtype != "fp32" else 4096 - 4
     V = H // (8 if dtype != "fp32" else 4)
     lanes = -(-(-(-V // vpt)) // 64) * 64
