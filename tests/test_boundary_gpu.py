@@ -207,6 +207,72 @@ def test_graph_replay_matches_eager(oracle_mod):
         assert torch.equal(dr.cpu().view(torch.int16), r2.view(torch.int16))
 
 
+def test_graph_replay_of_exchange_gather_and_fallback(oracle_mod):
+    """The Lamport exchange (W pushes + the polling consumer, which re-arms the slots), the
+    all-gather of a two-shot round and the two-kernel path, each captured once and replayed with
+    new inputs and eager work in between: every replay equals the oracle, and the exchange's
+    status word stays clear (each replay finds its slots re-armed by the previous one)."""
+    W, M, H, dtype = 8, 24, 7168, "bf16"
+    parts, res, gam, dp, dr, dg = _inputs(W, M, H, dtype, 21)
+    rbuf = torch.empty((W, M, H), dtype=torch.bfloat16, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ar.ar_lamport_arm(rbuf)
+    lro, lno = torch.empty_like(dr), torch.empty_like(dr)
+    # Two-shot gather of the rank slices of `gsrc` into `gout`.
+    gsrc = torch.empty_like(dr)
+    gout = torch.empty_like(dr)
+    slices = []
+    for j in range(W):
+        b, c = ar.ar_row_partition(W, M, j)
+        slices.append(gsrc[b:b + c])
+    # Two-kernel path on an odd width.
+    Hu = 7170
+    up, ur, ug = synth.custom(4, M, Hu, dtype, seed=22)
+    dup, dur, dug = [dev(p) for p in up], dev(ur), dev(ug)
+    uro, uno = torch.empty_like(dur), torch.empty_like(dur)
+
+    def calls():
+        for r in range(W):
+            ar.ar_lamport_push(dp[r], r, rbuf)
+        ar.ar_lamport_residual_rmsnorm(rbuf, dr, dg, 1e-6, lro, lno, status)
+        ar.ar_all_gather(slices, gout)
+        ar.ar_residual_rmsnorm_unfused(dup, dur, dug, 1e-6, uro, uno)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        calls()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    for rep in range(3):
+        p2, r2, _ = synth.custom(W, M, H, dtype, seed=200 + rep)
+        for d, h in zip(dp + [dr], p2 + [r2]):
+            d.copy_(h)
+        g2 = synth.custom(1, M, H, dtype, seed=300 + rep)[0][0]
+        gsrc.copy_(g2)
+        u2, ur2, _ = synth.custom(4, M, Hu, dtype, seed=400 + rep)
+        for d, h in zip(dup + [dur], u2 + [ur2]):
+            d.copy_(h)
+        ar.ar_sum(dp[:2], torch.empty_like(dr))          # unrelated eager work
+        graph.replay()
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0, "replay %d: a poll timed out" % rep
+        want_ro, want_no = oracle_mod.ar_residual_rmsnorm(
+            [host_np(p) for p in p2], host_np(r2), gam.numpy(), 1e-6, dtype)
+        assert_bit_exact(host_np(lro.cpu()), want_ro, dtype, "replay %d lamport residual_out" % rep)
+        assert_norm_close(host_np(lno.cpu()), want_no, dtype, "replay %d lamport norm_out" % rep)
+        assert_bit_exact(host_np(gout.cpu()), host_np(g2), dtype, "replay %d gather" % rep)
+        want_ro, want_no = oracle_mod.ar_residual_rmsnorm(
+            [host_np(p) for p in u2], host_np(ur2), ug.numpy(), 1e-6, dtype)
+        assert_bit_exact(host_np(uro.cpu()), want_ro, dtype, "replay %d unfused residual_out" % rep)
+        assert_norm_close(host_np(uno.cpu()), want_no, dtype, "replay %d unfused norm_out" % rep)
+    # Every slot is armed again after the last replay.
+    assert bool((rbuf.view(torch.int16) == -1).all())
+
+
 def test_device_facts():
     cu = ar.ar_device_cu_count()
     print("compute units:", cu, torch.cuda.get_device_name(0))
