@@ -198,16 +198,40 @@ inline hipError_t launch_lamport_norm_t(void* rbuf, int W, const void* residual,
                                         const ar_launch_cfg_t& c, arf::LamportSource src,
                                         hipStream_t s) {
   const int64_t nvec = M * H / T::kVec;
-  if (c.vecs_per_thread == 1) {
-#define AR_CALL(w) \
-  launch_lamport_norm_v<T, w, 1>(rbuf, nvec, residual, gamma, eps, residual_out, norm_out, M, H, c, src, s)
-    AR_W_SWITCH(W, AR_CALL)
-#undef AR_CALL
+#define AR_CALL_V(v)                                                                       \
+  if (c.vecs_per_thread == v) {                                                            \
+    switch (W) {                                                                           \
+      case 1: return launch_lamport_norm_v<T, 1, v>(rbuf, nvec, residual, gamma, eps,      \
+                                                    residual_out, norm_out, M, H, c, src, s); \
+      case 2: return launch_lamport_norm_v<T, 2, v>(rbuf, nvec, residual, gamma, eps,      \
+                                                    residual_out, norm_out, M, H, c, src, s); \
+      case 4: return launch_lamport_norm_v<T, 4, v>(rbuf, nvec, residual, gamma, eps,      \
+                                                    residual_out, norm_out, M, H, c, src, s); \
+      case 8: return launch_lamport_norm_v<T, 8, v>(rbuf, nvec, residual, gamma, eps,      \
+                                                    residual_out, norm_out, M, H, c, src, s); \
+      case 16: return launch_lamport_norm_v<T, 16, v>(rbuf, nvec, residual, gamma, eps,    \
+                                                      residual_out, norm_out, M, H, c, src, s); \
+      case 32: return launch_lamport_norm_v<T, 32, v>(rbuf, nvec, residual, gamma, eps,    \
+                                                      residual_out, norm_out, M, H, c, src, s); \
+      default: return launch_lamport_norm_v<T, 64, v>(rbuf, nvec, residual, gamma, eps,    \
+                                                      residual_out, norm_out, M, H, c, src, s); \
+    }                                                                                      \
   }
-#define AR_CALL(w) \
-  launch_lamport_norm_v<T, w, 2>(rbuf, nvec, residual, gamma, eps, residual_out, norm_out, M, H, c, src, s)
-  AR_W_SWITCH(W, AR_CALL)
-#undef AR_CALL
+  AR_CALL_V(1)
+  AR_CALL_V(2)
+  AR_CALL_V(4)
+#undef AR_CALL_V
+  // 8 vectors per thread only for W <= 4 (beyond, the polled batch spills); the host rejects
+  // rows that would need them.
+  switch (W) {
+    case 1: return launch_lamport_norm_v<T, 1, 8>(rbuf, nvec, residual, gamma, eps, residual_out,
+                                                  norm_out, M, H, c, src, s);
+    case 2: return launch_lamport_norm_v<T, 2, 8>(rbuf, nvec, residual, gamma, eps, residual_out,
+                                                  norm_out, M, H, c, src, s);
+    case 4: return launch_lamport_norm_v<T, 4, 8>(rbuf, nvec, residual, gamma, eps, residual_out,
+                                                  norm_out, M, H, c, src, s);
+    default: return hipErrorInvalidConfiguration;
+  }
 }
 
 template <class T>

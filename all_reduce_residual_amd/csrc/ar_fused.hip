@@ -500,8 +500,9 @@ int run_gather(const void* const* slices, int W, int64_t M, int64_t H, int dtype
 // ---- Lamport-style exchange ----------------------------------------------------------------------
 
 constexpr uint32_t kDefaultSpinLimit = 1u << 16;
-// Rows the Lamport fused kernel takes: up to 1024 lanes x 2 vectors.
-constexpr int64_t kLamportMaxRowVecs = 2048;
+// Vectors per thread of the Lamport fused consumer: 8 for W <= 4, 4 beyond (its polled batch
+// spills at 8), so rows of up to 1024 lanes x that many 16-byte vectors.
+int lamport_max_vpt(int W) { return W <= 4 ? 8 : 4; }
 
 int check_lamport_shape(int pattern, int W, int64_t M, int64_t H, int dtype) {
   int st = check_shape(AR_PATTERN_ALLREDUCE, W, M, H, dtype);
@@ -511,7 +512,7 @@ int check_lamport_shape(int pattern, int W, int64_t M, int64_t H, int dtype) {
     return AR_ERR_UNSUPPORTED;
   const int64_t vec = kVecBytes / elem_size(dtype);
   if (H % vec != 0) return AR_ERR_UNSUPPORTED;
-  if (pattern == AR_PATTERN_AR_RESIDUAL_RMSNORM && H / vec > kLamportMaxRowVecs)
+  if (pattern == AR_PATTERN_AR_RESIDUAL_RMSNORM && H / vec > 1024 * lamport_max_vpt(W))
     return AR_ERR_UNSUPPORTED;
   return AR_OK;
 }
@@ -639,10 +640,11 @@ int run_lamport_norm(void* rbuf, int W, int64_t M, int64_t H, int dtype, const v
   if (st != AR_OK) return st;
   ar_launch_cfg_t cfg;
   plan_norm(W, M, H, dtype, cu, &cfg);
-  if (cfg.vecs_per_thread > 2) {  // the Lamport consumer is instantiated for 1 or 2 vectors
+  const int vmax = lamport_max_vpt(W);
+  if (cfg.vecs_per_thread > vmax) {
     const int64_t V = H / (kVecBytes / elem_size(dtype));
-    cfg.vecs_per_thread = 2;
-    cfg.lanes_per_row = static_cast<int>(round_up(ceil_div(V, 2), 64));
+    cfg.vecs_per_thread = vmax;
+    cfg.lanes_per_row = static_cast<int>(round_up(ceil_div(V, vmax), 64));
     cfg.threads_per_block = cfg.lanes_per_row;
     cfg.rows_per_block = 1;
     cfg.grid = cap_grid(M);

@@ -192,7 +192,8 @@ int ar_all_gather(const void* const* slices, int W, int64_t M, int64_t H, int dt
  * Every wait is bounded: after `spin_limit` polls of one 16-byte vector (0 = 65536) the consumer
  * gives up on it, sets bit 0 of *status (a device int the caller clears) and carries on; the
  * outputs are then meaningless and the buffer is not left empty.  H must be a multiple of
- * 16 / sizeof(T); the fused consumer takes rows of at most 2048 16-byte vectors. */
+ * 16 / sizeof(T); the fused consumer takes rows of at most 8192 16-byte vectors for W <= 4
+ * and 4096 for W >= 8 (H <= 65536 / 32768 at 16 bits). */
 
 /* Empties all W slots (every element all ones).  Call once before the first round. */
 int ar_lamport_arm(void* rbuf, int W, int64_t M, int64_t H, int dtype, void* stream);

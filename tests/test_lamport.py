@@ -39,7 +39,10 @@ def test_lamport_validation():
         ar.AR_ERR_ALIAS
     assert L.ar_lamport_residual_rmsnorm(*args, res, gam, 1e-6, ro, no, ro + 16, 0, None) == \
         ar.AR_ERR_ALIAS
-    assert L.ar_lamport_residual_rmsnorm(rbuf, W, M, 32768, BF16, res, gam, 1e-6, ro, no,
+    # Row limits of the fused consumer: 8192 vectors (H = 65536 bf16) for W <= 4, 4096 for W >= 8.
+    assert L.ar_lamport_residual_rmsnorm(rbuf, W, M, 65544, BF16, res, gam, 1e-6, ro, no,
+                                         status, 0, None) == ar.AR_ERR_UNSUPPORTED
+    assert L.ar_lamport_residual_rmsnorm(rbuf, 8, M, 32776, BF16, res, gam, 1e-6, ro, no,
                                          status, 0, None) == ar.AR_ERR_UNSUPPORTED
     assert L.ar_lamport_residual_rmsnorm(*args, None, gam, 1e-6, ro, no, status, 0, None) == \
         ar.AR_ERR_INVALID_ARG

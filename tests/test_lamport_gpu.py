@@ -193,3 +193,28 @@ def test_workloads_through_the_exchange(oracle_mod, name, M):
                                                       gam.numpy(), wl.eps, wl.dtype)
     assert_bit_exact(host_np(ro.cpu()), want_ro, wl.dtype, "residual_out")
     assert_norm_close(host_np(no.cpu()), want_no, wl.dtype)
+
+
+@pytest.mark.parametrize("W,M,H,dtype", [(2, 2048, 4096, "bf16"), (1, 300, 4096, "fp16"),
+                                         (4, 3, 65536, "bf16"), (8, 5, 32768, "bf16"),
+                                         (16, 4, 32768, "fp16"), (64, 2, 16384, "bf16"),
+                                         (2, 6, 16384, "fp32")])
+def test_wide_rows_and_many_rows(oracle_mod, W, M, H, dtype):
+    """The fused consumer with 4 and 8 vectors per thread: rows up to 8192 vectors for W <= 4
+    and 4096 beyond, and the few-partial shapes the planner gives when rows outnumber CUs."""
+    print("case", W, M, H, dtype, flush=True)
+    parts, res, gam = synth.custom(W, M, H, dtype, seed=W + M + H)
+    tdt = synth.TORCH_DTYPES[dtype]
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    rbuf = _new_rbuf(W, M, H, tdt)
+    for r, p in enumerate(parts):
+        ar.ar_lamport_push(dev(p), r, rbuf)
+    d_res = dev(res)
+    ro, no = torch.empty_like(d_res), torch.empty_like(d_res)
+    ar.ar_lamport_residual_rmsnorm(rbuf, d_res, dev(gam), 1e-6, ro, no, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0 and _empty(rbuf)
+    want_ro, want_no = oracle_mod.ar_residual_rmsnorm([host_np(p) for p in parts], host_np(res),
+                                                      gam.numpy(), 1e-6, dtype)
+    assert_bit_exact(host_np(ro.cpu()), want_ro, dtype, "lamport residual_out")
+    assert_norm_close(host_np(no.cpu()), want_no, dtype, "lamport norm_out")
