@@ -16,6 +16,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 SOURCES = ["ar_fused.hip", "inst_bf16.hip", "inst_f16.hip", "inst_f32.hip"]
 LIB = os.path.join(PKG, "libar_fused.so")
+# The benchmark's streaming-bandwidth calibration (include/ar_probe.h), a library of its own.
+PROBE_SOURCES = ["stream_probe.hip"]
+PROBE_LIB = os.path.join(PKG, "libar_probe.so")
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from fusing binary32 adds/multiplies into packed
@@ -33,10 +36,12 @@ def hipcc() -> str:
     return cand if os.path.exists(cand) else "hipcc"
 
 
-def build(extra_flags=(), out: str = LIB, jobs: int = 0) -> str:
-    """Build the library and return its path (always recompiles)."""
+def build(extra_flags=(), out: str = LIB, jobs: int = 0, probe: bool = True) -> str:
+    """Build the library (and, with `probe`, the calibration probe library) and return the
+    library's path (always recompiles)."""
     inc = "-I" + os.path.join(ROOT, "include")
-    jobs = jobs or min(len(SOURCES), os.cpu_count() or 1)
+    sources = SOURCES + (PROBE_SOURCES if probe else [])
+    jobs = jobs or min(len(sources), os.cpu_count() or 1)
     with tempfile.TemporaryDirectory(prefix="ar_build_") as tmpdir:
         def compile_one(src):
             obj = os.path.join(tmpdir, os.path.splitext(src)[0] + ".o")
@@ -44,12 +49,17 @@ def build(extra_flags=(), out: str = LIB, jobs: int = 0) -> str:
                            [inc, "-c", "-o", obj, os.path.join(CSRC, src)], check=True)
             return obj
 
+        def link(objs, target):
+            tmp = target + ".tmp%d" % os.getpid()
+            subprocess.run([hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] +
+                           objs, check=True)
+            os.replace(tmp, target)
+
         with ThreadPoolExecutor(max_workers=jobs) as pool:
-            objs = list(pool.map(compile_one, SOURCES))
-        tmp = out + ".tmp%d" % os.getpid()
-        subprocess.run([hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs,
-                       check=True)
-        os.replace(tmp, out)
+            objs = list(pool.map(compile_one, sources))
+        link(objs[:len(SOURCES)], out)
+        if probe:
+            link(objs[len(SOURCES):], PROBE_LIB)
     return out
 
 

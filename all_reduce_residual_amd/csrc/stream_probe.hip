@@ -1,0 +1,61 @@
+// stream_probe.hip -- the streaming-bandwidth probe declared in ar_probe.h (benchmark
+// calibration only; not linked into the all-reduce library).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ar_probe.h"
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct Streams {
+  const u32x4* p[9];
+};
+
+template <int NR, int NW>
+__global__ __launch_bounds__(1024) void probe_kernel(Streams in, int64_t nvec, u32x4* o0,
+                                                     u32x4* o1) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= nvec) return;
+  u32x4 v[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) v[r] = __builtin_nontemporal_load(in.p[r] + i);
+  u32x4 a = v[0];
+#pragma unroll
+  for (int r = 1; r < NR; ++r) a ^= v[r];
+  __builtin_nontemporal_store(a, o0 + i);
+  if constexpr (NW == 2) __builtin_nontemporal_store(a + 1u, o1 + i);
+}
+
+bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" int ar_probe_stream(const void* const* inputs, int nr, int nw, int64_t nvec, void* out0,
+                               void* out1, int threads, void* stream) {
+  if (!inputs || (nr != 8 && nr != 9) || (nw != 1 && nw != 2) || nvec < 0) return 1;
+  if (threads < 64 || threads > 1024 || threads % 64 != 0) return 1;
+  if (nvec == 0) return 0;
+  Streams s{};
+  for (int r = 0; r < nr; ++r) {
+    if (!aligned16(inputs[r])) return 1;
+    s.p[r] = static_cast<const u32x4*>(inputs[r]);
+  }
+  if (!aligned16(out0) || (nw == 2 && !aligned16(out1))) return 1;
+  const int64_t blocks = (nvec + threads - 1) / threads;
+  if (blocks > INT32_MAX) return 1;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  u32x4* o0 = static_cast<u32x4*>(out0);
+  u32x4* o1 = static_cast<u32x4*>(nw == 2 ? out1 : out0);
+  if (nr == 9 && nw == 2) {
+    probe_kernel<9, 2><<<dim3(static_cast<unsigned>(blocks)), dim3(threads), 0, st>>>(s, nvec, o0, o1);
+  } else if (nr == 8 && nw == 1) {
+    probe_kernel<8, 1><<<dim3(static_cast<unsigned>(blocks)), dim3(threads), 0, st>>>(s, nvec, o0, o1);
+  } else if (nr == 9 && nw == 1) {
+    probe_kernel<9, 1><<<dim3(static_cast<unsigned>(blocks)), dim3(threads), 0, st>>>(s, nvec, o0, o1);
+  } else {
+    probe_kernel<8, 2><<<dim3(static_cast<unsigned>(blocks)), dim3(threads), 0, st>>>(s, nvec, o0, o1);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}

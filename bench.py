@@ -308,6 +308,62 @@ def lamport_lines(ar, torch, W=8, H=7168, Ms=(128, 2048)) -> list:
     return lines
 
 
+class ProbeCase(Case):
+    """The calibration probe (include/ar_probe.h): `nr` read streams and `nw` write streams of
+    M x H bf16 each with no arithmetic that matters, R rotated sets."""
+
+    def __init__(self, torch, L, nr, nw, M, H):
+        self.torch, self.L, self.nr, self.nw = torch, L, nr, nw
+        self.nvec = M * H * 2 // 16
+        self.bytes = (nr + nw) * self.nvec * 16
+        self.R = max(1, min(4096, math.ceil(ROTATE_BYTES / self.bytes)))
+        n32 = self.R * self.nvec * 4
+        self.ins = [torch.empty(n32, dtype=torch.int32, device="cuda").random_()
+                    for _ in range(nr)]
+        self.outs = [torch.empty(n32, dtype=torch.int32, device="cuda") for _ in range(2)]
+        self._keep = []
+        self.args = []
+        for k in range(self.R):
+            off = k * self.nvec * 16
+            arr = (ctypes.c_void_p * nr)(*[t.data_ptr() + off for t in self.ins])
+            self._keep.append(arr)
+            self.args.append((arr, nr, nw, self.nvec, self.outs[0].data_ptr() + off,
+                              self.outs[1].data_ptr() + off, 64))
+        torch.cuda.synchronize()
+
+    def call(self, i: int, stream_handle: int) -> None:
+        if self.L.ar_probe_stream(*self.args[i % self.R], ctypes.c_void_p(stream_handle)) != 0:
+            raise RuntimeError("ar_probe_stream failed")
+
+
+def stream_ceiling(torch, H=None, Ms=(2048, 512)) -> list:
+    """What the memory system delivers for the fused kernel's traffic (9 reads + 2 writes) and
+    the sum's (8 + 1) at the headline sizes, with no arithmetic or row reduction in the way
+    (hipGraph replay, rotated sets): the context for the kernels' fraction of 8 TB/s."""
+    H = H or HEADLINE["H"]
+    path = os.path.join(ROOT, "all_reduce_residual_amd", "libar_probe.so")
+    if not os.path.exists(path):
+        return [{"error": "calibration probe library not built"}]
+    L = ctypes.CDLL(path)
+    L.ar_probe_stream.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                  ctypes.c_void_p]
+    L.ar_probe_stream.restype = ctypes.c_int
+    lines = []
+    for m in Ms:
+        for nr, nw in ((9, 2), (8, 1)):
+            c = ProbeCase(torch, L, nr, nw, m, H)
+            us = c.time_graph(c.calls_per_batch(60))
+            gbs = c.bytes / (us * 1e-6) / 1e9
+            lines.append({"streams": "%dR+%dW" % (nr, nw), "M": m, "H": H, "bytes": c.bytes,
+                          "us_graph": round(us, 3), "GBs": round(gbs, 1),
+                          "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2)})
+            print("# ceiling %s" % json.dumps(lines[-1]), file=sys.stderr, flush=True)
+            del c
+            torch.cuda.empty_cache()
+    return lines
+
+
 def two_shot_lines(ar, torch, W=8, H=7168, Ms=(128, 512, 2048)) -> list:
     """One GPU's two-shot share: reduce-scatter of rank 0's row slice with the fused kernels,
     then the all-gather of each output (hipGraph replay, rotated buffers)."""
@@ -733,6 +789,7 @@ def main():
     calib["d2d_copy_GBs"] = round(2 * 2 ** 30 / (sorted(ts)[2] * 1e-3) / 1e9, 1)
     del src, dst
     torch.cuda.empty_cache()
+    calib["stream_ceiling"] = stream_ceiling(torch)
     result["calibration"] = calib
 
     if not args.no_sweep:

@@ -204,3 +204,27 @@ def test_unfused_and_rmsnorm_validation(L):
     assert L.ar_rmsnorm(x, 4, 7, BF16, y + 16, 1e-6, y, None) == ar.AR_ERR_ALIAS
     assert L.ar_rmsnorm(x, 1 << 40, 1 << 30, BF16, g, 1e-6, y, None) == ar.AR_ERR_UNSUPPORTED
     assert L.ar_rmsnorm(None, 0, 7, BF16, None, 1e-6, None, None) == ar.AR_OK
+
+
+def test_probe_library_exports_and_rejects():
+    """The benchmark's calibration probe (include/ar_probe.h) is a library of its own; it exports
+    its one function and rejects malformed calls before any device access."""
+    import os
+    import re
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    path = os.path.join(root, "all_reduce_residual_amd", "libar_probe.so")
+    with open(os.path.join(root, "include", "ar_probe.h")) as f:
+        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+    assert re.findall(r"^\s*int\s+(ar_\w+)\s*\(", text, flags=re.M) == ["ar_probe_stream"]
+    P = ctypes.CDLL(path)
+    fn = P.ar_probe_stream
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p,
+                   ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    p = _ptrs([0x10000 * (i + 1) for i in range(9)])
+    assert fn(p, 7, 1, 64, 0x900000, 0xA00000, 64, None) == 1      # stream count
+    assert fn(p, 9, 3, 64, 0x900000, 0xA00000, 64, None) == 1
+    assert fn(p, 9, 2, 64, 0x900000, 0xA00000, 100, None) == 1     # threads
+    assert fn(p, 9, 2, 64, 0x900008, 0xA00000, 64, None) == 1      # misaligned output
+    assert fn(None, 9, 2, 64, 0x900000, 0xA00000, 64, None) == 1
+    assert fn(p, 9, 2, 0, 0x900000, 0xA00000, 64, None) == 0       # nothing to do
