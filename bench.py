@@ -578,7 +578,7 @@ def summarize_stats(d: str) -> str:
         raise SystemExit("no kernel_stats.csv under %s" % d)
     out = ["| kernel | calls | avg µs | min µs | max µs | share % |", "|---|---|---|---|---|---|"]
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
-        name = r["Name"]
+        name = r["Name"].replace("(anonymous namespace)::", "")
         short = re.sub(r"\(.*", "", name)[:90]
         out.append("| `%s` | %s | %.2f | %.2f | %.2f | %.1f |" % (
             short, r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
