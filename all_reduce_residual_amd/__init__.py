@@ -12,6 +12,8 @@ Operations (fusion patterns kAllReduce and kARResidualRMSNorm):
   ar_residual_rmsnorm(inputs, residual, gamma, eps, residual_out, norm_out)
                                          residual_out = sum + residual
                                          norm_out = RMSNorm(residual_out) * gamma
+  ar_residual_rmsnorm_ws(..., workspace) the same; few-row calls split each row over
+                                         several blocks (caller-owned workspace)
 """
 from __future__ import annotations
 
@@ -67,6 +69,21 @@ class LaunchConfig(ctypes.Structure):
         return cls(**{name: int(d.get(name, 0)) for name, _ in cls._fields_})
 
 
+class SplitConfig(ctypes.Structure):
+    _fields_ = [("threads_per_block", ctypes.c_int32), ("vecs_per_thread", ctypes.c_int32),
+                ("segments", ctypes.c_int32), ("max_polls", ctypes.c_uint32)]
+
+    def as_dict(self) -> Dict[str, int]:
+        return {name: int(getattr(self, name)) for name, _ in self._fields_}
+
+    @classmethod
+    def from_dict(cls, d: Dict[str, int]) -> "SplitConfig":
+        return cls(**{name: int(d.get(name, 0)) for name, _ in cls._fields_})
+
+
+SPLIT_SLOTS = 64
+
+
 def lib():
     """The loaded library (ctypes.CDLL); raises if it has not been built."""
     global _lib
@@ -102,11 +119,19 @@ def lib():
             "ar_device_cu_count": [ctypes.POINTER(ctypes.c_int)],
             "ar_rmsnorm": [vp, i64, i64, i32, vp, f32, vp, vp],
             "ar_residual_rmsnorm_unfused": [vp, i32, i64, i64, i32, vp, vp, f32, vp, vp, vp],
+            "ar_split_workspace_bytes": [i64],
+            "ar_workspace_clear": [vp, i64, vp],
+            "ar_split_config": [i32, i64, i64, i32, i32, ctypes.POINTER(SplitConfig)],
+            "ar_residual_rmsnorm_ws": [vp, i32, i64, i64, i32, vp, vp, f32, vp, vp, vp, i64, vp],
+            "ar_residual_rmsnorm_split_with_config": [vp, i32, i64, i64, i32, vp, vp, f32, vp,
+                                                      vp, vp, i64, vp,
+                                                      ctypes.POINTER(SplitConfig)],
         }
         for name, argtypes in sig.items():
             fn = getattr(L, name)
             fn.argtypes = argtypes
-            fn.restype = ctypes.c_char_p if name == "ar_status_string" else ctypes.c_int
+            fn.restype = {"ar_status_string": ctypes.c_char_p,
+                          "ar_split_workspace_bytes": ctypes.c_int64}.get(name, ctypes.c_int)
         _lib = L
         return L
 
@@ -193,6 +218,62 @@ def ar_residual_rmsnorm(inputs, residual, gamma, eps: float, residual_out, norm_
         cfg = LaunchConfig.from_dict(config)
         st = lib().ar_residual_rmsnorm_with_config(*args, ctypes.byref(cfg))
     _check(st, "ar_residual_rmsnorm")
+
+
+def split_workspace_bytes(M: int) -> int:
+    """Bytes of workspace ar_residual_rmsnorm_ws needs for calls of up to M rows."""
+    n = int(lib().ar_split_workspace_bytes(int(M)))
+    if n < 0:
+        raise ValueError("bad row count %d" % M)
+    return n
+
+
+def ar_workspace_clear(workspace, stream=None) -> None:
+    """Zero-fills a workspace tensor (a kernel, so it may be captured in a graph)."""
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("the workspace must be a contiguous device tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    s = _stream_handle(stream, workspace.device)
+    _check(lib().ar_workspace_clear(workspace.data_ptr(), nbytes, s), "ar_workspace_clear")
+
+
+def new_workspace(M: int, device):
+    """A zero-filled uint8 tensor of split_workspace_bytes(M) bytes on `device` (torch's
+    allocator; the library allocates nothing)."""
+    import torch
+    return torch.zeros(split_workspace_bytes(M), dtype=torch.uint8, device=device)
+
+
+def ar_split_config(W: int, M: int, H: int, dtype: int, cu_count: int = 0) -> Dict[str, int]:
+    """The split launch shape the heuristic picks (all zeros: one block per row)."""
+    c = SplitConfig()
+    _check(lib().ar_split_config(W, M, H, dtype, cu_count, ctypes.byref(c)), "ar_split_config")
+    return c.as_dict()
+
+
+def ar_residual_rmsnorm_ws(inputs, residual, gamma, eps: float, residual_out, norm_out,
+                           workspace, stream=None, config: Optional[Dict[str, int]] = None) -> None:
+    """kARResidualRMSNorm with a workspace: few-row calls split each row over several blocks
+    (results as ar_residual_rmsnorm).  `workspace`: a contiguous device tensor of at least
+    split_workspace_bytes(M) bytes, zero-filled before its first use (new_workspace).  With
+    `config` the split kernel runs with that shape (ar_residual_rmsnorm_split_with_config)."""
+    ptrs, W, M, H, dt = _marshal_inputs(inputs, residual_out)
+    _marshal_inputs([residual], norm_out)
+    _marshal_inputs([residual], residual_out)
+    _check_gamma(gamma, H, residual_out.device)
+    if not workspace.is_cuda or workspace.device != residual_out.device or \
+            not workspace.is_contiguous():
+        raise ValueError("the workspace must be a contiguous tensor on %s" % residual_out.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    s = _stream_handle(stream, residual_out.device)
+    args = (ptrs, W, M, H, dt, residual.data_ptr(), gamma.data_ptr(), float(eps),
+            residual_out.data_ptr(), norm_out.data_ptr(), workspace.data_ptr(), nbytes, s)
+    if config is None:
+        _check(lib().ar_residual_rmsnorm_ws(*args), "ar_residual_rmsnorm_ws")
+    else:
+        cfg = SplitConfig.from_dict(config)
+        _check(lib().ar_residual_rmsnorm_split_with_config(*args, ctypes.byref(cfg)),
+               "ar_residual_rmsnorm_split_with_config")
 
 
 def _check_gamma(gamma, H, device):

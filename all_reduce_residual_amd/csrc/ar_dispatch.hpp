@@ -328,6 +328,53 @@ inline hipError_t launch_rmsnorm_rows_t(const void* x, const float* gamma, float
   return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, 0, s);
 }
 
+// ---- kARResidualRMSNorm with a row split over several blocks ------------------------------------
+
+struct SplitLaunch {
+  int threads, vpt, segments;
+  uint32_t max_polls;
+};
+
+template <class T, int W, int VPT>
+hipError_t launch_norm_split_v(const void* const* inputs, const void* residual,
+                               const float* gamma, float eps, void* residual_out, void* norm_out,
+                               int64_t M, int64_t H, void* workspace, const SplitLaunch& c,
+                               hipStream_t s) {
+  RankPtrs<W> p = pack_ptrs<W>(inputs);
+  const u32x4* res = static_cast<const u32x4*>(residual);
+  const f32x4* gam = reinterpret_cast<const f32x4*>(gamma);
+  u32x4* ro = static_cast<u32x4*>(residual_out);
+  u32x4* no = static_cast<u32x4*>(norm_out);
+  int V = static_cast<int>(H / T::kVec);
+  int S = c.segments;
+  float count_h = static_cast<float>(H);  // exact: H <= 2^16
+  uint64_t* slots = static_cast<uint64_t*>(workspace);
+  uint32_t polls = c.max_polls;
+  void* args[] = {&p, &res, &gam, &ro, &no, &V, &S, &eps, &count_h, &slots, &polls};
+  const void* fn = reinterpret_cast<const void*>(&arf::ar_norm_split_kernel<T, W, VPT, true>);
+  return hipLaunchKernel(fn, dim3(static_cast<unsigned>(M * S)), dim3(c.threads), args, 0, s);
+}
+
+// vecs_per_thread 1 or 2.
+template <class T>
+inline hipError_t launch_norm_split_t(const void* const* inputs, int W, const void* residual,
+                                      const float* gamma, float eps, void* residual_out,
+                                      void* norm_out, int64_t M, int64_t H, void* workspace,
+                                      const SplitLaunch& c, hipStream_t s) {
+  if (c.vpt == 1) {
+#define AR_CALL(w)                                                                            \
+  launch_norm_split_v<T, w, 1>(inputs, residual, gamma, eps, residual_out, norm_out, M, H, \
+                               workspace, c, s)
+    AR_W_SWITCH(W, AR_CALL)
+#undef AR_CALL
+  }
+#define AR_CALL(w)                                                                            \
+  launch_norm_split_v<T, w, 2>(inputs, residual, gamma, eps, residual_out, norm_out, M, H, \
+                               workspace, c, s)
+  AR_W_SWITCH(W, AR_CALL)
+#undef AR_CALL
+}
+
 // ---- per-element-type entry points (defined in inst_bf16.hip, inst_f16.hip, inst_f32.hip) ----
 
 #define AR_DECLARE_LAUNCHERS(suffix)                                                         \
@@ -355,7 +402,11 @@ inline hipError_t launch_rmsnorm_rows_t(const void* x, const float* gamma, float
                                      hipStream_t s);                                          \
   hipError_t launch_rmsnorm_rows_##suffix(const void* x, const float* gamma, float eps,       \
                                           void* y, int64_t M, int64_t H, int grid,            \
-                                          int threads, int vecs_per_thread, hipStream_t s);
+                                          int threads, int vecs_per_thread, hipStream_t s);\
+  hipError_t launch_norm_split_##suffix(const void* const* inputs, int W, const void* residual, \
+                                        const float* gamma, float eps, void* residual_out,    \
+                                        void* norm_out, int64_t M, int64_t H,                 \
+                                        void* workspace, const SplitLaunch& c, hipStream_t s);
 AR_DECLARE_LAUNCHERS(bf16)
 AR_DECLARE_LAUNCHERS(f16)
 AR_DECLARE_LAUNCHERS(f32)

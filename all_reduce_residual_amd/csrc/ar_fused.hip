@@ -320,6 +320,154 @@ int run_norm(const void* const* inputs, int W, int64_t M, int64_t H, int dtype,
   return e == hipSuccess ? AR_OK : AR_ERR_LAUNCH;
 }
 
+// ---- kARResidualRMSNorm with a row split over several blocks ---------------------------------------
+//
+// For few rows: S blocks per row exchange their partial sums of squares through a caller
+// workspace of AR_SPLIT_SLOTS 8-byte slots per row (see the kernel).  The exchange is what lets a
+// row's W + 1 input streams spread over S CUs instead of one.
+
+constexpr int64_t kSplitSlotBytes = 8;
+constexpr uint32_t kDefaultMaxPolls = 1u << 14;
+
+int64_t split_workspace_bytes(int64_t M) { return M * arf::kSplitSlots * kSplitSlotBytes; }
+
+int split_segments(int64_t V, int threads, int vpt) {
+  return static_cast<int>(ceil_div(V, int64_t(threads) * vpt));
+}
+
+int check_split_cfg(int64_t M, int64_t H, int dtype, const ar_split_cfg_t* c) {
+  if (!c) return AR_ERR_INVALID_ARG;
+  const int t = c->threads_per_block;
+  if (t < 64 || t > arf::kMaxThreads || t % 64 != 0) return AR_ERR_INVALID_ARG;
+  if (c->vecs_per_thread != 1 && c->vecs_per_thread != 2) return AR_ERR_INVALID_ARG;
+  const int64_t V = H / (kVecBytes / elem_size(dtype));
+  const int64_t S = ceil_div(V, int64_t(t) * c->vecs_per_thread);
+  if (S > arf::kSplitSlots || c->segments != S) return AR_ERR_INVALID_ARG;
+  if (M > INT_MAX / S) return AR_ERR_UNSUPPORTED;  // grid = M * S blocks
+  return AR_OK;
+}
+
+// The planned split for (W, M, H): false when one block per row is the better kernel.  From
+// launch sweeps on the MI355X (W = 2 ... 64, H = 4096 ... 8192, M = 1 ... 256):
+//  * the split pays once a row's inputs are large: (W + 1) H sizeof(T) >= 64 KiB (W = 2,
+//    H = 4096, 24 KiB rows: the exchange costs more than it saves at every M);
+//  * one vector per thread, and the narrowest segments (64 lanes, one wave) that keep the grid
+//    within one block per CU: M S <= CUs (M <= 16 at H = 7168: 14 segments, 4.7 -> 3.5 us);
+//  * at least 4 segments, or 2 for rows of >= 192 KiB: with 2 the gain ranged from -4 % (W = 8,
+//    H = 7168, M = 128) to +11 % (W = 64, H = 4096).
+bool plan_split(int W, int64_t M, int64_t H, int dtype, int cu, ar_split_cfg_t* c) {
+  const int64_t V = H / (kVecBytes / elem_size(dtype));
+  const int64_t row_bytes = int64_t(W + 1) * H * elem_size(dtype);
+  if (M < 1 || row_bytes < (int64_t(64) << 10)) return false;
+  const int64_t s_cap = std::min<int64_t>(arf::kSplitSlots, int64_t(cu) / M);
+  const int64_t s_min = row_bytes >= (int64_t(192) << 10) ? 2 : 4;
+  if (s_cap < s_min) return false;
+  int threads = 64;
+  while (ceil_div(V, threads) > s_cap && threads < arf::kMaxThreads) threads *= 2;
+  const int S = split_segments(V, threads, 1);
+  if (S < s_min || S > s_cap) return false;
+  c->threads_per_block = threads;
+  c->vecs_per_thread = 1;
+  c->segments = S;
+  c->max_polls = kDefaultMaxPolls;
+  return true;
+}
+
+// Workspace checks beside validate_norm's.  alias_free: the outputs must not overlap the residual
+// or any input at all (a block that stops waiting re-reads other segments' inputs).
+int validate_split(const void* const* inputs, int W, int64_t M, int64_t H, int dtype,
+                   const void* residual, const float* gamma, const void* residual_out,
+                   const void* norm_out, const void* workspace, int64_t workspace_bytes,
+                   bool* alias_free) {
+  if (!workspace) return AR_ERR_INVALID_ARG;
+  if (!aligned16(workspace)) return AR_ERR_MISALIGNED;
+  if (workspace_bytes < split_workspace_bytes(M)) return AR_ERR_INVALID_ARG;
+  const int64_t bytes = M * H * elem_size(dtype);
+  const Range ws = range_of(workspace, split_workspace_bytes(M));
+  const Range ro = range_of(residual_out, bytes), no = range_of(norm_out, bytes);
+  const Range res = range_of(residual, bytes);
+  if (overlap(ws, ro) || overlap(ws, no) || overlap(ws, res) ||
+      overlap(ws, range_of(gamma, H * int64_t(sizeof(float)))))
+    return AR_ERR_ALIAS;
+  bool free_ = !overlap(ro, res) && !overlap(no, res);
+  for (int r = 0; r < W; ++r) {
+    const Range in = range_of(inputs[r], bytes);
+    if (overlap(ws, in)) return AR_ERR_ALIAS;
+    if (overlap(ro, in) || overlap(no, in)) free_ = false;
+  }
+  *alias_free = free_;
+  return AR_OK;
+}
+
+// planned (user_cfg null): the split kernel when the plan splits and no output aliases an input,
+// else the one-block-per-row kernel.  With user_cfg: the split kernel with that shape, or
+// AR_ERR_ALIAS when an output aliases an input.
+int run_norm_ws(const void* const* inputs, int W, int64_t M, int64_t H, int dtype,
+                const void* residual, const float* gamma, float eps, void* residual_out,
+                void* norm_out, void* workspace, int64_t workspace_bytes, void* stream,
+                const ar_split_cfg_t* user_cfg) {
+  int st = validate_norm(inputs, W, M, H, dtype, residual, gamma, eps, residual_out, norm_out);
+  if (st != AR_OK) return st;
+  if (user_cfg) {
+    st = check_split_cfg(M, H, dtype, user_cfg);
+    if (st != AR_OK) return st;
+  }
+  if (M == 0) return AR_OK;
+  bool alias_free = false;
+  st = validate_split(inputs, W, M, H, dtype, residual, gamma, residual_out, norm_out, workspace,
+                      workspace_bytes, &alias_free);
+  if (st != AR_OK) return st;
+  ar_split_cfg_t cfg;
+  if (user_cfg) {
+    if (!alias_free) return AR_ERR_ALIAS;
+    cfg = *user_cfg;
+  } else {
+    int cu = 0;
+    st = query_cu_count(&cu);
+    if (st != AR_OK) return st;
+    if (!alias_free || !plan_split(W, M, H, dtype, cu, &cfg))
+      return run_norm(inputs, W, M, H, dtype, residual, gamma, eps, residual_out, norm_out,
+                      stream, nullptr);
+  }
+  const arfh::SplitLaunch c{cfg.threads_per_block, cfg.vecs_per_thread, cfg.segments,
+                            cfg.max_polls};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  switch (dtype) {
+    case AR_DTYPE_FP32:
+      e = arfh::launch_norm_split_f32(inputs, W, residual, gamma, eps, residual_out, norm_out, M,
+                                      H, workspace, c, s);
+      break;
+    case AR_DTYPE_FP16:
+      e = arfh::launch_norm_split_f16(inputs, W, residual, gamma, eps, residual_out, norm_out, M,
+                                      H, workspace, c, s);
+      break;
+    default:
+      e = arfh::launch_norm_split_bf16(inputs, W, residual, gamma, eps, residual_out, norm_out,
+                                       M, H, workspace, c, s);
+      break;
+  }
+  return e == hipSuccess ? AR_OK : AR_ERR_LAUNCH;
+}
+
+int run_workspace_clear(void* workspace, int64_t bytes, void* stream) {
+  if (!workspace || bytes < 0) return AR_ERR_INVALID_ARG;
+  if (!aligned16(workspace)) return AR_ERR_MISALIGNED;
+  if (bytes % kSplitSlotBytes != 0) return AR_ERR_INVALID_ARG;
+  if (bytes == 0) return AR_OK;
+  int cu = 0;
+  const int st = query_cu_count(&cu);
+  if (st != AR_OK) return st;
+  uint64_t* p = static_cast<uint64_t*>(workspace);
+  int64_t n = bytes / kSplitSlotBytes;
+  void* args[] = {&p, &n};
+  const int grid = static_cast<int>(std::max<int64_t>(1, std::min(ceil_div(n, 256), int64_t(cu) * 4)));
+  const hipError_t e =
+      hipLaunchKernel(reinterpret_cast<const void*>(&arf::ar_fill_zero_kernel<uint64_t>),
+                      dim3(grid), dim3(256), args, 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? AR_OK : AR_ERR_LAUNCH;
+}
+
 // ---- two-kernel (unfused) path and the stand-alone RMSNorm ----------------------------------------
 //
 // The route for kARResidualRMSNorm shapes the fused kernel does not take (rows that are not whole
@@ -701,6 +849,48 @@ int ar_residual_rmsnorm_with_config(const void* const* inputs, int W, int64_t M,
   if (!cfg) return AR_ERR_INVALID_ARG;
   return run_norm(inputs, W, M, H, dtype, residual, gamma, eps, residual_out, norm_out, stream,
                   cfg);
+}
+
+int64_t ar_split_workspace_bytes(int64_t M) {
+  if (M < 0 || M > (int64_t(1) << 40)) return -1;
+  return split_workspace_bytes(M);
+}
+
+int ar_workspace_clear(void* workspace, int64_t workspace_bytes, void* stream) {
+  return run_workspace_clear(workspace, workspace_bytes, stream);
+}
+
+int ar_split_config(int W, int64_t M, int64_t H, int dtype, int cu_count, ar_split_cfg_t* cfg) {
+  if (!cfg) return AR_ERR_INVALID_ARG;
+  const int st = check_shape(AR_PATTERN_AR_RESIDUAL_RMSNORM, W, M, H, dtype);
+  if (st != AR_OK) return st;
+  int cu = cu_count;
+  if (cu <= 0) {
+    const int q = query_cu_count(&cu);
+    if (q != AR_OK) return q;
+  }
+  if (!plan_split(W, M, H, dtype, cu, cfg) || check_split_cfg(M, H, dtype, cfg) != AR_OK) {
+    *cfg = ar_split_cfg_t{0, 0, 0, 0};
+  }
+  return AR_OK;
+}
+
+int ar_residual_rmsnorm_ws(const void* const* inputs, int W, int64_t M, int64_t H, int dtype,
+                           const void* residual, const float* gamma, float eps,
+                           void* residual_out, void* norm_out, void* workspace,
+                           int64_t workspace_bytes, void* stream) {
+  return run_norm_ws(inputs, W, M, H, dtype, residual, gamma, eps, residual_out, norm_out,
+                     workspace, workspace_bytes, stream, nullptr);
+}
+
+int ar_residual_rmsnorm_split_with_config(const void* const* inputs, int W, int64_t M, int64_t H,
+                                          int dtype, const void* residual, const float* gamma,
+                                          float eps, void* residual_out, void* norm_out,
+                                          void* workspace, int64_t workspace_bytes, void* stream,
+                                          const ar_split_cfg_t* cfg) {
+  if (!cfg) return AR_ERR_INVALID_ARG;
+  return run_norm_ws(inputs, W, M, H, dtype, residual, gamma, eps, residual_out, norm_out,
+                     workspace, workspace_bytes, stream, cfg);
 }
 
 int ar_rmsnorm(const void* x, int64_t M, int64_t H, int dtype, const float* gamma, float eps,

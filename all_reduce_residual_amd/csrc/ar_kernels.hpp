@@ -721,6 +721,181 @@ __global__ __launch_bounds__(kMaxThreads) void ar_rmsnorm_rows_kernel(const void
   }
 }
 
+// ---- kARResidualRMSNorm with a row split over several blocks -------------------------------------
+//
+// With few rows, one block per row leaves most CUs idle and one CU has to stream the whole row of
+// W + 1 inputs (W = 8, H = 7168 bf16: 126 KiB through one CU, the bound at M = 1).  Here a row
+// gets S blocks ("segments") of L threads x VPT vectors.  Each block sums its segment, stores
+// residual_out, reduces the segment's sum of squares and publishes it; the row's blocks then read
+// each other's partial sums, add them in segment order and finish the norm from registers.
+//
+// Exchange: a caller workspace of kSplitSlots 8-byte slots per row; slot j of row m holds
+// (tag << 32) | bits(partial sum of segment j).  Between calls every slot of a row carries the
+// same tag t (a zero-filled workspace: t = 0).  A block reads t from its own slot (no other block
+// writes that slot), and the call leaves tag t + 1 in all kSplitSlots slots of each of its rows
+// (segment sums in the first S, zeros after, written by the last segment), so a slot showing
+// t + 1 holds this call's value.  Tag and value travel in one naturally aligned 8-byte store,
+// which is single-copy atomic, so no fence has to order them; the accesses are relaxed
+// agent-scope atomics, coherent across the XCDs.
+//
+// Waits are bounded: after `max_polls` polls a block stops waiting and computes every segment's
+// partial sum itself with the same code and the same reduction order, so the result is
+// bit-identical either way.  That recomputation re-reads other segments' inputs, so the outputs
+// may not alias any input; and calls that share a workspace must not overlap in time.
+constexpr int kSplitSlots = 64;
+
+// The VPT vectors of segment `seg` owned by this thread: seg * L * VPT + threadIdx.x + k * L
+// (L = blockDim.x); vectors past the row's V are !ok and re-read vector 0.
+template <int VPT>
+__device__ inline void split_offsets(int V, int seg, uint32_t (&boff)[VPT], bool (&ok)[VPT]) {
+  const int L = blockDim.x;
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int i = seg * L * VPT + static_cast<int>(threadIdx.x) + k * L;
+    ok[k] = i < V;
+    boff[k] = static_cast<uint32_t>(ok[k] ? i : 0) * 16u;
+  }
+}
+
+// Sums this thread's vectors of a segment in rank order with the residual last, rounds them to
+// T, and returns this thread's sum of squares of the rounded values.
+template <class T, int W, int VPT>
+__device__ inline float split_segment(const RankPtrs<W>& in, const u32x4* residual, int64_t base,
+                                      const uint32_t (&boff)[VPT], const bool (&ok)[VPT],
+                                      u32x4 (&rounded)[VPT]) {
+  constexpr int kVec = T::kVec;
+  // A segment block is often the only wave on its CU, so its loads in flight are all the memory
+  // parallelism there is: the residual loads go first and every rank batch is staged.  Left
+  // alone, the scheduler issued the second vector's loads and the residual's a round trip late
+  // (two vectors per thread) or recycled registers after ~10 loads (W >= 16).
+  u32x4 rv[VPT];
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) rv[k] = load_stream(at(residual + base, boff[k]));
+  float acc[VPT][kVec];
+  rank_sum<T, W, VPT, default_max_loads<T, VPT>(), true>(in, base, boff, acc);
+  float ss = 0.0f;
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    accumulate<T>(acc[k], rv[k]);
+    rounded[k] = T::narrow(acc[k]);
+    if (ok[k]) {
+      float v[kVec];
+      T::widen(rounded[k], v);
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) ss += v[e] * v[e];
+    }
+  }
+  return ss;
+}
+
+// Grid: M * S blocks of L threads; block b serves segment b % S of row b / S.  Requires
+// 1 <= S <= kSplitSlots, L a multiple of 64, and S * L * VPT >= V.
+template <class T, int W, int VPT, bool kNtStore>
+__global__ __launch_bounds__(kMaxThreads) void ar_norm_split_kernel(
+    RankPtrs<W> in, const u32x4* residual, const f32x4* gamma, u32x4* residual_out,
+    u32x4* norm_out, int V, int S, float eps, float count_h, uint64_t* slots,
+    uint32_t max_polls) {
+  constexpr int kVec = T::kVec;
+  __shared__ float red[kMaxWavesPerBlock];
+  __shared__ float part[kSplitSlots];
+  __shared__ float total_sh;
+  __shared__ int missing_sh;
+
+  const int tid = threadIdx.x;
+  const int m = blockIdx.x / S;
+  const int s = blockIdx.x - m * S;
+  const int64_t base = static_cast<int64_t>(m) * V;
+  uint64_t* row = slots + static_cast<int64_t>(m) * kSplitSlots;
+
+  // Wave 0 reads the row's slots (lane j: slot j) while the data loads are in flight; only this
+  // block's own slot s is used (its tag is the row's current tag, and nobody else writes it).
+  uint64_t slot = 0;
+  if (tid < 64) slot = __hip_atomic_load(row + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  uint32_t boff[VPT];
+  bool ok[VPT];
+  split_offsets<VPT>(V, s, boff, ok);
+  // gamma first: issued with the data loads, not a round trip after them.
+  float gam[VPT][kVec];
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) load_gamma(gamma, boff[k] / 16u, gam[k]);
+  u32x4 rounded[VPT];
+  const float ss = split_segment<T, W, VPT>(in, residual, base, boff, ok, rounded);
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    if (ok[k]) store_vec<kNtStore>(at(residual_out + base, boff[k]), rounded[k]);
+  }
+  const float mine = block_sum(ss, red);
+
+  if (tid < 64) {
+    const int lane = tid;
+    const uint32_t want =
+        static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(slot >> 32), s)) + 1u;
+    const uint64_t tag = static_cast<uint64_t>(want) << 32;
+    if (lane == s) {
+      slot = tag | __float_as_uint(mine);
+      __hip_atomic_store(row + s, slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (s == S - 1 && lane >= S)
+      __hip_atomic_store(row + lane, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bool have = lane >= S || lane == s;
+    for (uint32_t n = 0; __builtin_amdgcn_ballot_w64(!have) != 0 && n < max_polls; ++n) {
+      if (n > 0) __builtin_amdgcn_s_sleep(1);
+      if (!have) {
+        slot = __hip_atomic_load(row + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        have = static_cast<uint32_t>(slot >> 32) == want;
+      }
+    }
+    const bool all = __builtin_amdgcn_ballot_w64(!have) == 0;
+    if (all) {
+      const float p = segment_sum(lane < S ? __uint_as_float(static_cast<uint32_t>(slot)) : 0.0f, 64);
+      if (lane == 0) total_sh = p;
+    }
+    if (lane == 0) missing_sh = all ? 0 : 1;
+  }
+  __syncthreads();
+  if (missing_sh) {
+    // Some segment did not arrive in time: compute every segment's partial sum here.
+    for (int j = 0; j < S; ++j) {
+      float pj = mine;
+      if (j != s) {
+        uint32_t bj[VPT];
+        bool okj[VPT];
+        u32x4 rj[VPT];
+        split_offsets<VPT>(V, j, bj, okj);
+        pj = block_sum(split_segment<T, W, VPT>(in, residual, base, bj, okj, rj), red);
+      }
+      if (tid == 0) part[j] = pj;
+    }
+    __syncthreads();
+    if (tid < 64) {
+      const float p = segment_sum(tid < S ? part[tid] : 0.0f, 64);
+      if (tid == 0) total_sh = p;
+    }
+    __syncthreads();
+  }
+  const float rstd = rsqrtf(total_sh / count_h + eps);
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    if (ok[k]) {
+      float v[kVec];
+      T::widen(rounded[k], v);
+      float y[kVec];
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) y[e] = (v[e] * rstd) * gam[k][e];
+      store_vec<kNtStore>(at(norm_out + base, boff[k]), T::narrow(y));
+    }
+  }
+}
+
+// Zero-fills n 8-byte words (the split kernel's workspace), without a memset node in graphs.
+template <class V>
+__global__ __launch_bounds__(kMaxThreads) void ar_fill_zero_kernel(V* p, int64_t n) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    p[i] = 0;
+}
+
 // ---- Lamport-style one-shot exchange (receive side) ---------------------------------------------
 //
 // The one-shot exchange of the MNNVL all-reduce (flashinfer pull request "Optimizations for

@@ -51,4 +51,12 @@ hipError_t launch_rmsnorm_rows_f16(const void* x, const float* gamma, float eps,
   return launch_rmsnorm_rows_t<F16>(x, gamma, eps, y, M, H, grid, threads, vecs_per_thread, s);
 }
 
+hipError_t launch_norm_split_f16(const void* const* inputs, int W, const void* residual,
+                              const float* gamma, float eps, void* residual_out, void* norm_out,
+                              int64_t M, int64_t H, void* workspace, const SplitLaunch& c,
+                              hipStream_t s) {
+  return launch_norm_split_t<F16>(inputs, W, residual, gamma, eps, residual_out, norm_out, M, H,
+                                  workspace, c, s);
+}
+
 }  // namespace arfh

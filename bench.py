@@ -77,7 +77,7 @@ def metric_bytes(pattern: str, W: int, M: int, H: int, esize: int) -> int:
     stand-alone RMSNorm reads x and writes y."""
     if pattern == "rmsnorm":
         return 2 * M * H * esize
-    extra = 3 if pattern in ("rms", "unfused") else 1
+    extra = 3 if pattern in ("rms", "unfused", "rms_ws") else 1
     return (W + extra) * M * H * esize
 
 
@@ -106,7 +106,7 @@ class Case:
             return t.to(tdt)
 
         self.parts = [randn(*dist) for _ in range(W)]
-        if pattern in ("rms", "unfused", "rmsnorm"):
+        if pattern in ("rms", "unfused", "rmsnorm", "rms_ws"):
             self.res = randn(0.0, 1.0)
             self.gamma = torch.empty(H, dtype=torch.float32, device="cuda").uniform_(
                 0.8, 1.2, generator=g)
@@ -114,7 +114,10 @@ class Case:
             self.no = torch.empty_like(self.res)
             self.fn = {"rms": ar.lib().ar_residual_rmsnorm,
                        "unfused": ar.lib().ar_residual_rmsnorm_unfused,
-                       "rmsnorm": ar.lib().ar_rmsnorm}[pattern]
+                       "rmsnorm": ar.lib().ar_rmsnorm,
+                       "rms_ws": ar.lib().ar_residual_rmsnorm_ws}[pattern]
+            # One workspace serves every rotation set (calls on one stream never overlap).
+            self.ws = ar.new_workspace(M, "cuda") if pattern == "rms_ws" else None
         else:
             self.out = torch.empty_like(self.parts[0])
             self.fn = ar.lib().ar_sum
@@ -132,10 +135,13 @@ class Case:
         if self.pattern == "rmsnorm":
             return (self._sl(self.res, r), self.M, self.H, self.dt, self.gamma.data_ptr(),
                     ctypes.c_float(self.eps), self._sl(self.no, r))
-        if self.pattern in ("rms", "unfused"):
-            return (ptrs, self.W, self.M, self.H, self.dt, self._sl(self.res, r),
+        if self.pattern in ("rms", "unfused", "rms_ws"):
+            args = (ptrs, self.W, self.M, self.H, self.dt, self._sl(self.res, r),
                     self.gamma.data_ptr(), ctypes.c_float(self.eps), self._sl(self.ro, r),
                     self._sl(self.no, r))
+            if self.pattern == "rms_ws":
+                args += (self.ws.data_ptr(), self.ws.numel())
+            return args
         return (ptrs, self.W, self.M, self.H, self.dt, self._sl(self.out, r))
 
     def call(self, i: int, stream_handle: int) -> None:
@@ -543,12 +549,22 @@ def summarize_sweep_trace(d: str, bench_json: str) -> str:
     with open(bench_json) as f:
         line = json.loads(f.read().strip().splitlines()[-1])
     per_call = {(e["pattern"], e["M"]): e for e in line.get("sweep", [])}
+    for e in line.get("sweep", []):
+        if "us_graph_workspace" in e:
+            per_call[("kARResidualRMSNorm, split rows", e["M"])] = dict(
+                e, us_graph=e["us_graph_workspace"])
     W, H = HEADLINE["W"], HEADLINE["H"]
     V = H // 8
     durs = {}
     for r in rows:
         name = r["Kernel_Name"]
         wg, grid = int(r["Workgroup_Size_X"]), int(r["Grid_Size_X"])
+        sp = re.search(r"ar_norm_split_kernel<arf::Bf16, (\d+), (\d+), \w+>", name)
+        if sp and int(sp.group(1)) == W:
+            segments = -(-V // (wg * int(sp.group(2))))
+            durs.setdefault(("kARResidualRMSNorm, split rows", grid // wg // segments), []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+            continue
         m = re.search(r"ar_(norm|sum)_kernel<arf::Bf16, (\d+), (\d+), \w+, arf::StreamSource", name)
         if not m or int(m.group(2)) != W:
             continue
@@ -810,6 +826,16 @@ def main():
                               "GBs": round(c.bytes / (best * 1e-6) / 1e9, 1),
                               "pct_of_peak": round(100 * c.bytes / (best * 1e-6) / 1e9 /
                                                    HBM_PEAK_GBS, 2)})
+                if pattern == "rms":
+                    # The workspace form: rows split over several blocks where the heuristic
+                    # splits them (ar_split_config), else the same kernel as above.
+                    seg = ar.ar_split_config(W, m, H, ar.DTYPE_BF16)["segments"]
+                    if seg:
+                        cw = Case(ar, torch, "rms_ws", W, m, H)
+                        us_ws = cw.time_graph(cw.calls_per_batch(200))
+                        sweep[-1].update({"split_segments": seg,
+                                          "us_graph_workspace": round(us_ws, 3)})
+                        del cw
                 print("# sweep %s" % json.dumps(sweep[-1]), file=sys.stderr, flush=True)
                 del c, warm
                 torch.cuda.empty_cache()

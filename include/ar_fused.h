@@ -27,8 +27,9 @@
  * allocation per partial.  gamma is binary32 [H] for every element type.
  *
  * Ownership: the caller owns every buffer.  `inputs` is a HOST array of W DEVICE pointers; it is
- * read during the call and not retained.  The library allocates no device memory, keeps no
- * workspace and retains no pointer, so calls are safe to capture in a hipGraph and replay.  The
+ * read during the call and not retained.  The library allocates no device memory and retains
+ * no pointer (the one scratch buffer, the split form's workspace below, is the caller's), so
+ * calls are safe to capture in a hipGraph and replay.  The
  * only state is a per-device cache of the compute-unit count.
  *
  * Streams: `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue one kernel (two
@@ -149,6 +150,74 @@ int ar_residual_rmsnorm_with_config(const void* const* inputs, int W, int64_t M,
                                     int dtype, const void* residual, const float* gamma,
                                     float eps, void* residual_out, void* norm_out, void* stream,
                                     const ar_launch_cfg_t* cfg);
+
+/* ---- few rows: one row split over several blocks ---------------------------------------------------
+ *
+ * At decode sizes (few rows) the launch shape, not the arithmetic, sets the time (the flashinfer
+ * pull request "update allreduce to match trtllm", Description: the thread-block / cluster
+ * retuning for a concurrency-128 decode step).  One block per row then leaves most CUs idle and
+ * one CU streams the row's W + 1 inputs.  ar_residual_rmsnorm_ws lets S blocks share a row
+ * (the CDNA4 stand-in for a thread-block cluster): each sums its segment, writes residual_out,
+ * publishes its segment's sum of squares in a caller workspace, reads the others' and finishes
+ * the norm.  Results as ar_residual_rmsnorm (residual_out bit-identical; norm_out within one ulp
+ * of T of the exact expression, deterministic for a given launch shape).
+ *
+ * Workspace: device memory of ar_split_workspace_bytes(M) bytes (AR_SPLIT_SLOTS 8-byte slots
+ * per row), 16-byte aligned, owned by the caller, zero-filled once before its first use (e.g. by
+ * ar_workspace_clear) and then left to the library: every call leaves it valid for the next,
+ * for any shape up to the rows it was sized for.  Calls that share a workspace must not run
+ * concurrently (issue them on one stream).  A workspace that was not zero-filled can make
+ * norm_out wrong.  The workspace must not overlap any tensor argument.
+ *
+ * Waits are bounded: a block that has polled max_polls times without seeing every segment's sum
+ * computes them all itself (same arithmetic, same result, slower), so the kernel always ends. */
+#define AR_SPLIT_SLOTS 64
+
+/* Split launch shape.
+ *   threads_per_block : L, multiple of 64, 64..1024
+ *   vecs_per_thread   : 1 or 2
+ *   segments          : S = ceil((H / (16 / sizeof(T))) / (L * vecs_per_thread)), 1..64
+ *                       (checked; blocks in the grid = M * S)
+ *   max_polls         : polls of the exchange before a block computes the row alone (0: never
+ *                       wait; every block then reads the whole row) */
+typedef struct {
+  int32_t threads_per_block;
+  int32_t vecs_per_thread;
+  int32_t segments;
+  uint32_t max_polls;
+} ar_split_cfg_t;
+
+/* Workspace bytes for calls of up to M rows: M * AR_SPLIT_SLOTS * 8; -1 for M < 0 or
+ * M > 2^40. */
+int64_t ar_split_workspace_bytes(int64_t M);
+
+/* Zero-fills `workspace_bytes` (a multiple of 8) bytes at `workspace` (16-byte aligned) with a
+ * kernel on `stream` (no memset node, so it may be captured in a hipGraph). */
+int ar_workspace_clear(void* workspace, int64_t workspace_bytes, void* stream);
+
+/* The split the heuristic picks for (W, M, H, dtype) on cu_count CUs (<= 0: the current device):
+ * AR_OK with *cfg filled, or all fields 0 when it keeps one block per row for this shape; the
+ * shape's status otherwise.  Pure host arithmetic when cu_count > 0. */
+int ar_split_config(int W, int64_t M, int64_t H, int dtype, int cu_count, ar_split_cfg_t* cfg);
+
+/* kARResidualRMSNorm with a workspace.  Arguments as ar_residual_rmsnorm plus
+ *   workspace, workspace_bytes : as described above (bytes >= ar_split_workspace_bytes(M))
+ * Runs the split kernel when ar_split_config splits the shape and neither output overlaps the
+ * residual or an input; otherwise exactly ar_residual_rmsnorm (in-place calls included).
+ * AR_ERR_INVALID_ARG for a null or too small workspace, AR_ERR_MISALIGNED, AR_ERR_ALIAS if it
+ * overlaps a tensor. */
+int ar_residual_rmsnorm_ws(const void* const* inputs, int W, int64_t M, int64_t H, int dtype,
+                           const void* residual, const float* gamma, float eps,
+                           void* residual_out, void* norm_out, void* workspace,
+                           int64_t workspace_bytes, void* stream);
+
+/* The split kernel with an explicit shape (tuning and tests).  AR_ERR_INVALID_ARG for a
+ * malformed shape, AR_ERR_ALIAS if an output overlaps the residual or an input. */
+int ar_residual_rmsnorm_split_with_config(const void* const* inputs, int W, int64_t M, int64_t H,
+                                          int dtype, const void* residual, const float* gamma,
+                                          float eps, void* residual_out, void* norm_out,
+                                          void* workspace, int64_t workspace_bytes, void* stream,
+                                          const ar_split_cfg_t* cfg);
 
 /* ---- two-shot share -----------------------------------------------------------------------
  *

@@ -27,7 +27,9 @@ def test_exports_every_declared_function(L):
                           "ar_all_gather", "ar_lamport_arm", "ar_lamport_push",
                           "ar_lamport_sum", "ar_lamport_residual_rmsnorm",
                           "ar_policy_default", "ar_route", "ar_rmsnorm",
-                          "ar_residual_rmsnorm_unfused"}
+                          "ar_residual_rmsnorm_unfused", "ar_split_workspace_bytes",
+                          "ar_workspace_clear", "ar_split_config", "ar_residual_rmsnorm_ws",
+                          "ar_residual_rmsnorm_split_with_config"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -228,3 +230,95 @@ def test_probe_library_exports_and_rejects():
     assert fn(p, 9, 2, 64, 0x900008, 0xA00000, 64, None) == 1      # misaligned output
     assert fn(None, 9, 2, 64, 0x900000, 0xA00000, 64, None) == 1
     assert fn(p, 9, 2, 0, 0x900000, 0xA00000, 64, None) == 0       # nothing to do
+
+
+def test_split_workspace_bytes(L):
+    assert L.ar_split_workspace_bytes(0) == 0
+    assert L.ar_split_workspace_bytes(1) == ar.SPLIT_SLOTS * 8
+    assert L.ar_split_workspace_bytes(2048) == 2048 * ar.SPLIT_SLOTS * 8
+    assert L.ar_split_workspace_bytes(-1) == -1
+    assert L.ar_split_workspace_bytes(1 << 41) == -1
+
+
+def test_split_config_invariants():
+    """Planned split shapes are well formed: whole waves, one or two vectors per thread, 2..64
+    segments covering the row exactly once, and a grid of M * S blocks that fits an int; no split
+    once rows alone fill the GPU."""
+    for W, M, H, dt in itertools.product(ar.SUPPORTED_W, [1, 2, 3, 8, 31, 64, 128, 200, 256, 512,
+                                                           4096],
+                                         [8, 256, 1024, 1032, 4096, 7168, 8192, 16384, 65536],
+                                         [BF16, FP16, FP32]):
+        if ar.ar_supports(RMS, W, M, H, dt) != ar.AR_OK:
+            continue
+        c = ar.ar_split_config(W, M, H, dt, 256)
+        if c["segments"] == 0:
+            assert c == {"threads_per_block": 0, "vecs_per_thread": 0, "segments": 0,
+                         "max_polls": 0}
+            continue
+        V = H // (4 if dt == FP32 else 8)
+        t, v, S = c["threads_per_block"], c["vecs_per_thread"], c["segments"]
+        assert t % 64 == 0 and 64 <= t <= 1024 and v in (1, 2), c
+        assert 2 <= S <= ar.SPLIT_SLOTS and S == -(-V // (t * v)), (W, M, H, c)
+        assert (S - 1) * t * v < V <= S * t * v
+        assert M * S < 2 ** 31 and c["max_polls"] > 0
+    assert ar.ar_split_config(8, 4096, 7168, BF16, 256)["segments"] == 0
+    assert ar.ar_split_config(8, 1, 7168, BF16, 256)["segments"] >= 2
+    with pytest.raises(ar.ArError) as e:
+        ar.ar_split_config(12, 4, 7168, BF16, 256)
+    assert e.value.status == ar.AR_ERR_UNSUPPORTED
+    with pytest.raises(ar.ArError) as e:
+        ar.ar_split_config(8, 4, 7170, BF16, 256)
+    assert e.value.status == ar.AR_ERR_UNSUPPORTED
+
+
+def test_split_validation_rejects_before_device_access(L):
+    """Workspace and split-shape checks reject before any device access (fake pointers)."""
+    p = [0x10000 * (i + 1) for i in range(16)]
+    M, H = 4, 7168
+    res, gam, ro, no = 0x1000000, 0x2000000, 0x3000000, 0x4000000
+    ws = 0x5000000
+    need = L.ar_split_workspace_bytes(M)
+
+    def ws_call(workspace, nbytes, cfg=None, ins=p[:8], W=8, r_out=ro, n_out=no):
+        if cfg is None:
+            return L.ar_residual_rmsnorm_ws(_ptrs(ins), W, M, H, BF16, res, gam, 1e-6, r_out,
+                                            n_out, workspace, nbytes, None)
+        return L.ar_residual_rmsnorm_split_with_config(_ptrs(ins), W, M, H, BF16, res, gam, 1e-6,
+                                                       r_out, n_out, workspace, nbytes, None,
+                                                       ctypes.byref(cfg))
+
+    good = ar.SplitConfig(threads_per_block=64, vecs_per_thread=1, segments=14, max_polls=100)
+    assert ws_call(None, need) == ar.AR_ERR_INVALID_ARG
+    assert ws_call(ws, need - 8) == ar.AR_ERR_INVALID_ARG
+    assert ws_call(ws, -1) == ar.AR_ERR_INVALID_ARG
+    assert ws_call(ws + 8, need) == ar.AR_ERR_MISALIGNED
+    assert ws_call(ro + 1024, need) == ar.AR_ERR_ALIAS                 # inside residual_out
+    assert ws_call(p[3] + 512, need) == ar.AR_ERR_ALIAS                # inside a partial
+    assert ws_call(gam - 256, need) == ar.AR_ERR_ALIAS                 # over gamma
+    # Malformed split shapes.
+    for bad in (dict(threads_per_block=96, vecs_per_thread=1, segments=10),
+                dict(threads_per_block=64, vecs_per_thread=4, segments=4),
+                dict(threads_per_block=64, vecs_per_thread=1, segments=13),
+                dict(threads_per_block=2048, vecs_per_thread=1, segments=1)):
+        cfg = ar.SplitConfig(max_polls=1, **bad)
+        assert ws_call(ws, need, cfg) == ar.AR_ERR_INVALID_ARG, bad
+    assert L.ar_residual_rmsnorm_split_with_config(_ptrs(p[:8]), 8, M, H, BF16, res, gam, 1e-6,
+                                                   ro, no, ws, need, None,
+                                                   None) == ar.AR_ERR_INVALID_ARG
+    # More than 64 segments (H = 65536 bf16 at 64 x 1 vectors per block: 128).
+    cfg = ar.SplitConfig(threads_per_block=64, vecs_per_thread=1, segments=128, max_polls=1)
+    assert L.ar_residual_rmsnorm_split_with_config(
+        _ptrs(p[:8]), 8, M, 65536, BF16, res, gam, 1e-6, ro, no, ws, need, None,
+        ctypes.byref(cfg)) == ar.AR_ERR_INVALID_ARG
+    # The explicit split refuses outputs that alias the residual or an input.
+    assert ws_call(ws, need, good, r_out=res) == ar.AR_ERR_ALIAS
+    assert ws_call(ws, need, good, n_out=p[2]) == ar.AR_ERR_ALIAS
+    # Ordinary norm validation still applies (world size 12, bad eps).
+    assert ws_call(ws, need, ins=p[:12], W=12) == ar.AR_ERR_UNSUPPORTED
+    assert L.ar_residual_rmsnorm_ws(None, 8, 0, H, BF16, None, None, 1e-6, None, None, None, 0,
+                                    None) == ar.AR_OK
+    # Workspace clearing: null, misaligned, not a multiple of 8; zero bytes is a no-op.
+    assert L.ar_workspace_clear(None, 64, None) == ar.AR_ERR_INVALID_ARG
+    assert L.ar_workspace_clear(ws + 8, 64, None) == ar.AR_ERR_MISALIGNED
+    assert L.ar_workspace_clear(ws, 12, None) == ar.AR_ERR_INVALID_ARG
+    assert L.ar_workspace_clear(ws, 0, None) == ar.AR_OK

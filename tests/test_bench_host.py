@@ -1,0 +1,62 @@
+"""Host logic of bench.py (no GPU): the metric's byte count and the summaries it writes from
+rocprofv3 output."""
+import csv
+import json
+import os
+
+import bench
+
+
+def test_metric_bytes():
+    # kARResidualRMSNorm: W partial reads + residual read + two writes; kAllReduce: W reads + 1.
+    assert bench.metric_bytes("rms", 8, 2048, 7168, 2) == 322_961_408
+    assert bench.metric_bytes("rms_ws", 8, 2048, 7168, 2) == 322_961_408
+    assert bench.metric_bytes("unfused", 8, 2048, 7168, 2) == 322_961_408
+    assert bench.metric_bytes("sum", 8, 2048, 7168, 2) == 264_241_152
+    assert bench.metric_bytes("sum", 4, 5120, 8192, 2) == 419_430_400
+    assert bench.metric_bytes("rmsnorm", 1, 2048, 7168, 2) == 2 * 2048 * 7168 * 2
+
+
+def _trace(path, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Workgroup_Size_X", "Grid_Size_X",
+                                          "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for r in rows:
+            w.writerow(r)
+
+
+def test_sweep_trace_summary(tmp_path):
+    """One-block rows (M = grid / block), split rows (M = grid / block / segments) and flat sums
+    (M = grid x U / vectors per row) are attributed to their sweep entries."""
+    norm = "void arf::ar_norm_kernel<arf::Bf16, 8, 2, true, arf::StreamSource, false>(...)"
+    split = "void arf::ar_norm_split_kernel<arf::Bf16, 8, 1, true>(...)"
+    summ = "void arf::ar_sum_kernel<arf::Bf16, 8, 2, true, arf::StreamSource>(...)"
+    rows = []
+    for i in range(3):
+        rows.append(dict(Kernel_Name=norm, Workgroup_Size_X=448, Grid_Size_X=448 * 32,
+                         Start_Timestamp=1000 * i, End_Timestamp=1000 * i + 3000))
+        # 32 rows x 7 segments of 128 lanes (896 vectors per row).
+        rows.append(dict(Kernel_Name=split, Workgroup_Size_X=128, Grid_Size_X=128 * 7 * 32,
+                         Start_Timestamp=1000 * i, End_Timestamp=1000 * i + 2000))
+        # 32 rows x 896 vectors / 2 per thread.
+        rows.append(dict(Kernel_Name=summ, Workgroup_Size_X=64, Grid_Size_X=32 * 896 // 2,
+                         Start_Timestamp=0, End_Timestamp=1500))
+    d = tmp_path / "trace"
+    d.mkdir()
+    _trace(d / "sw_kernel_trace.csv", rows)
+    line = {"sweep": [
+        {"pattern": "kARResidualRMSNorm", "M": 32, "bytes": 5_046_272, "us_graph": 5.3,
+         "split_segments": 7, "us_graph_workspace": 4.2},
+        {"pattern": "kAllReduce", "M": 32, "bytes": 4_128_768, "us_graph": 2.7}]}
+    bj = tmp_path / "bench.json"
+    bj.write_text("# noise\n" + json.dumps(line) + "\n")
+    out = bench.summarize_sweep_trace(str(d), str(bj))
+    lines = [x for x in out.splitlines() if x.startswith("| k")]
+    assert len(lines) == 3, out
+    by = {x.split("|")[1].strip(): x for x in lines}
+    assert "| 32 | 5046272 | 3 | 3.00 |" in by["kARResidualRMSNorm"]
+    assert "| 32 | 5046272 | 3 | 2.00 |" in by["kARResidualRMSNorm, split rows"]
+    assert "| 4.20 |" in by["kARResidualRMSNorm, split rows"]
+    assert "| 32 | 4128768 | 3 | 1.50 |" in by["kAllReduce"]
+    assert os.path.exists(bj)
