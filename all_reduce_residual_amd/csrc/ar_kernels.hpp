@@ -489,6 +489,8 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_kernel(
 
   // gamma does not depend on the row.  With few vectors per thread this thread's slice is
   // loaded once and kept in registers; with many it is re-read (from L2) in the epilogue.
+  // (Kept for 4 vectors with one or two partials: 7 % faster at 2 rows per CU, 20-30 % slower
+  // from 3 on -- the extra registers cost waves; measured.)
   constexpr bool kKeepGamma = VPT <= 2;
   float gam[kKeepGamma ? VPT : 1][kVec];
   if constexpr (kKeepGamma) {
