@@ -3,8 +3,9 @@
 // per element type in inst_*.hip; the all-gather kernel is instantiated here).
 //
 // Nothing here allocates device memory or synchronises: each entry point validates, picks a
-// launch shape and enqueues exactly one kernel on the caller's stream.  Validation runs before
-// any HIP call, so a rejected call touches neither the device nor the outputs.
+// launch shape and enqueues its kernel on the caller's stream (two for the two-kernel path).
+// Validation runs before any HIP call, so a rejected call touches neither the device nor the
+// outputs.
 
 #include <hip/hip_runtime.h>
 

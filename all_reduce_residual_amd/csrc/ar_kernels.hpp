@@ -1,17 +1,22 @@
 // ar_kernels.hpp -- gfx950 device code of the fused all-reduce-sum (+ residual + RMSNorm) core.
 //
-// Two kernels, templated on the element type T, the number of partials W, the number of
-// 16-byte vectors per thread and the store policy:
+// The two core kernels, templated on the element type T, the number of partials W, the number
+// of 16-byte vectors per thread and the store policy:
 //
-//   ar_sum_kernel   kAllReduce.  A flat grid-stride walk over the [M, H] tensors viewed as
-//                   16-byte vectors.  Each thread issues the W loads of its vectors before it
-//                   starts the binary32 chain, so a wave keeps W x U x 1 KiB of reads in flight.
+//   ar_sum_kernel   kAllReduce.  A flat walk over the [M, H] tensors viewed as 16-byte vectors.
+//                   Each thread issues the W loads of its vectors before it starts the binary32
+//                   chain, so a wave keeps W x U x 1 KiB of reads in flight.
 //   ar_norm_kernel  kARResidualRMSNorm.  `lanes_per_row` consecutive threads own one row; each
 //                   holds its vectors' rounded residual_out values in registers between the sum
 //                   and the norm, so every byte is read once and written once.  The per-row sum
 //                   of squares is reduced with DPP lane moves and a swizzle inside a wave, then
 //                   across waves through LDS with one barrier per row (LDS slots alternate
 //                   between two banks so consecutive rows need no second barrier).
+//
+// Around them: ar_norm_split_kernel (few rows: a row split over several blocks that exchange
+// partial sums of squares through a caller workspace), ar_rmsnorm_rows_kernel (RMSNorm of rows
+// of any width, the two-kernel path's second step), the Lamport-style exchange (a polling input
+// source plus producer and arming kernels) and ar_gather_kernel (the two-shot all-gather share).
 //
 // The fusion patterns are the ones named in the tokenspeed pull request "perf(comm): route
 // generic MNNVL AR patterns to upstream flashinfer" (Summary).  The peers' buffers are passed as

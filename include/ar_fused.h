@@ -343,8 +343,8 @@ typedef struct {
  * one-shot moves the whole payload S over each peer link, two-shot 2 S / W but pays a second
  * exchange (~5 us); two-shot wins once S (1 - 2 / W) / 153 GB/s exceeds 5 us, i.e. from
  * 5 us * 153 GB/s / (1 - 2 / W) (W = 8: 1.02 MB); for W <= 2 two-shot never wins (INT64_MAX).
- * max_payload_bytes = 0: the library needs no workspace.  A model, not a measurement: the
- * crossover needs two GPUs to measure. */
+ * max_payload_bytes = 0: no path here needs a payload-sized workspace.  A model, not a
+ * measurement: the crossover needs two GPUs to measure. */
 int ar_policy_default(int W, ar_policy_t* policy);
 
 /* Route for one call: AR_ROUTE_FALLBACK if neither the fused kernel nor the two-kernel path
