@@ -84,6 +84,24 @@ def test_wide_hidden_decode_sizes_planned(oracle_mod, M):
     _check(oracle_mod, parts, res, gam, wl.eps, "bf16", ro, no)
 
 
+PLANNED = [(16, 4, 8192, "fp16"), (4, 32, 8192, "bf16"), (64, 2, 4096, "bf16"),
+           (32, 3, 8192, "fp32"), (16, 100, 8192, "bf16"), (8, 64, 7168, "fp16")]
+
+
+@pytest.mark.parametrize("W,M,H,dtype", PLANNED, ids=["W%d-M%d-H%d-%s" % c for c in PLANNED])
+def test_planned_splits_match_oracle(oracle_mod, W, M, H, dtype):
+    """Shapes the heuristic splits (2 to 16 segments), through the planned entry point."""
+    cfg = ar.ar_split_config(W, M, H, {"bf16": ar.DTYPE_BF16, "fp16": ar.DTYPE_FP16,
+                                       "fp32": ar.DTYPE_FP32}[dtype])
+    assert cfg["segments"] >= 2, cfg
+    print("case split planned", W, M, H, dtype, cfg, flush=True)
+    parts, res, gam = synth.custom(W, M, H, dtype, seed=13 * W + M)
+    ws = ar.new_workspace(M, "cuda")
+    ro, no = _run(parts, res, gam, 1e-6, ws)
+    _check(oracle_mod, parts, res, gam, 1e-6, dtype, ro, no)
+    assert (_tags(ws, M) == 1).all()
+
+
 def test_fp16_outliers_many_ranks(oracle_mod):
     print("case split fp16 outliers", flush=True)
     wl = synth.WORKLOADS["fp16_many_rank"]
