@@ -112,16 +112,38 @@ int cap_grid(int64_t blocks) {
   return blocks > INT_MAX ? INT_MAX : static_cast<int>(blocks);
 }
 
-void plan_sum(int W, int64_t n, int dtype, int cu, ar_launch_cfg_t* c) {
+// max_resident_u: the largest vectors per thread the one-round shapes below may use -- 4 for the
+// plain sum; 2 for the two-kernel path's residual sum (its kernel is built for one or two
+// vectors per thread); 0 for none (the Lamport consumer keeps the single-wave shape it was
+// tuned with).
+void plan_sum(int W, int64_t n, int dtype, int cu, ar_launch_cfg_t* c, int max_resident_u = 4) {
   const int64_t vec = kVecBytes / elem_size(dtype);
   const int64_t nvec = n / vec;
   // Single-wave blocks, one 16-byte vector per thread, one block per 64 vectors: the most
   // independent waves for the dispatcher to spread over the 256 CUs.  Small payloads (fewer
   // than 16 such blocks per CU) do better with two vectors per thread and half the blocks.
-  const int threads = 64;
+  int threads = 64;
   // (Two vectors per thread only for W <= 8: beyond that the doubled loads and rank pointers no
   // longer fit the registers and spill.)
-  const int u = (W <= 8 && ceil_div(nvec, threads) < int64_t(cu) * 16) ? 2 : 1;
+  int u = (W <= 8 && ceil_div(nvec, threads) < int64_t(cu) * 16) ? 2 : 1;
+  // Mid-size payloads that one resident round of 3/4 to 2 blocks of 256 threads per CU covers
+  // exactly: one launch round with no block scheduling behind it beats many single-wave blocks
+  // (W = 8, H = 7168 bf16: M = 64 / 128 11 % and 8 % faster at one vector per thread, M = 512
+  // 2-5 % at four; W = 32 / 64 at M = 512 8-14 %).  One vector per thread only for W <= 8
+  // (with more ranks it measured from 8 % slower to 9 % faster), four only for W >= 8 (2-5 %
+  // slower at W = 2 and 4).
+  if (max_resident_u >= 1) {
+    const int64_t b1 = ceil_div(nvec, int64_t(256));
+    const int64_t b4 = ceil_div(nvec, int64_t(1024));
+    if (W <= 8 && b1 >= int64_t(cu) * 3 / 4 && b1 <= int64_t(cu) * 2) {
+      threads = 256;
+      u = 1;
+    } else if (max_resident_u >= 4 && W >= 8 && b4 >= int64_t(cu) * 3 / 2 &&
+               b4 <= int64_t(cu) * 2) {
+      threads = 256;
+      u = 4;
+    }
+  }
   c->threads_per_block = threads;
   c->vecs_per_thread = u;
   c->lanes_per_row = 0;
@@ -564,7 +586,7 @@ int run_unfused(const void* const* inputs, int W, int64_t M, int64_t H, int dtyp
   st = query_cu_count(&cu);
   if (st != AR_OK) return st;
   ar_launch_cfg_t cfg;
-  plan_sum(W + 1, M * H, dtype, cu, &cfg);
+  plan_sum(W + 1, M * H, dtype, cu, &cfg, 2);
   const int64_t vec = kVecBytes / elem_size(dtype);
   const int64_t nvec = M * H / vec;
   const int tail = static_cast<int>(M * H - nvec * vec);
@@ -750,7 +772,7 @@ int run_lamport_sum(void* rbuf, int W, int64_t M, int64_t H, int dtype, void* ou
   st = query_cu_count(&cu);
   if (st != AR_OK) return st;
   ar_launch_cfg_t cfg;
-  plan_sum(W, M * H, dtype, cu, &cfg);
+  plan_sum(W, M * H, dtype, cu, &cfg, 0);
   cfg.vecs_per_thread = 1;  // the Lamport consumer is instantiated for one vector per thread
   cfg.grid = cap_grid(ceil_div(M * H / (kVecBytes / elem_size(dtype)), cfg.threads_per_block));
   cfg.nt_store = 1;

@@ -122,6 +122,29 @@ def test_launch_config_headline_shapes():
         assert c["lanes_per_row"] * c["vecs_per_thread"] >= 896
 
 
+def test_launch_config_sum_resident_round():
+    """Mid-size sums that 3/4 to 2 blocks of 256 threads per CU cover run as one resident round
+    (one vector per thread for W <= 8, four for W >= 8); other sizes keep single-wave blocks."""
+    def shape(W, M, H=7168):
+        c = ar.ar_launch_config(SUM, W, M, H, BF16, cu_count=256)
+        return c["threads_per_block"], c["vecs_per_thread"], c["grid"]
+    assert shape(8, 64) == (256, 1, 224)
+    assert shape(8, 128) == (256, 1, 448)
+    assert shape(2, 128) == (256, 1, 448)
+    assert shape(8, 512) == (256, 4, 448)
+    assert shape(64, 512) == (256, 4, 448)
+    assert shape(16, 512, 8192) == (256, 4, 512)
+    assert shape(2, 512) == (64, 1, 7168)          # W <= 4: four vectors per thread lose
+    assert shape(16, 128) == (64, 1, 1792)         # W >= 16: one vector per thread is mixed
+    assert shape(8, 2048) == (64, 1, 28672)        # beyond one round
+    assert shape(8, 8) == (64, 2, 56)              # too few blocks for the round
+    # On a GPU with fewer CUs the bands move with the CU count.
+    c = ar.ar_launch_config(SUM, 8, 128, 7168, BF16, cu_count=80)
+    assert (c["threads_per_block"], c["vecs_per_thread"]) == (64, 1)
+    c = ar.ar_launch_config(SUM, 8, 40, 7168, BF16, cu_count=80)
+    assert (c["threads_per_block"], c["vecs_per_thread"], c["grid"]) == (256, 1, 140)
+
+
 def test_launch_config_rejects():
     with pytest.raises(ar.ArError) as e:
         ar.ar_launch_config(RMS, 12, 4, 256, BF16, cu_count=256)
