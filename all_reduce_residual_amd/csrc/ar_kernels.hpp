@@ -673,9 +673,15 @@ __device__ inline float block_sum(float v, float* red) {
 
 // One block per row (grid stride over rows).  K > 0: thread t owns vectors t + k * blockDim.x
 // (k < K) and keeps their values in registers between the sum of squares and the scaling, so x
-// is read once.  K = 0 (rows longer than 8 vectors per thread of a 1024-thread block): the row is
-// read twice, the second time normally from cache.  y may be x itself: every element is read
-// (pass 1) before the barrier and written afterwards by the thread that read it.
+// is read once.  Every one of those K vectors is loaded whole and unconditionally first (a lane
+// with no vector re-reads an in-range one), so the K loads are in flight together; elements of a
+// vector that belong to a neighbouring row are then masked to zero.  Only a vector that runs
+// past the end of the tensor (the last row's last vector when M * H is not a multiple of the
+// vector width) is read element by element.  K = 0 (rows longer than 8 vectors per thread of a
+// 1024-thread block): the row is read twice, the second time normally from cache.  y may be x
+// itself: every element is read (pass 1) before the barrier and written afterwards by the thread
+// that read it (a whole-vector load may also read a neighbouring row's elements while that row's
+// block rewrites them; those values are discarded).
 template <class T, int K>
 __global__ __launch_bounds__(kMaxThreads) void ar_rmsnorm_rows_kernel(const void* x,
                                                                       const float* gamma,
@@ -685,6 +691,9 @@ __global__ __launch_bounds__(kMaxThreads) void ar_rmsnorm_rows_kernel(const void
   constexpr int kVec = T::kVec;
   __shared__ float red[kMaxWavesPerBlock];
   const int64_t nthreads = blockDim.x;
+  // Whole vectors in the tensor; a vector index at or past this one is not wholly inside it.
+  const int64_t nfull = (M * H) / kVec;
+  const u32x4* xv = static_cast<const u32x4*>(x);
   for (int64_t m = blockIdx.x; m < M; m += gridDim.x) {
     const int64_t e0 = m * H;
     const int64_t e1 = e0 + H;
@@ -693,18 +702,40 @@ __global__ __launch_bounds__(kMaxThreads) void ar_rmsnorm_rows_kernel(const void
     float ss = 0.0f;
     if constexpr (K > 0) {
       float f[K][kVec];
+      if (nfull > 0) {
+        u32x4 raw[K];
 #pragma unroll
-      for (int k = 0; k < K; ++k) {
-        const int64_t j = threadIdx.x + k * nthreads;
-        if (j < nv) {
-          load_row_vec<T, true>(x, e0, e1, v0 + j, f[k]);
-        } else {
+        for (int k = 0; k < K; ++k) {
+          const int64_t v = v0 + threadIdx.x + k * nthreads;
+          raw[k] = load_stream(xv + (v < nfull ? v : nfull - 1));
+        }
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          const int64_t j = threadIdx.x + k * nthreads;
+          const int64_t a = (v0 + j) * kVec;
+          T::widen(raw[k], f[k]);
+#pragma unroll
+          for (int e = 0; e < kVec; ++e) {
+            const bool in_row = j < nv && a + e >= e0 && a + e < e1;
+            f[k][e] = in_row ? f[k][e] : 0.0f;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
 #pragma unroll
           for (int e = 0; e < kVec; ++e) f[k][e] = 0.0f;
         }
+      }
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int64_t j = threadIdx.x + k * nthreads;
+        if (j < nv && v0 + j >= nfull) load_row_vec<T, false>(x, e0, e1, v0 + j, f[k]);
 #pragma unroll
         for (int e = 0; e < kVec; ++e) ss += f[k][e] * f[k][e];
       }
+      // gamma is read in the epilogue, per vector (L2): moving all of it before the barrier
+      // measured slower (H = 7170: 15.9 -> 18.3 us), the other blocks on the CU hide its latency.
       const float rstd = rsqrtf(block_sum(ss, red) / count_h + eps);
 #pragma unroll
       for (int k = 0; k < K; ++k) {
