@@ -519,6 +519,79 @@ def cpu_baseline(min_wall: float = 1.5) -> dict:
             "cpu_model": cpu_model()}
 
 
+def cpu_oracle_configs(min_wall: float = 0.3) -> list:
+    """The oracle (unchanged) on the other workload configurations, one call at their full
+    size (row slices over the host threads as for the headline's baseline; calls of fewer than
+    2^20 input elements on one thread), repeated for at least `min_wall` seconds: milliseconds
+    per call and GB/s of the same byte count."""
+    import numpy as np
+
+    import oracle
+    import synth
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    threads = max(1, min(16, avail))
+    out = []
+    for name in ("tiny", "llama3_decode", "large_sum", "fp16_many_rank"):
+        wl = synth.WORKLOADS[name]
+        M = wl.Ms[0]
+        parts, res, gam = synth.inputs(wl, M)
+        hp = [synth.storage_numpy(p) for p in parts]
+        pattern = "rms" if "rms" in wl.patterns else "sum"
+        o1 = np.empty_like(hp[0])
+        o2 = np.empty_like(hp[0])
+        # Small calls on one thread: starting threads would cost more than the work.
+        nt = 1 if (wl.W + 1) * M * wl.H < (1 << 20) else max(1, min(threads, M))
+        bounds = [(M * i // nt, M * (i + 1) // nt) for i in range(nt)]
+        if pattern == "rms":
+            hr, g = synth.storage_numpy(res), gam.numpy()
+            fn = lambda b: oracle.ar_residual_rmsnorm(hp, hr, g, wl.eps, wl.dtype, rows=b,  # noqa
+                                                      residual_out=o1, norm_out=o2)
+        else:
+            fn = lambda b: oracle.ar_sum(hp, wl.dtype, rows=b, out=o1)  # noqa: E731
+
+        def one_call():
+            if nt == 1:
+                fn(bounds[0])
+                return
+            ts = [threading.Thread(target=fn, args=(b,)) for b in bounds]
+            for t in ts:
+                t.start()
+            for t in ts:
+                t.join()
+
+        one_call()
+        n, t0 = 0, time.perf_counter()
+        while True:
+            one_call()
+            n += 1
+            if time.perf_counter() - t0 >= min_wall:
+                break
+        dt = (time.perf_counter() - t0) / n
+        nbytes = metric_bytes(pattern, wl.W, M, wl.H, 4 if wl.dtype == "fp32" else 2)
+        out.append({"config": name, "pattern": "kARResidualRMSNorm" if pattern == "rms"
+                    else "kAllReduce", "W": wl.W, "M": M, "H": wl.H, "element_type": wl.dtype,
+                    "threads": nt, "calls": n, "ms_per_call": round(dt * 1e3, 4),
+                    "GBs": round(nbytes / dt / 1e9, 3)})
+        print("# oracle %s" % json.dumps(out[-1]), file=sys.stderr, flush=True)
+    return out
+
+
+def box_facts(torch, ar) -> dict:
+    """What the numbers were measured on: the GPU (name, architecture, compute units as the
+    library's launch planning sees them, device memory) and the host (CPU model, threads this
+    process may run on)."""
+    props = torch.cuda.get_device_properties(0)
+    return {"gpu": torch.cuda.get_device_name(0),
+            "arch": getattr(props, "gcnArchName", "unknown"),
+            "compute_units": ar.ar_device_cu_count(),
+            "device_memory_GiB": round(props.total_memory / 2 ** 30, 1),
+            "host_cpu": cpu_model(),
+            "host_threads": len(os.sched_getaffinity(0))}
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -731,9 +804,10 @@ def main():
                           max(2, args.steps), "rotation_sets": case.R}))
         return 0
 
-    print("# device: %s, %d CUs, host %s, %d host threads" % (
-        torch.cuda.get_device_name(0), ar.ar_device_cu_count(), cpu_model(),
-        len(os.sched_getaffinity(0))), file=sys.stderr, flush=True)
+    box = box_facts(torch, ar)
+    print("# device: %s (%s), %d CUs, %.0f GiB, host %s, %d host threads" % (
+        box["gpu"], box["arch"], box["compute_units"], box["device_memory_GiB"], box["host_cpu"],
+        box["host_threads"]), file=sys.stderr, flush=True)
 
     # Headline: warm-up, then exactly `steps` timed steps on rotated buffer sets.
     case = Case(ar, torch, "rms", W, M, H)
@@ -780,6 +854,7 @@ def main():
                    "bytes_per_call": metric_bytes("rms", W, M, H, 2),
                    "launch": launch_cfg, "parity": parity},
     }
+    result["box"] = box
     traffic = read_traffic()
     result["roofline"] = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
                           "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
@@ -846,6 +921,7 @@ def main():
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline()
+        result["cpu_baseline"]["other_configs"] = cpu_oracle_configs()
     print(json.dumps(result), flush=True)
     return 0
 
