@@ -523,11 +523,23 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_kernel(
     } else if constexpr (VPT <= 2 || (W + 1) * VPT <= 20) {
       // All vectors' chains together: the most independent loads per batch (with few
       // partials even 4-8 vectors' accumulators fit beside a batch of loads, no spill).
+      // Staged with two or four partials and two vectors: left alone, the scheduler issued
+      // those loads one rank at a time, each a round trip after the previous one.  The staged
+      // form issues the residual's loads first (its fences would otherwise hold them back a
+      // round trip); it is still added after the W partials.
+      constexpr bool kStageChains = (W == 2 || W == 4) && VPT == 2;
+      u32x4 res_v[VPT];
+      if constexpr (kStageChains) {
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) res_v[k] = load_stream(at(residual + base, boff[k]));
+      }
       float acc[VPT][kVec];
-      src.template sum<T, W, VPT>(in, base, boff, ok, acc);
+      src.template sum<T, W, VPT, default_max_loads<T, VPT>(), kStageChains>(in, base, boff, ok,
+                                                                             acc);
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {
-        accumulate<T>(acc[k], load_stream(at(residual + base, boff[k])));
+        if constexpr (!kStageChains) res_v[k] = load_stream(at(residual + base, boff[k]));
+        accumulate<T>(acc[k], res_v[k]);
         rounded[k] = T::narrow(acc[k]);
       }
     } else {
