@@ -145,6 +145,22 @@ def test_launch_config_sum_resident_round():
     assert (c["threads_per_block"], c["vecs_per_thread"], c["grid"]) == (256, 1, 140)
 
 
+def test_launch_config_many_ranks_many_rows():
+    """W >= 32 with 16-bit rows and at least 8 rows per CU: one vector per thread over the
+    whole row; otherwise the two-vector rows of up to 512 lanes."""
+    def shape(W, M, H=7168, dt=BF16, cu=256):
+        c = ar.ar_launch_config(RMS, W, M, H, dt, cu_count=cu)
+        return c["threads_per_block"], c["vecs_per_thread"]
+    assert shape(32, 2048) == (896, 1)
+    assert shape(64, 2048) == (896, 1)
+    assert shape(32, 2048, 8192, FP16) == (1024, 1)
+    assert shape(64, 4096, 16384) == (1024, 2)            # wider rows: the fewest vectors
+    assert shape(32, 2047) == (448, 2)                    # under 8 rows per CU
+    assert shape(16, 2048) == (448, 2)
+    assert shape(32, 2048, 4096, FP32) == (512, 2)
+    assert shape(32, 640, cu=80) == (896, 1)              # the bound moves with the CU count
+
+
 def test_launch_config_rejects():
     with pytest.raises(ar.ArError) as e:
         ar.ar_launch_config(RMS, 12, 4, 256, BF16, cu_count=256)

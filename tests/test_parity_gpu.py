@@ -288,3 +288,34 @@ def test_sum_resident_round_shapes(oracle_mod, W, M, H):
     torch.cuda.synchronize()
     want = oracle_mod.ar_sum([host_np(p.cpu()) for p in parts], "bf16")
     assert_bit_exact(host_np(out.cpu()), want, "bf16", "out")
+
+
+# ---- many ranks at many rows: one vector per thread over the whole row -----------------------------
+
+MANY = [(32, 2048, 7168, "bf16"), (64, 2048, 8192, "fp16")]
+
+
+@pytest.mark.parametrize("W,M,H,dtype", MANY, ids=["W%d-M%d-H%d-%s" % c for c in MANY])
+def test_many_ranks_many_rows_sampled(oracle_mod, W, M, H, dtype):
+    """The planned shape for W >= 32 with 16-bit rows and >= 8 rows per CU; sampled rows of
+    both outputs against the oracle run on those rows.  Inputs drawn on the GPU by torch's
+    seeded generator."""
+    tdt = TD[dtype]
+    cfg = ar.ar_launch_config(ar.PATTERN_AR_RESIDUAL_RMSNORM, W, M, H, ar.dtype_code(tdt))
+    print("case", W, M, H, dtype, cfg, flush=True)
+    assert cfg["vecs_per_thread"] == 1 and cfg["lanes_per_row"] * 8 == H
+    g = torch.Generator(device="cuda")
+    g.manual_seed(W + M)
+    parts = [torch.empty((M, H), dtype=tdt, device="cuda").normal_(0.0, 0.05, generator=g)
+             for _ in range(W)]
+    res = torch.empty((M, H), dtype=tdt, device="cuda").normal_(0.0, 1.0, generator=g)
+    gam = torch.empty(H, dtype=torch.float32, device="cuda").uniform_(0.5, 1.5, generator=g)
+    ro, no = torch.empty_like(res), torch.empty_like(res)
+    ar.ar_residual_rmsnorm(parts, res, gam, 1e-6, ro, no)
+    torch.cuda.synchronize()
+    rows = torch.tensor([0, 1, 255, 256, 1023, 1024, M - 2, M - 1], device="cuda")
+    want_ro, want_no = oracle_mod.ar_residual_rmsnorm(
+        [host_np(p[rows].cpu()) for p in parts], host_np(res[rows].cpu()),
+        gam.cpu().numpy(), 1e-6, dtype)
+    assert_bit_exact(host_np(ro[rows].cpu()), want_ro, dtype, "residual_out")
+    assert_norm_close(host_np(no[rows].cpu()), want_no, dtype)
