@@ -8,8 +8,11 @@ numpy's float16 cast, over
     that decide a rounding (exact tie, one below, one above, all ones, zero) at every rounding
     position the format can have (normal and subnormal targets),
   * a random sample of binary32 patterns,
+  * every binary32 pattern (exhaustive, 2^32 inputs in parallel chunks, ~30 s),
 and to hand-derived IEEE cases (ties to even, overflow, gradual underflow).
 """
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -83,6 +86,31 @@ def test_round_bf16_matches_torch(oracle_mod, xs):
 @pytest.mark.parametrize("xs", [CRITICAL, SAMPLE], ids=["critical", "random"])
 def test_round_f16_matches_numpy(oracle_mod, xs):
     _assert_same_rounding(oracle_mod.round_f32(xs, "fp16"), _numpy_f16_bits(xs), xs, "fp16")
+
+
+def test_round_exhaustive_every_binary32(oracle_mod):
+    """All 2^32 binary32 patterns through both of the oracle's rounding converters, against
+    torch's bfloat16 and float16 casts (IEEE round to nearest even, subnormals kept, overflow
+    to infinity); NaN inputs must give NaN."""
+    chunk = 1 << 24
+
+    def check(i):
+        x = np.arange(i * chunk, (i + 1) * chunk, dtype=np.uint64).astype(np.uint32)
+        x = x.view(np.float32)
+        nan = np.isnan(x)
+        bad = 0
+        for fmt, tdt in (("bf16", torch.bfloat16), ("fp16", torch.float16)):
+            got = oracle_mod.round_f32(x, fmt)
+            want = torch.from_numpy(x).to(tdt).view(torch.int16).numpy().view(np.uint16)
+            bad += int((~((got == want) | nan)).sum())
+            exp_mask, man_mask = (0x7F80, 0x007F) if fmt == "bf16" else (0x7C00, 0x03FF)
+            g = got[nan]
+            bad += int((~(((g & exp_mask) == exp_mask) & ((g & man_mask) != 0))).sum())
+        return bad
+
+    with ThreadPoolExecutor(max_workers=8) as pool:
+        mismatches = sum(pool.map(check, range((1 << 32) // chunk)))
+    assert mismatches == 0
 
 
 def test_critical_set_covers_every_exponent():
