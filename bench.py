@@ -685,6 +685,10 @@ def _pmc_by_kernel(d: str, counter: str):
     return vals
 
 
+# The plain-sum workload whose counters the pmc mode also collects (80 MiB per partial).
+PMC_SUM = {"W": 4, "M": 5120, "H": 8192}
+
+
 def summarize_pmc(fetch_dir: str, write_dir: str) -> str:
     """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the norm kernel, scaled by what the same
     counters read for torch's device copy of COPY_CAL_BYTES (reads and writes that many bytes)."""
@@ -732,6 +736,27 @@ def summarize_pmc(fetch_dir: str, write_dir: str) -> str:
         "",
         "traffic_json: " + json.dumps(data),
     ]
+    # The plain sum on the 80 MiB payload, when the run holds it.
+    sw = PMC_SUM
+    is_sum = lambda k: re.search(r"ar_sum_kernel<arf::Bf16, %d, " % sw["W"], k) is not None
+    if any(is_sum(k) for k in fetch) and any(is_sum(k) for k in write):
+        ks, f_sum, m1 = pick(fetch, is_sum)
+        _, w_sum, m2 = pick(write, is_sum)
+        s_read = sw["W"] * sw["M"] * sw["H"] * 2
+        s_write = sw["M"] * sw["H"] * 2
+        sf, swb = f_sum * 1024.0 * f_factor, w_sum * 1024.0 * w_factor
+        lines += [
+            "",
+            "sum kernel (W=%d, M=%d, H=%d bf16, 80 MiB per partial): `%s` (%d + %d dispatches)" % (
+                sw["W"], sw["M"], sw["H"], re.sub(r"\(.*", "", ks), m1, m2),
+            "",
+            "| counter | sum kernel KiB/dispatch | scale | scaled bytes | algorithmic bytes | ratio |",
+            "|---|---|---|---|---|---|",
+            "| FETCH_SIZE | %.0f | %.4f | %.0f | %d | %.3f |" % (f_sum, f_factor, sf, s_read,
+                                                            sf / s_read),
+            "| WRITE_SIZE | %.0f | %.4f | %.0f | %d | %.3f |" % (w_sum, w_factor, swb, s_write,
+                                                            swb / s_write),
+        ]
     return "\n".join(lines)
 
 
@@ -800,8 +825,18 @@ def main():
         for i in range(max(2, args.steps)):
             case.call(i, h)
         torch.cuda.synchronize()
+        R = case.R
+        del case
+        torch.cuda.empty_cache()
+        # The plain sum on the largest payload (W = 4 partials of 80 MiB), the same way.
+        sw = PMC_SUM
+        case = Case(ar, torch, "sum", sw["W"], sw["M"], sw["H"], dist=(0.0, 0.5))
+        for i in range(max(2, args.steps)):
+            case.call(i, h)
+        torch.cuda.synchronize()
         print(json.dumps({"mode": "pmc", "copy_bytes": COPY_CAL_BYTES, "norm_calls":
-                          max(2, args.steps), "rotation_sets": case.R}))
+                          max(2, args.steps), "rotation_sets": R, "sum_calls": max(2, args.steps),
+                          "sum_rotation_sets": case.R}))
         return 0
 
     box = box_facts(torch, ar)

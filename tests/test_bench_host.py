@@ -60,3 +60,45 @@ def test_sweep_trace_summary(tmp_path):
     assert "| 4.20 |" in by["kARResidualRMSNorm, split rows"]
     assert "| 32 | 4128768 | 3 | 1.50 |" in by["kAllReduce"]
     assert os.path.exists(bj)
+
+
+def _counters(path, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for r in rows:
+            w.writerow(r)
+
+
+def test_counter_summary_scales_by_the_copy(tmp_path):
+    """Counters are scaled by what they read for a copy of known size; the headline's traffic
+    line and the 80 MiB sum's table come out in bytes."""
+    norm = "void arf::ar_norm_kernel<arf::Bf16, 8, 2, true, arf::StreamSource, false>(...)"
+    summ = "void arf::ar_sum_kernel<arf::Bf16, 4, 1, false, arf::StreamSource>(...)"
+    copy = "__amd_rocclr_copyBuffer.kd"
+    kib = 1024.0
+    copy_fetch = bench.COPY_CAL_BYTES / 2 / kib            # the fetch counter reads half
+    copy_write = bench.COPY_CAL_BYTES / kib
+    norm_read, norm_write = 9 * 2048 * 7168 * 2, 2 * 2048 * 7168 * 2
+    sum_read, sum_write = 4 * 5120 * 8192 * 2, 5120 * 8192 * 2
+    fetch = [dict(Kernel_Name=copy, Counter_Name="FETCH_SIZE", Counter_Value=copy_fetch),
+             dict(Kernel_Name=norm, Counter_Name="FETCH_SIZE", Counter_Value=norm_read / 2 / kib),
+             dict(Kernel_Name=summ, Counter_Name="FETCH_SIZE", Counter_Value=sum_read / 2 / kib)]
+    write = [dict(Kernel_Name=copy, Counter_Name="WRITE_SIZE", Counter_Value=copy_write),
+             dict(Kernel_Name=norm, Counter_Name="WRITE_SIZE", Counter_Value=norm_write / kib),
+             dict(Kernel_Name=summ, Counter_Name="WRITE_SIZE", Counter_Value=sum_write / kib)]
+    fd, wd = tmp_path / "f", tmp_path / "w"
+    fd.mkdir()
+    wd.mkdir()
+    _counters(fd / "fetch_counter_collection.csv", fetch)
+    _counters(wd / "write_counter_collection.csv", write)
+    out = bench.summarize_pmc(str(fd), str(wd))
+    data = json.loads([x for x in out.splitlines() if x.startswith("traffic_json:")][0]
+                      .split(":", 1)[1])
+    assert data["traffic_bytes"] == norm_read + norm_write
+    assert data["fetch_factor"] == 2.0 and data["write_factor"] == 1.0
+    rows = [x for x in out.splitlines() if x.startswith("| FETCH_SIZE") or
+            x.startswith("| WRITE_SIZE")]
+    assert len(rows) == 4, out                            # norm and sum tables
+    assert rows[2].endswith("| %d | 1.000 |" % sum_read) and "%d" % sum_read in rows[2]
+    assert rows[3].endswith("| %d | 1.000 |" % sum_write)
