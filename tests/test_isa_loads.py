@@ -7,7 +7,11 @@ trip (`load, s_waitcnt vmcnt(0), load, ...`), correct but up to 2x slower, and t
 compare results cannot see that. This test compiles the norm-kernel shapes the launch planner
 picks for rows of whole vectors up to H = 8192 (one or two 16-byte vectors per thread with one
 chain per batch: W <= 8, and W = 16 with one vector) for the three element types, and asserts
-that no full wait (`s_waitcnt vmcnt(0)`) falls between two of a kernel's streaming loads.
+that no full wait (`s_waitcnt vmcnt(0)`) falls between two of a kernel's streaming loads. For
+the sum kernel it compiles every (W, vectors per thread) and checks its loop-free path (kernel
+entry to the first store): whole rank batches only, with exactly one full wait between
+consecutive batches and none inside one (16 loads per batch, 8 once a thread holds 32 or more
+binary32 values).
 """
 import os
 import re
@@ -24,14 +28,62 @@ SHAPES = [(w, v) for w in (1, 2, 4, 8) for v in (1, 2)] + [(16, 1)]
 TYPES = ("Bf16", "F16", "F32")
 
 
+SUM_W = (1, 2, 4, 8, 16, 32, 64)
+SUM_U = (1, 2, 4)
+KVEC = {"Bf16": 8, "F16": 8, "F32": 4}
+
+
 def _source() -> str:
     refs = []
     for t in TYPES:
         for w, v in SHAPES:
             refs.append("reinterpret_cast<const void*>(&arf::ar_norm_kernel<arf::%s, %d, %d, true>)"
                         % (t, w, v))
+        for w in SUM_W:
+            for u in SUM_U:
+                refs.append("reinterpret_cast<const void*>(&arf::ar_sum_kernel<arf::%s, %d, %d, "
+                            "true>)" % (t, w, u))
     return ('#include "ar_kernels.hpp"\n'
-            "const void* const kNormKernels[] = {\n  " + ",\n  ".join(refs) + "};\n")
+            "const void* const kKernels[] = {\n  " + ",\n  ".join(refs) + "};\n")
+
+
+def _sum_batch_loads(W: int, U: int, kvec: int) -> int:
+    """Streaming loads per rank batch of the sum kernel by design: ranks per batch x U, with 16
+    loads per batch, 8 once a thread holds 32 or more binary32 values."""
+    max_loads = 8 if U * kvec >= 32 else 16
+    return max(1, min(max_loads // U, W)) * U
+
+
+def _sum_fast_path_waits(asm: str) -> dict:
+    """Per sum kernel symbol: (streaming loads, full waits between two of them) from the kernel
+    entry to its first store (the loop-free path for a chunk wholly in range)."""
+    out, name, done = {}, None, False
+    for line in asm.splitlines():
+        m = re.match(r"^(_Z\S*ar_sum_kernel\S*):", line)
+        if m:
+            name, done = m.group(1), False
+            out[name] = [0, 0, False]
+            continue
+        if name is None or done:
+            if "s_endpgm" in line:
+                name = None
+            continue
+        r = out[name]
+        if "global_store" in line:
+            done = True
+        elif "global_load" in line and " nt" in line:
+            if r[2]:
+                r[1] += 1
+                r[2] = False
+            r[0] += 1
+        elif "s_waitcnt" in line and "vmcnt(0)" in line and r[0] > 0:
+            r[2] = True
+    return {k: (v[0], v[1]) for k, v in out.items()}
+
+
+def _sum_symbol(t: str, w: int, u: int) -> str:
+    tn = {"Bf16": "4Bf16", "F16": "3F16", "F32": "3F32"}[t]
+    return "_ZN3arf13ar_sum_kernelINS_%sELi%dELi%dELb1ENS_12StreamSourceEEE" % (tn, w, u)
 
 
 def _waits_between_streaming_loads(asm: str) -> dict:
@@ -80,6 +132,23 @@ def norm_asm():
 def test_every_planned_shape_is_compiled(norm_asm):
     waits = _waits_between_streaming_loads(norm_asm)
     assert len(waits) == len(TYPES) * len(SHAPES), sorted(waits)
+    assert len(_sum_fast_path_waits(norm_asm)) == len(TYPES) * len(SUM_W) * len(SUM_U)
+
+
+def test_sum_fast_path_waits_only_between_rank_batches(norm_asm):
+    got = _sum_fast_path_waits(norm_asm)
+    bad = []
+    for t in TYPES:
+        for w in SUM_W:
+            for u in SUM_U:
+                sym = [k for k in got if k.startswith(_sum_symbol(t, w, u))]
+                assert len(sym) == 1, (t, w, u, sym)
+                nt, waits = got[sym[0]]
+                per_batch = _sum_batch_loads(w, u, KVEC[t])
+                # Whole batches only, and one full wait between consecutive batches.
+                if nt == 0 or nt % per_batch or waits != nt // per_batch - 1:
+                    bad.append((t, w, u, nt, per_batch, waits))
+    assert not bad, "(type, W, U, loads, loads per batch, full waits): %s" % bad
 
 
 def test_no_full_wait_between_streaming_loads(norm_asm):
