@@ -179,3 +179,15 @@ def test_rmsnorm_special_values(oracle_mod, H, dtype):
     torch.cuda.synchronize()
     want = oracle_mod.rmsnorm(host_np(x), gam.numpy(), 1e-6, dtype)
     assert_norm_close(host_np(y.cpu()), want, dtype)
+
+
+# The residual sum at sizes its launch plan covers with one resident round of 256-thread blocks
+# (W + 1 <= 8 operands: one vector per thread), whole rows and odd widths with an element tail.
+ROUND = [(1, 128, 7168), (2, 128, 7168), (4, 128, 7168), (2, 100, 7170), (4, 57, 7169)]
+
+
+@pytest.mark.parametrize("W,M,H", ROUND, ids=["W%d-M%d-H%d" % c for c in ROUND])
+def test_unfused_resident_round_sizes(oracle_mod, W, M, H):
+    print("case unfused", W, M, H, flush=True)
+    parts, res, gam = synth.custom(W, M, H, "bf16", seed=W * 7 + M + H)
+    _check_unfused(oracle_mod, parts, res, gam, 1e-6, "bf16")
