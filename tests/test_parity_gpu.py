@@ -265,29 +265,32 @@ def test_norm_vectors_per_thread_branches(oracle_mod, W, vpt, dtype):
 
 # ---- the sum's one-round launch shapes at every world size ----------------------------------------
 
-ROUND_CASES = [(2, 128, 7168), (4, 128, 7168), (4, 127, 7169), (2, 64, 7168),
-               (8, 511, 7169), (16, 512, 7168), (32, 512, 7168), (64, 512, 7168),
-               (16, 512, 8192), (64, 450, 7173)]
+ROUND_CASES = [(2, 128, 7168, "bf16"), (4, 128, 7168, "bf16"), (4, 127, 7169, "bf16"),
+               (2, 64, 7168, "bf16"), (8, 511, 7169, "bf16"), (16, 512, 7168, "bf16"),
+               (32, 512, 7168, "bf16"), (64, 512, 7168, "bf16"), (16, 512, 8192, "bf16"),
+               (64, 450, 7173, "bf16"), (4, 64, 7168, "fp32"), (8, 256, 7168, "fp32"),
+               (32, 255, 7171, "fp32"), (2, 100, 7170, "fp16"), (16, 512, 8192, "fp16")]
 
 
-@pytest.mark.parametrize("W,M,H", ROUND_CASES, ids=["W%d-M%d-H%d" % c for c in ROUND_CASES])
-def test_sum_resident_round_shapes(oracle_mod, W, M, H):
+@pytest.mark.parametrize("W,M,H,dtype", ROUND_CASES,
+                         ids=["W%d-M%d-H%d-%s" % c for c in ROUND_CASES])
+def test_sum_resident_round_shapes(oracle_mod, W, M, H, dtype):
     """Sizes that the planner covers with one resident round of 256-thread blocks (one vector
     per thread for W <= 8, four for W >= 8), odd widths leaving an element-wise tail; the whole
     output against the oracle.  Inputs are drawn on the GPU by torch's seeded generator."""
-    cfg = ar.ar_launch_config(ar.PATTERN_ALLREDUCE, W, M, H, ar.DTYPE_BF16)
-    print("case", W, M, H, cfg, flush=True)
+    tdt = TD[dtype]
+    cfg = ar.ar_launch_config(ar.PATTERN_ALLREDUCE, W, M, H, ar.dtype_code(tdt))
+    print("case", W, M, H, dtype, cfg, flush=True)
     assert cfg["threads_per_block"] == 256 and cfg["vecs_per_thread"] in (1, 4)
     g = torch.Generator(device="cuda")
     g.manual_seed(W * 1000 + M)
-    parts = [torch.empty((M, H), dtype=torch.bfloat16, device="cuda").normal_(0.0, 1.0,
-                                                                              generator=g)
+    parts = [torch.empty((M, H), dtype=tdt, device="cuda").normal_(0.0, 1.0, generator=g)
              for _ in range(W)]
     out = torch.empty_like(parts[0])
     ar.ar_sum(parts, out)
     torch.cuda.synchronize()
-    want = oracle_mod.ar_sum([host_np(p.cpu()) for p in parts], "bf16")
-    assert_bit_exact(host_np(out.cpu()), want, "bf16", "out")
+    want = oracle_mod.ar_sum([host_np(p.cpu()) for p in parts], dtype)
+    assert_bit_exact(host_np(out.cpu()), want, dtype, "out")
 
 
 # ---- many ranks at many rows: one vector per thread over the whole row -----------------------------
