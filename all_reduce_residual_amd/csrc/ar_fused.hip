@@ -175,7 +175,13 @@ void plan_norm(int W, int64_t M, int64_t H, int dtype, int cu, ar_launch_cfg_t* 
     // H = 4096: one wave of 8 vectors per thread per row, 13 % faster than 512 lanes; at
     // W = 4 the 512-lane shape stays ahead, measured).
     int64_t target = 512;
-    if (W <= 2) target = std::max<int64_t>(64, 512 / std::max<int64_t>(1, M / cu));
+    const int64_t rows_per_cu = M / cu;
+    // Two partials with 16-bit rows at 12 or more rows per CU: the shape of W >= 4 again (up
+    // to 512 lanes); the narrower rows below lost there by 1-14 % (W = 2, M = 3072 ... 8192;
+    // H = 8192 fp16 M = 4096: 61.7 -> 55.4 us, H = 4096 M = 8192: 62.1 -> 54.4 us).
+    const bool wide_again = W == 2 && elem_size(dtype) == 2 && rows_per_cu >= 12;
+    if (W <= 2 && !wide_again)
+      target = std::max<int64_t>(64, 512 / std::max<int64_t>(1, rows_per_cu));
     // Many ranks at eight or more rows per CU (16-bit types): one vector per thread over the
     // whole row (up to 1024 lanes).  A thread's rank batches then hold one chain instead of two,
     // half the round trips per row, and the other rows on the CU keep it busy (W = 32 / 64,
@@ -190,7 +196,10 @@ void plan_norm(int W, int64_t M, int64_t H, int dtype, int cu, ar_launch_cfg_t* 
     // except for a single tensor (W = 1, the RMSNorm step alone) once rows outnumber CUs
     // eightfold, where 8 vectors per thread stay faster despite the idle slots (H = 7168,
     // M = 2048: 13.5 -> 10.6 us; at M <= 4 rows per CU halving measured 4-11 % faster).
-    const bool keep_wide = W == 1 && M >= int64_t(cu) * 8;
+    // Two partials with 16-bit rows from 4 rows per CU on keep them too (W = 2, H = 7168 bf16,
+    // M = 1024 / 2048: 14.7 -> 12.7 / 28.2 -> 26.3 us; binary32 rows lost 7-10 % that way).
+    const bool keep_wide = (W == 1 && M >= int64_t(cu) * 8) ||
+                           (W == 2 && elem_size(dtype) == 2 && rows_per_cu >= 4);
     while (!keep_wide && vpt > 1 &&
            round_up(ceil_div(V, vpt), 64) * vpt - V >= round_up(ceil_div(V, vpt), 64) &&
            round_up(ceil_div(V, vpt / 2), 64) <= 1024)

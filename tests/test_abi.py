@@ -109,9 +109,11 @@ def test_launch_config_invariants(cu):
                 assert t % L_ == 0 and R == t // L_
                 assert L_ * vpt >= H // _vec(dt), c                     # row covered
                 assert c["grid"] * R >= M                              # rows covered
-                # No thread is idle for a whole row when the row fits the block (except the
-                # single-tensor rows kept at 8 vectors per thread once M >= 8 x CUs).
-                assert L_ * vpt - H // _vec(dt) < L_ or L_ <= 64 or (W == 1 and M >= 8 * cu), c
+                # No thread is idle for a whole row when the row fits the block (except the rows
+                # kept at 8 vectors per thread: a single tensor once M >= 8 x CUs, two 16-bit
+                # partials once M >= 4 x CUs).
+                kept = (W == 1 and M >= 8 * cu) or (W == 2 and dt != FP32 and M // cu >= 4)
+                assert L_ * vpt - H // _vec(dt) < L_ or L_ <= 64 or kept, c
 
 
 def test_launch_config_headline_shapes():
@@ -159,6 +161,24 @@ def test_launch_config_many_ranks_many_rows():
     assert shape(16, 2048) == (448, 2)
     assert shape(32, 2048, 4096, FP32) == (512, 2)
     assert shape(32, 640, cu=80) == (896, 1)              # the bound moves with the CU count
+
+
+def test_launch_config_two_partials_by_rows_per_cu():
+    """W = 2: rows shrink with the rows per CU and keep 8 vectors per thread from 4 rows per CU
+    (16-bit), then return to the W >= 4 shape from 12 rows per CU (16-bit); binary32 and a
+    single tensor keep the narrow rows."""
+    def shape(W, M, H=7168, dt=BF16, cu=256):
+        c = ar.ar_launch_config(RMS, W, M, H, dt, cu_count=cu)
+        return c["threads_per_block"], c["vecs_per_thread"]
+    assert shape(2, 512) == (256, 4)                      # 2 rows per CU: halved, no idle slot
+    assert shape(2, 1024) == (128, 8)                     # 4: 8 vectors kept (896 of 1024 slots)
+    assert shape(2, 2048) == (128, 8)
+    assert shape(2, 2048, 4096) == (64, 8)
+    assert shape(2, 3072) == (448, 2)                     # 12: the W >= 4 shape
+    assert shape(2, 8192, 4096) == (512, 1)
+    assert shape(2, 4096, 8192, FP16) == (512, 2)
+    assert shape(2, 4096, 3584, FP32) == (256, 4)         # binary32: narrow rows, halved
+    assert shape(1, 4096) == (128, 8)                     # single tensor: unchanged
 
 
 def test_launch_config_rejects():
