@@ -102,3 +102,30 @@ def test_counter_summary_scales_by_the_copy(tmp_path):
     assert len(rows) == 4, out                            # norm and sum tables
     assert rows[2].endswith("| %d | 1.000 |" % sum_read) and "%d" % sum_read in rows[2]
     assert rows[3].endswith("| %d | 1.000 |" % sum_write)
+
+
+def test_headline_parity_check_accepts_and_rejects(oracle_mod):
+    """The CPU leg's spot check passes the oracle's own rows and rejects a flipped residual_out
+    bit or a norm_out 2 ulp away."""
+    import numpy as np
+    import synth
+    parts, res, gam = synth.custom(2, 3, 256, "bf16", seed=5)
+    hp = [synth.storage_numpy(p) for p in parts]
+    hr = synth.storage_numpy(res)
+    ro, no = oracle_mod.ar_residual_rmsnorm(hp, hr, gam.numpy(), 1e-6, "bf16")
+    sample = {"rows": [0, 1, 2], "eps": 1e-6, "dtype": "bf16", "parts": hp, "residual": hr,
+              "gamma": gam.numpy(), "residual_out": ro.copy(), "norm_out": no.copy()}
+    assert bench.check_headline_parity(sample)["norm_out_max_ulp"] == 0
+    bad = dict(sample, residual_out=ro ^ np.uint16(1))
+    try:
+        bench.check_headline_parity(bad)
+        raise RuntimeError("a flipped residual_out bit was accepted")
+    except AssertionError:
+        pass
+    off = no.copy()
+    off[1, 7] = off[1, 7] + 2 if (off[1, 7] & 0x7FFF) < 0x7F00 else off[1, 7] - 2
+    try:
+        bench.check_headline_parity(dict(sample, norm_out=off))
+        raise RuntimeError("a norm_out 2 ulp away was accepted")
+    except AssertionError:
+        pass
