@@ -397,13 +397,18 @@ int check_split_cfg(int64_t M, int64_t H, int dtype, const ar_split_cfg_t* c) {
 //  * one vector per thread, and the narrowest segments (64 lanes, one wave) that keep the grid
 //    within one block per CU: M S <= CUs (M <= 16 at H = 7168: 14 segments, 4.7 -> 3.5 us);
 //  * at least 4 segments, or 2 for rows of >= 192 KiB: with 2 the gain ranged from -4 % (W = 8,
-//    H = 7168, M = 128) to +11 % (W = 64, H = 4096).
+//    H = 7168, M = 128) to +11 % (W = 64, H = 4096); or 2 for rows of >= 112 KiB while the
+//    grid of two segments per row leaves an eighth of the CUs free (M <= 112 on 256 CUs):
+//    W = 8, H = 7168 / 8192, M = 80 ... 112: 0-13 % faster (interleaved A/B), W = 4 rows
+//    (70-80 KiB) never gained.
 bool plan_split(int W, int64_t M, int64_t H, int dtype, int cu, ar_split_cfg_t* c) {
   const int64_t V = H / (kVecBytes / elem_size(dtype));
   const int64_t row_bytes = int64_t(W + 1) * H * elem_size(dtype);
   if (M < 1 || row_bytes < (int64_t(64) << 10)) return false;
   const int64_t s_cap = std::min<int64_t>(arf::kSplitSlots, int64_t(cu) / M);
-  const int64_t s_min = row_bytes >= (int64_t(192) << 10) ? 2 : 4;
+  const bool two_ok = row_bytes >= (int64_t(192) << 10) ||
+                      (row_bytes >= (int64_t(112) << 10) && M * 16 <= int64_t(cu) * 7);
+  const int64_t s_min = two_ok ? 2 : 4;
   if (s_cap < s_min) return false;
   int threads = 64;
   while (ceil_div(V, threads) > s_cap && threads < arf::kMaxThreads) threads *= 2;

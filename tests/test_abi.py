@@ -322,6 +322,13 @@ def test_split_config_invariants():
         assert (S - 1) * t * v < V <= S * t * v
         assert M * S < 2 ** 31 and c["max_polls"] > 0
     assert ar.ar_split_config(8, 4096, 7168, BF16, 256)["segments"] == 0
+    # Two segments: rows >= 192 KiB up to a full grid, rows >= 112 KiB (W = 8 at H = 7168) while
+    # an eighth of the CUs stays free; W = 4 rows never.
+    assert ar.ar_split_config(8, 112, 7168, BF16, 256)["segments"] == 2
+    assert ar.ar_split_config(8, 96, 8192, FP16, 256)["segments"] == 2
+    assert ar.ar_split_config(8, 128, 7168, BF16, 256)["segments"] == 0
+    assert ar.ar_split_config(16, 128, 7168, BF16, 256)["segments"] == 2
+    assert ar.ar_split_config(4, 96, 8192, BF16, 256)["segments"] == 0
     assert ar.ar_split_config(8, 1, 7168, BF16, 256)["segments"] >= 2
     with pytest.raises(ar.ArError) as e:
         ar.ar_split_config(12, 4, 7168, BF16, 256)

@@ -85,7 +85,8 @@ def test_wide_hidden_decode_sizes_planned(oracle_mod, M):
 
 
 PLANNED = [(16, 4, 8192, "fp16"), (4, 32, 8192, "bf16"), (64, 2, 4096, "bf16"),
-           (32, 3, 8192, "fp32"), (16, 100, 8192, "bf16"), (8, 64, 7168, "fp16")]
+           (32, 3, 8192, "fp32"), (16, 100, 8192, "bf16"), (8, 64, 7168, "fp16"),
+           (8, 80, 7168, "bf16"), (8, 112, 8192, "fp16")]
 
 
 @pytest.mark.parametrize("W,M,H,dtype", PLANNED, ids=["W%d-M%d-H%d-%s" % c for c in PLANNED])
