@@ -140,6 +140,11 @@ def test_launch_config_sum_resident_round():
     assert shape(16, 128) == (64, 1, 1792)         # W >= 16: one vector per thread is mixed
     assert shape(8, 2048) == (64, 1, 28672)        # beyond one round
     assert shape(8, 8) == (64, 2, 56)              # too few blocks for the round
+    # 16 or more ranks: the 4-vector blocks up to 8 blocks per CU.
+    assert shape(32, 2048) == (256, 4, 1792)
+    assert shape(16, 1024, 8192) == (256, 4, 1024)
+    assert shape(64, 3072) == (64, 1, 43008)        # beyond 8 blocks per CU
+    assert shape(8, 1024) == (64, 1, 14336)         # W = 8: up to 2 blocks per CU only
     # On a GPU with fewer CUs the bands move with the CU count.
     c = ar.ar_launch_config(SUM, 8, 128, 7168, BF16, cu_count=80)
     assert (c["threads_per_block"], c["vecs_per_thread"]) == (64, 1)

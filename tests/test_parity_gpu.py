@@ -269,15 +269,17 @@ ROUND_CASES = [(2, 128, 7168, "bf16"), (4, 128, 7168, "bf16"), (4, 127, 7169, "b
                (2, 64, 7168, "bf16"), (8, 511, 7169, "bf16"), (16, 512, 7168, "bf16"),
                (32, 512, 7168, "bf16"), (64, 512, 7168, "bf16"), (16, 512, 8192, "bf16"),
                (64, 450, 7173, "bf16"), (4, 64, 7168, "fp32"), (8, 256, 7168, "fp32"),
-               (32, 255, 7171, "fp32"), (2, 100, 7170, "fp16"), (16, 512, 8192, "fp16")]
+               (32, 255, 7171, "fp32"), (2, 100, 7170, "fp16"), (16, 512, 8192, "fp16"),
+               (16, 1024, 8192, "bf16"), (32, 600, 7173, "fp16")]
 
 
 @pytest.mark.parametrize("W,M,H,dtype", ROUND_CASES,
                          ids=["W%d-M%d-H%d-%s" % c for c in ROUND_CASES])
 def test_sum_resident_round_shapes(oracle_mod, W, M, H, dtype):
-    """Sizes that the planner covers with one resident round of 256-thread blocks (one vector
-    per thread for W <= 8, four for W >= 8), odd widths leaving an element-wise tail; the whole
-    output against the oracle.  Inputs are drawn on the GPU by torch's seeded generator."""
+    """Sizes that the planner covers with 256-thread blocks (one vector per thread for W <= 8
+    in one resident round, four for W >= 8 up to 2 or, from 16 ranks, 8 blocks per CU), odd
+    widths leaving an element-wise tail; the whole output against the oracle.  Inputs are
+    drawn on the GPU by torch's seeded generator."""
     tdt = TD[dtype]
     cfg = ar.ar_launch_config(ar.PATTERN_ALLREDUCE, W, M, H, ar.dtype_code(tdt))
     print("case", W, M, H, dtype, cfg, flush=True)
