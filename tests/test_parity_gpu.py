@@ -324,3 +324,60 @@ def test_many_ranks_many_rows_sampled(oracle_mod, W, M, H, dtype):
         gam.cpu().numpy(), 1e-6, dtype)
     assert_bit_exact(host_np(ro[rows].cpu()), want_ro, dtype, "residual_out")
     assert_norm_close(host_np(no[rows].cpu()), want_no, dtype)
+
+
+# ---- seeded random shapes through every entry point, in the launch shapes the library picks -----
+
+def _random_cases(n=36, seed=20261202):
+    """(W, M, H, dtype) drawn from a fixed seed: every supported W and type, M log-uniform over
+    1 ... 1536 rows, H any whole number of 16-byte vectors up to the type's limit, capped at
+    6 Mi summed elements so the oracle stays quick."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        W = int(rng.choice([1, 2, 4, 8, 16, 32, 64]))
+        dtype = str(rng.choice(["bf16", "fp16", "fp32"]))
+        vec = 4 if dtype == "fp32" else 8
+        max_v = (32768 if dtype == "fp32" else 65536) // vec
+        V = int(np.exp(rng.uniform(0.0, np.log(max_v))))
+        M = int(np.exp(rng.uniform(0.0, np.log(1536))))
+        H = max(1, V) * vec
+        if (W + 1) * M * H > 6 << 20:
+            continue
+        cases.append((W, M, H, dtype))
+    return cases
+
+
+RANDOM = _random_cases()
+
+
+@pytest.mark.parametrize("W,M,H,dtype", RANDOM, ids=["W%d-M%d-H%d-%s" % c for c in RANDOM])
+def test_random_shapes_every_entry_point(oracle_mod, W, M, H, dtype):
+    """ar_sum, ar_residual_rmsnorm, its workspace form and its two-kernel form, each in the launch
+    shape the library plans for the shape, against one oracle result."""
+    print("case", W, M, H, dtype, flush=True)
+    parts, res, gam = synth.custom(W, M, H, dtype, seed=W * 7919 + M * 31 + H)
+    d_parts = [dev(p) for p in parts]
+    d_res, d_gam = dev(res), dev(gam)
+    h_parts = [host_np(p) for p in parts]
+    want_out = oracle_mod.ar_sum(h_parts, dtype)
+    want_ro, want_no = oracle_mod.ar_residual_rmsnorm(h_parts, host_np(res), gam.numpy(), 1e-6,
+                                                      dtype)
+    out = torch.empty_like(d_res)
+    ar.ar_sum(d_parts, out)
+    ws = ar.new_workspace(M, "cuda")
+    forms = {"fused": lambda ro, no: ar.ar_residual_rmsnorm(d_parts, d_res, d_gam, 1e-6, ro, no),
+             "workspace": lambda ro, no: ar.ar_residual_rmsnorm_ws(d_parts, d_res, d_gam, 1e-6,
+                                                                   ro, no, ws),
+             "two-kernel": lambda ro, no: ar.ar_residual_rmsnorm_unfused(d_parts, d_res, d_gam,
+                                                                         1e-6, ro, no)}
+    got = {}
+    for name, call in forms.items():
+        ro, no = torch.empty_like(d_res), torch.empty_like(d_res)
+        call(ro, no)
+        got[name] = (ro, no)
+    torch.cuda.synchronize()
+    assert_bit_exact(host_np(out.cpu()), want_out, dtype, "out")
+    for name, (ro, no) in got.items():
+        assert_bit_exact(host_np(ro.cpu()), want_ro, dtype, name + " residual_out")
+        assert_norm_close(host_np(no.cpu()), want_no, dtype, name + " norm_out")
