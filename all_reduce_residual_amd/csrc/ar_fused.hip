@@ -847,6 +847,24 @@ int run_lamport_norm(void* rbuf, int W, int64_t M, int64_t H, int dtype, const v
     cfg.rows_per_block = 1;
     cfg.grid = cap_grid(M);
   }
+  // Few rows (a quarter of the CUs or fewer hold one): each row's block is latency-bound, and a
+  // polled batch holds half the stream source's loads, so two vectors per thread cost W = 8 two
+  // round trips where one vector costs one.  Take the fewest vectors per thread (1 or 2) that
+  // one block of up to 1024 threads allows: H = 7168 bf16, M = 1 ... 48: 5-28 % faster at
+  // W = 2 ... 64 (W = 8: 7.8 -> 6.2 us at M = 1); two instead of four at H = 16384: 13-35 %
+  // (W = 64, M = 2: 119 -> 78 us); binary32 W = 8 M = 32: 16.5 -> 12.4 us.  From 128 rows on
+  // the planned shape stays ahead (W = 8: 12.8 against 15.6 us).
+  if (M * 4 <= cu && cfg.rows_per_block == 1) {
+    const int64_t V = H / (kVecBytes / elem_size(dtype));
+    const int v = round_up(V, 64) <= 1024 ? 1 : 2;
+    const int64_t lanes = round_up(ceil_div(V, v), 64);
+    if (v < cfg.vecs_per_thread && lanes <= 1024) {
+      cfg.vecs_per_thread = v;
+      cfg.lanes_per_row = static_cast<int>(lanes);
+      cfg.threads_per_block = static_cast<int>(lanes);
+      cfg.grid = cap_grid(M);
+    }
+  }
   cfg.nt_store = 1;
   arf::LamportSource src{status, spin_limit ? spin_limit : kDefaultSpinLimit};
   hipStream_t s = static_cast<hipStream_t>(stream);

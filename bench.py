@@ -287,7 +287,7 @@ class LamportCase(Case):
                 raise RuntimeError("Lamport consumer failed: %s" % self.ar.status_string(st))
 
 
-def lamport_lines(ar, torch, W=8, H=7168, Ms=(128, 2048)) -> list:
+def lamport_lines(ar, torch, W=8, H=7168, Ms=(8, 128, 2048)) -> list:
     """hipGraph-replayed µs of the Lamport exchange steps (pushes + consumer, pushes alone)."""
     lines = []
     for m in Ms:

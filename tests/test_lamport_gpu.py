@@ -218,3 +218,32 @@ def test_wide_rows_and_many_rows(oracle_mod, W, M, H, dtype):
                                                       gam.numpy(), 1e-6, dtype)
     assert_bit_exact(host_np(ro.cpu()), want_ro, dtype, "lamport residual_out")
     assert_norm_close(host_np(no.cpu()), want_no, dtype, "lamport norm_out")
+
+
+FEW_ROWS = [(8, 1, 7168, "bf16"), (2, 64, 7168, "bf16"), (16, 48, 7168, "bf16"),
+            (64, 16, 7168, "bf16"), (32, 64, 8192, "fp16"), (8, 32, 7168, "fp32"),
+            (4, 7, 7176, "bf16"), (8, 3, 16376, "fp16")]
+
+
+@pytest.mark.parametrize("W,M,H,dtype", FEW_ROWS, ids=["W%d-M%d-H%d-%s" % c for c in FEW_ROWS])
+def test_few_rows_fewest_vectors_per_thread(oracle_mod, W, M, H, dtype):
+    """Few rows (a quarter of the CUs or fewer): the fused consumer runs one or two vectors per
+    thread over up to 1024 lanes, ragged widths (897 and 2047 vectors) included; then a second
+    round through the re-armed buffer."""
+    print("case", W, M, H, dtype, flush=True)
+    tdt = synth.TORCH_DTYPES[dtype]
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    rbuf = _new_rbuf(W, M, H, tdt)
+    for rnd in range(2):
+        parts, res, gam = synth.custom(W, M, H, dtype, seed=W * 31 + M + H + rnd)
+        for r, p in enumerate(parts):
+            ar.ar_lamport_push(dev(p), r, rbuf)
+        d_res = dev(res)
+        ro, no = torch.empty_like(d_res), torch.empty_like(d_res)
+        ar.ar_lamport_residual_rmsnorm(rbuf, d_res, dev(gam), 1e-6, ro, no, status)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0 and _empty(rbuf)
+        want_ro, want_no = oracle_mod.ar_residual_rmsnorm(
+            [host_np(p) for p in parts], host_np(res), gam.numpy(), 1e-6, dtype)
+        assert_bit_exact(host_np(ro.cpu()), want_ro, dtype, "lamport residual_out")
+        assert_norm_close(host_np(no.cpu()), want_no, dtype, "lamport norm_out")
