@@ -190,6 +190,15 @@ void plan_norm(int W, int64_t M, int64_t H, int dtype, int cu, ar_launch_cfg_t* 
     // M = 2048, H = 7168 bf16: 184 -> 170 / 350 -> 326 us; H = 8192 fp16 W = 32: 3 % faster).
     // At M <= 512, at W = 16 and for binary32 the two-vector rows stayed ahead (2-26 %).
     if (W >= 32 && elem_size(dtype) == 2 && M >= int64_t(cu) * 8) target = 1024;
+    // Binary32 rows of 1025 to 2048 vectors while a quarter of the CUs or fewer hold a row, or
+    // at eight or more rows per CU: two vectors per thread over up to 1024 lanes instead of four
+    // over up to 512 -- twice the waves per row, and a thread's rank batch (16 loads) spans 8
+    // ranks instead of 4.  H = 7168, W = 2 ... 64: M <= 64 2-14 % faster (W = 32, M = 16:
+    // 24.4 -> 21.0 us), M = 2048 / 4096 1-6.5 %; H = 5120 and 8192 alike.  Between the two
+    // (M = 128 ... 1024) it ranged from 9 % slower to 6 % faster.
+    if (elem_size(dtype) == 4 && V > 1024 && V <= 2048 &&
+        (M * 4 <= int64_t(cu) || M >= int64_t(cu) * 8))
+      target = 1024;
     vpt = 1;
     while (vpt < 8 && ceil_div(V, vpt) > target) vpt *= 2;
     while (vpt < 8 && round_up(ceil_div(V, vpt), 64) > 1024) vpt *= 2;

@@ -168,6 +168,29 @@ def test_launch_config_many_ranks_many_rows():
     assert shape(32, 640, cu=80) == (896, 1)              # the bound moves with the CU count
 
 
+
+def test_launch_config_binary32_rows_by_row_count():
+    """Binary32 rows of 1025-2048 vectors: two vectors per thread over up to 1024 lanes while a
+    quarter of the CUs or fewer hold a row, or from 8 rows per CU; four over up to 512 between,
+    and narrower rows keep their shapes."""
+    def shape(W, M, H=7168, cu=256):
+        c = ar.ar_launch_config(RMS, W, M, H, FP32, cu_count=cu)
+        return c["threads_per_block"], c["vecs_per_thread"]
+    assert shape(8, 1) == (896, 2)
+    assert shape(32, 64) == (896, 2)
+    assert shape(8, 65) == (448, 4)                       # over a quarter of the CUs
+    assert shape(8, 1024) == (448, 4)
+    assert shape(8, 2047) == (448, 4)
+    assert shape(8, 2048) == (896, 2)
+    assert shape(2, 2048, 8192) == (1024, 2)              # W = 2's narrow rows give way too
+    assert shape(8, 32, 5120) == (640, 2)
+    assert shape(8, 1, 4096) == (512, 2)                  # 1024 vectors: unchanged
+    assert shape(8, 1, 16384) == (512, 8)                 # 4096 vectors: unchanged
+    assert shape(8, 20, cu=80) == (896, 2)                # the bounds move with the CU count
+    assert shape(8, 21, cu=80) == (448, 4)
+    c = ar.ar_launch_config(RMS, 8, 1, 7168, BF16, cu_count=256)
+    assert (c["threads_per_block"], c["vecs_per_thread"]) == (448, 2)   # 16-bit: unchanged
+
 def test_launch_config_two_partials_by_rows_per_cu():
     """W = 2: rows shrink with the rows per CU and keep 8 vectors per thread from 4 rows per CU
     (16-bit), then return to the W >= 4 shape from 12 rows per CU (16-bit); binary32 and a

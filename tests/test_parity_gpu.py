@@ -381,3 +381,37 @@ def test_random_shapes_every_entry_point(oracle_mod, W, M, H, dtype):
     for name, (ro, no) in got.items():
         assert_bit_exact(host_np(ro.cpu()), want_ro, dtype, name + " residual_out")
         assert_norm_close(host_np(no.cpu()), want_no, dtype, name + " norm_out")
+
+
+# ---- binary32 rows of 1025-2048 vectors: two vectors per thread at few or many rows ---------------
+
+F32_ROWS = [(8, 1, 7168), (32, 64, 7168), (64, 16, 5120), (2, 40, 8192), (8, 2048, 7168),
+            (2, 2048, 8192)]
+
+
+@pytest.mark.parametrize("W,M,H", F32_ROWS, ids=["W%d-M%d-H%d" % c for c in F32_ROWS])
+def test_binary32_two_vector_rows(oracle_mod, W, M, H):
+    """The planned shape (up to 1024 lanes, two vectors per thread) against the oracle: every row
+    at few rows, sampled rows at 2048 (inputs drawn on the GPU by torch's seeded generator)."""
+    cfg = ar.ar_launch_config(ar.PATTERN_AR_RESIDUAL_RMSNORM, W, M, H, ar.dtype_code(torch.float32))
+    print("case", W, M, H, cfg, flush=True)
+    assert cfg["vecs_per_thread"] == 2 and cfg["lanes_per_row"] * 8 >= H
+    if M < 2048:
+        parts, res, gam = synth.custom(W, M, H, "fp32", seed=W * 17 + M + H)
+        run_rms_both(oracle_mod, parts, res, gam, 1e-6, "fp32")
+        return
+    g = torch.Generator(device="cuda")
+    g.manual_seed(W * 3 + M)
+    parts = [torch.empty((M, H), dtype=torch.float32, device="cuda").normal_(0.0, 1.0, generator=g)
+             for _ in range(W)]
+    res = torch.empty((M, H), dtype=torch.float32, device="cuda").normal_(0.0, 1.0, generator=g)
+    gam = torch.empty(H, dtype=torch.float32, device="cuda").uniform_(0.5, 1.5, generator=g)
+    ro, no = torch.empty_like(res), torch.empty_like(res)
+    ar.ar_residual_rmsnorm(parts, res, gam, 1e-6, ro, no)
+    torch.cuda.synchronize()
+    rows = torch.tensor([0, 1, 255, 256, 1023, 1024, M - 2, M - 1], device="cuda")
+    want_ro, want_no = oracle_mod.ar_residual_rmsnorm(
+        [host_np(p[rows].cpu()) for p in parts], host_np(res[rows].cpu()),
+        gam.cpu().numpy(), 1e-6, "fp32")
+    assert_bit_exact(host_np(ro[rows].cpu()), want_ro, "fp32", "residual_out")
+    assert_norm_close(host_np(no[rows].cpu()), want_no, "fp32")
