@@ -121,11 +121,13 @@ void plan_sum(int W, int64_t n, int dtype, int cu, ar_launch_cfg_t* c, int max_r
   const int64_t nvec = n / vec;
   // Single-wave blocks, one 16-byte vector per thread, one block per 64 vectors: the most
   // independent waves for the dispatcher to spread over the 256 CUs.  Small payloads (fewer
-  // than 16 such blocks per CU) do better with two vectors per thread and half the blocks.
+  // than 8 such blocks per CU) do better with two vectors per thread and half the blocks; from
+  // 8 to 16 blocks per CU one vector stayed ahead (W = 2 / 4 / 8, H = 7168: bf16 3-7.5 %,
+  // binary32 1.5-10 % faster in 17 of 18 cases).
   int threads = 64;
   // (Two vectors per thread only for W <= 8: beyond that the doubled loads and rank pointers no
   // longer fit the registers and spill.)
-  int u = (W <= 8 && ceil_div(nvec, threads) < int64_t(cu) * 16) ? 2 : 1;
+  int u = (W <= 8 && ceil_div(nvec, threads) < int64_t(cu) * 8) ? 2 : 1;
   // Mid-size payloads that one resident round of 3/4 to 2 blocks of 256 threads per CU covers
   // exactly: one launch round with no block scheduling behind it beats many single-wave blocks
   // (W = 8, H = 7168 bf16: M = 64 / 128 11 % and 8 % faster at one vector per thread, M = 512

@@ -140,6 +140,9 @@ def test_launch_config_sum_resident_round():
     assert shape(16, 128) == (64, 1, 1792)         # W >= 16: one vector per thread is mixed
     assert shape(8, 2048) == (64, 1, 28672)        # beyond one round
     assert shape(8, 8) == (64, 2, 56)              # too few blocks for the round
+    assert shape(8, 256) == (64, 1, 3584)          # 8-16 single-wave blocks per CU: one vector
+    assert shape(4, 160) == (64, 1, 2240)
+    assert shape(8, 16) == (64, 2, 112)            # under 8 blocks per CU: two vectors
     # 16 or more ranks: the 4-vector blocks up to 8 blocks per CU.
     assert shape(32, 2048) == (256, 4, 1792)
     assert shape(16, 1024, 8192) == (256, 4, 1024)

@@ -295,6 +295,23 @@ def test_sum_resident_round_shapes(oracle_mod, W, M, H, dtype):
     assert_bit_exact(host_np(out.cpu()), want, dtype, "out")
 
 
+SINGLE_WAVE = [(8, 256, 7168, "bf16"), (4, 160, 7171, "bf16"), (2, 200, 7168, "fp16"),
+               (8, 128, 7168, "fp32"), (8, 16, 7168, "bf16"), (4, 20, 7170, "fp32")]
+
+
+@pytest.mark.parametrize("W,M,H,dtype", SINGLE_WAVE,
+                         ids=["W%d-M%d-H%d-%s" % c for c in SINGLE_WAVE])
+def test_sum_single_wave_shapes(oracle_mod, W, M, H, dtype):
+    """Sizes the planner covers with single-wave blocks: one vector per thread from 8 blocks per
+    CU, two below (the last two cases), odd widths with an element-wise tail; whole output."""
+    tdt = TD[dtype]
+    cfg = ar.ar_launch_config(ar.PATTERN_ALLREDUCE, W, M, H, ar.dtype_code(tdt))
+    print("case", W, M, H, dtype, cfg, flush=True)
+    assert cfg["threads_per_block"] == 64
+    assert cfg["vecs_per_thread"] == (2 if M <= 20 else 1)
+    parts, _, _ = synth.custom(W, M, H, dtype, seed=W * 101 + M, with_norm=False)
+    run_sum_both(oracle_mod, parts, dtype)
+
 # ---- many ranks at many rows: one vector per thread over the whole row -----------------------------
 
 MANY = [(32, 2048, 7168, "bf16"), (64, 2048, 8192, "fp16")]
