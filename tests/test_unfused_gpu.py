@@ -146,6 +146,27 @@ def test_rmsnorm_matches_oracle(oracle_mod, M, H, dtype):
     assert_norm_close(host_np(y.cpu()), want, dtype)
 
 
+# Odd widths in the row kernel's planned shapes at many rows (8 or more per CU: blocks of at most
+# 192 threads, 128 with 8 vectors per thread) and at few rows (at most one per CU: the widest
+# block up to 1024 threads); the last case runs in place.
+ROW_PLAN = [(2048, 7170, "bf16", False), (2048, 2562, "fp16", False), (2048, 1539, "fp32", False),
+            (4096, 3074, "bf16", False), (8, 16386, "bf16", False), (64, 5122, "fp32", False),
+            (1, 7170, "fp16", False), (100, 6146, "bf16", False), (2048, 7170, "fp16", True)]
+
+
+@pytest.mark.parametrize("M,H,dtype,in_place", ROW_PLAN,
+                         ids=["M%d-H%d-%s%s" % (m, h, d, "-inplace" if i else "")
+                              for m, h, d, i in ROW_PLAN])
+def test_rmsnorm_planned_row_shapes(oracle_mod, M, H, dtype, in_place):
+    print("case rmsnorm rows", M, H, dtype, in_place, flush=True)
+    parts, _, gam = synth.custom(1, M, H, dtype, seed=5 * H + M)
+    x = dev(parts[0])
+    y = x if in_place else torch.empty_like(x)
+    ar.ar_rmsnorm(x, dev(gam), 1e-6, y)
+    torch.cuda.synchronize()
+    want = oracle_mod.rmsnorm(host_np(parts[0]), gam.numpy(), 1e-6, dtype)
+    assert_norm_close(host_np(y.cpu()), want, dtype)
+
 @pytest.mark.parametrize("H", [7168, 1001, 40001, 70001])
 def test_rmsnorm_in_place(oracle_mod, H):
     parts, _, gam = synth.custom(1, 6, H, "fp16", seed=H)
