@@ -588,16 +588,26 @@ int launch_rmsnorm(const void* x, int64_t M, int64_t H, int dtype, const float* 
       }
     }
     // At most one row per CU: the fewest vectors per thread that one block of up to 1024
-    // threads allows (more waves for the one row each CU holds).  Eight or more rows per CU:
-    // small blocks, at most 192 threads (128 with 8 vectors per thread), so more rows are in
-    // flight on each CU.  Interleaved A/B over 17 odd widths, 16-bit and binary32: M <= 128
-    // up to 23 % faster, never slower by more than 0.1 % (bf16 H = 16386, M = 8: 7.43 -> 5.69
-    // us); M = 2048 / 4096 5-29 % faster (bf16 H = 7170, M = 2048: 16.0 -> 13.5 us; fp16
-    // H = 5122: 13.9 -> 9.8 us).  At M = 512 the wide blocks were mixed (-17 ... +5 %).
-    if (M <= int64_t(cu) || M >= int64_t(cu) * 8) {
+    // threads allows (more waves for the one row each CU holds); two rows per CU: the same
+    // up to 704 threads.  Eight or more rows per CU: small blocks, at most 192 threads (128
+    // with 8 vectors per thread), so more rows are in flight on each CU.  Interleaved A/B over
+    // 17 odd widths, 16-bit and binary32: M <= 256 up to 23 % faster, never slower by more than
+    // 0.5 % (bf16 H = 16386, M = 8: 7.43 -> 5.69 us); M = 384 / 512 5-18 % (the 1024 bound
+    // there ranged from -17 to +5 %); M = 2048 / 4096 5-29 % (bf16 H = 7170, M = 2048:
+    // 16.0 -> 13.5 us; fp16 H = 5122: 13.9 -> 9.8 us).  From 3 to 7 rows per CU the 704 bound
+    // lost up to 39 %, so those keep the shape above.
+    int64_t cap = 0;  // 0: keep the shape above; -1: the small-block bound
+    if (M <= int64_t(cu)) {
+      cap = 1024;
+    } else if (M <= int64_t(cu) * 2) {
+      cap = 704;
+    } else if (M >= int64_t(cu) * 8) {
+      cap = -1;
+    }
+    if (cap != 0) {
       for (int k = 1; k <= 8; k *= 2) {
         const int64_t tk = round_up(ceil_div(nv, k), 64);
-        if (tk <= (M <= int64_t(cu) ? 1024 : (k == 8 ? 128 : 192))) {
+        if (tk <= (cap > 0 ? cap : (k == 8 ? 128 : 192))) {
           vpt = k;
           threads = tk;
           break;

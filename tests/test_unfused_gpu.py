@@ -148,10 +148,11 @@ def test_rmsnorm_matches_oracle(oracle_mod, M, H, dtype):
 
 # Odd widths in the row kernel's planned shapes at many rows (8 or more per CU: blocks of at most
 # 192 threads, 128 with 8 vectors per thread) and at few rows (at most one per CU: the widest
-# block up to 1024 threads); the last case runs in place.
+# block up to 1024 threads; two per CU: up to 704); one case runs in place.
 ROW_PLAN = [(2048, 7170, "bf16", False), (2048, 2562, "fp16", False), (2048, 1539, "fp32", False),
             (4096, 3074, "bf16", False), (8, 16386, "bf16", False), (64, 5122, "fp32", False),
-            (1, 7170, "fp16", False), (100, 6146, "bf16", False), (2048, 7170, "fp16", True)]
+            (1, 7170, "fp16", False), (100, 6146, "bf16", False), (2048, 7170, "fp16", True),
+            (512, 8194, "bf16", False), (384, 16386, "bf16", False), (500, 5122, "fp32", False)]
 
 
 @pytest.mark.parametrize("M,H,dtype,in_place", ROW_PLAN,
