@@ -556,8 +556,8 @@ int validate_rmsnorm(const void* x, int64_t M, int64_t H, int dtype, const float
   return AR_OK;
 }
 
-// Launches RMSNorm of x into y (validated arguments, M > 0): the row kernel in norm-only mode
-// when rows fit it, else the two-pass kernel for rows of any width.
+// Launches RMSNorm of x into y (validated arguments, M > 0): the fused kernel in norm-only mode
+// when rows fit it, else the row kernel for rows of any width.
 int launch_rmsnorm(const void* x, int64_t M, int64_t H, int dtype, const float* gamma, float eps,
                    void* y, hipStream_t s) {
   int cu = 0;
@@ -575,13 +575,16 @@ int launch_rmsnorm(const void* x, int64_t M, int64_t H, int dtype, const float* 
   } else {
     // One block per row, grid stride over rows (at most 8 blocks per CU).  A row spans at most
     // H / vec + 2 aligned vectors; the fewest vectors per thread (1, 2, 4 or 8) that keep the
-    // block at <= 512 threads (1024 for 8) hold the row in registers, else two passes.
+    // block at <= 512 threads (640 for 4, 1024 for 8) hold the row in registers, else two
+    // passes.  (Rows of 2049-2560 vectors: 4 vectors over up to 640 threads ran 8-39 % faster
+    // than 8 over 320 at M = 768 ... 4096, bf16 H = 16386 / 20002, fp16 18434, binary32 9002;
+    // bf16 H = 16386, M = 2048: 41.1 -> 30.0 us.)
     const int vec = kVecBytes / elem_size(dtype);
     const int64_t nv = H / vec + 2;
     int vpt = 0;
     int64_t threads = 1024;
     for (int k = 1; k <= 8; k *= 2) {
-      if (ceil_div(nv, k) <= (k == 8 ? 1024 : 512)) {
+      if (ceil_div(nv, k) <= (k == 8 ? 1024 : k == 4 ? 640 : 512)) {
         vpt = k;
         threads = round_up(ceil_div(nv, k), 64);
         break;

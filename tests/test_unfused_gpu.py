@@ -152,7 +152,8 @@ def test_rmsnorm_matches_oracle(oracle_mod, M, H, dtype):
 ROW_PLAN = [(2048, 7170, "bf16", False), (2048, 2562, "fp16", False), (2048, 1539, "fp32", False),
             (4096, 3074, "bf16", False), (8, 16386, "bf16", False), (64, 5122, "fp32", False),
             (1, 7170, "fp16", False), (100, 6146, "bf16", False), (2048, 7170, "fp16", True),
-            (512, 8194, "bf16", False), (384, 16386, "bf16", False), (500, 5122, "fp32", False)]
+            (512, 8194, "bf16", False), (384, 16386, "bf16", False), (500, 5122, "fp32", False),
+            (2048, 16386, "bf16", False), (1024, 9002, "fp32", False), (800, 20002, "fp16", True)]
 
 
 @pytest.mark.parametrize("M,H,dtype,in_place", ROW_PLAN,
