@@ -194,6 +194,23 @@ def test_launch_config_binary32_rows_by_row_count():
     c = ar.ar_launch_config(RMS, 8, 1, 7168, BF16, cu_count=256)
     assert (c["threads_per_block"], c["vecs_per_thread"]) == (448, 2)   # 16-bit: unchanged
 
+
+def test_launch_config_many_ranks_widest_rows():
+    """Eight or more partials on rows of over 2048 vectors: four vectors per thread while the row
+    fits 768 lanes (1024 for W = 16); fewer partials and wider rows keep eight."""
+    def shape(W, M, H, dt=BF16):
+        c = ar.ar_launch_config(RMS, W, M, H, dt, cu_count=256)
+        return c["threads_per_block"], c["vecs_per_thread"]
+    assert shape(16, 1, 20480) == (640, 4)
+    assert shape(16, 1024, 32768, FP16) == (1024, 4)
+    assert shape(32, 1, 24576) == (768, 4)
+    assert shape(64, 256, 20480) == (640, 4)
+    assert shape(8, 64, 20480) == (640, 4)
+    assert shape(32, 1, 32768) == (512, 8)                # over 768 lanes: eight
+    assert shape(16, 1, 65536) == (1024, 8)               # over 1024 lanes at four
+    assert shape(4, 1, 20480) == (320, 8)                 # fewer partials: unchanged
+    assert shape(16, 1, 16384) == (512, 4)                # 2048 vectors: four already
+
 def test_launch_config_two_partials_by_rows_per_cu():
     """W = 2: rows shrink with the rows per CU and keep 8 vectors per thread from 4 rows per CU
     (16-bit), then return to the W >= 4 shape from 12 rows per CU (16-bit); binary32 and a

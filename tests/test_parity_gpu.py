@@ -432,3 +432,20 @@ def test_binary32_two_vector_rows(oracle_mod, W, M, H):
         gam.cpu().numpy(), 1e-6, "fp32")
     assert_bit_exact(host_np(ro[rows].cpu()), want_ro, "fp32", "residual_out")
     assert_norm_close(host_np(no[rows].cpu()), want_no, "fp32")
+
+
+# ---- eight or more partials on rows of over 2048 vectors: four vectors per thread -------------
+
+WIDE_MANY = [(16, 3, 20480, "fp16"), (16, 2, 32768, "bf16"), (32, 2, 24576, "bf16"),
+             (64, 2, 20480, "bf16"), (8, 5, 20480, "bf16"), (16, 300, 20480, "bf16")]
+
+
+@pytest.mark.parametrize("W,M,H,dtype", WIDE_MANY, ids=["W%d-M%d-H%d-%s" % c for c in WIDE_MANY])
+def test_many_partials_widest_rows(oracle_mod, W, M, H, dtype):
+    """The planned 4-vector shape on rows of 2560-4096 vectors, whole output against the
+    oracle."""
+    cfg = ar.ar_launch_config(ar.PATTERN_AR_RESIDUAL_RMSNORM, W, M, H, ar.dtype_code(TD[dtype]))
+    print("case", W, M, H, dtype, cfg, flush=True)
+    assert cfg["vecs_per_thread"] == 4
+    parts, res, gam = synth.custom(W, M, H, dtype, seed=W * 13 + M + H)
+    run_rms_both(oracle_mod, parts, res, gam, 1e-6, dtype)
