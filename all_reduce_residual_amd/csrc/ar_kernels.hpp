@@ -562,10 +562,12 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_kernel(
           ok_g[g] = ok[k0 + g];
         }
         float acc[G][kVec];
-        // Staged only for groups of several vectors: that is where the scheduler otherwise
-        // issues the loads one round trip apart (W = 8: 2x); single-vector chains (W >= 16)
-        // measured faster unstaged.
-        src.template sum<T, W, G, kLoads, (G >= 2)>(in, base, boff_g, ok_g, acc);
+        // Staged for groups of several vectors: that is where the scheduler otherwise issues
+        // the loads one round trip apart (W = 8: 2x); single-vector chains (W >= 16) measured
+        // faster unstaged -- except W = 16 with 8 vectors per thread, whose unstaged 8-load
+        // batches compiled to a full wait after every load (136 loads, 135 waits).
+        constexpr bool kStageGroup = G >= 2 || (W == 16 && VPT >= 8);
+        src.template sum<T, W, G, kLoads, kStageGroup>(in, base, boff_g, ok_g, acc);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           accumulate<T>(acc[g], load_stream(at(residual + base, boff_g[g])));
