@@ -205,11 +205,14 @@ void plan_norm(int W, int64_t M, int64_t H, int dtype, int cu, ar_launch_cfg_t* 
     while (vpt < 8 && ceil_div(V, vpt) > target) vpt *= 2;
     while (vpt < 8 && round_up(ceil_div(V, vpt), 64) > 1024) vpt *= 2;
     // Eight or more partials on rows of over 2048 vectors: four vectors per thread while the
-    // row fits 768 lanes (1024 for W = 16) rather than eight over up to 512.  The 8-vector
-    // kernel at W = 16 ran 1.6-4x slower (H = 20480 bf16, M = 1: 64.8 -> 15.6 us); W = 32 / 64
-    // 6-20 % faster at M = 1 and 9-12 % at M = 1024 (mixed beyond 3072 vectors); W = 8 2-13 %
-    // at 2560 vectors.
-    if (vpt == 8 && W >= 8 && round_up(ceil_div(V, 4), 64) <= (W == 16 ? 1024 : 768)) vpt = 4;
+    // row fits 768 lanes (1024 for W = 16) rather than eight over up to 512 (16-bit rows
+    // H = 20480 / 24576 / 32768: W = 16 5-30 % faster than its staged 8-vector form, W = 32 / 64
+    // 6-20 % at M = 1 and 9-12 % at M = 1024, mixed beyond 3072 vectors; W = 8 2-13 % at 2560
+    // vectors).  Binary32 rows only while a quarter of the CUs or fewer hold a row: 5-39 %
+    // faster at M = 1, but 1.5-7 % slower at M = 256 and mixed at 1024.
+    if (vpt == 8 && W >= 8 && (elem_size(dtype) == 2 || M * 4 <= int64_t(cu)) &&
+        round_up(ceil_div(V, 4), 64) <= (W == 16 ? 1024 : 768))
+      vpt = 4;
     // Rounding the lane count up to whole waves can leave a vector slot that no lane uses
     // (e.g. 1792 vectors at 8 per thread on 256 lanes); halve the vectors per thread instead --
     // except for a single tensor (W = 1, the RMSNorm step alone) once rows outnumber CUs

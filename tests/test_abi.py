@@ -210,6 +210,8 @@ def test_launch_config_many_ranks_widest_rows():
     assert shape(16, 1, 65536) == (1024, 8)               # over 1024 lanes at four
     assert shape(4, 1, 20480) == (320, 8)                 # fewer partials: unchanged
     assert shape(16, 1, 16384) == (512, 4)                # 2048 vectors: four already
+    assert shape(16, 64, 12288, FP32) == (768, 4)         # binary32 at few rows
+    assert shape(16, 65, 12288, FP32) == (384, 8)         # binary32 beyond: eight
 
 def test_launch_config_two_partials_by_rows_per_cu():
     """W = 2: rows shrink with the rows per CU and keep 8 vectors per thread from 4 rows per CU

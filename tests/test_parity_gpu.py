@@ -437,7 +437,8 @@ def test_binary32_two_vector_rows(oracle_mod, W, M, H):
 # ---- eight or more partials on rows of over 2048 vectors: four vectors per thread -------------
 
 WIDE_MANY = [(16, 3, 20480, "fp16"), (16, 2, 32768, "bf16"), (32, 2, 24576, "bf16"),
-             (64, 2, 20480, "bf16"), (8, 5, 20480, "bf16"), (16, 300, 20480, "bf16")]
+             (64, 2, 20480, "bf16"), (8, 5, 20480, "bf16"), (16, 300, 20480, "bf16"),
+             (16, 3, 12288, "fp32"), (32, 1, 10240, "fp32")]
 
 
 @pytest.mark.parametrize("W,M,H,dtype", WIDE_MANY, ids=["W%d-M%d-H%d-%s" % c for c in WIDE_MANY])
