@@ -9,7 +9,8 @@ picks for rows of whole vectors up to H = 8192 (one or two 16-byte vectors per t
 chain per batch: W <= 8, and W = 16 with one vector) for the three element types, and asserts
 that no full wait (`s_waitcnt vmcnt(0)`) falls between two of a kernel's streaming loads; for
 the wide-row shapes (4 or 8 vectors per thread, W >= 8) it allows waits between rank batches
-but at most one per 4 loads. For
+but at most one per 4 loads, and the same bound holds for the split (workspace) kernel at
+every W. For
 the sum kernel it compiles every (W, vectors per thread) and checks its loop-free path (kernel
 entry to the first store): whole rank batches only, with exactly one full wait between
 consecutive batches and none inside one (16 loads per batch, 8 once a thread holds 32 or more
@@ -46,6 +47,9 @@ def _source() -> str:
             refs.append("reinterpret_cast<const void*>(&arf::ar_norm_kernel<arf::%s, %d, %d, true>)"
                         % (t, w, v))
         for w in SUM_W:
+            for v in (1, 2):
+                refs.append("reinterpret_cast<const void*>(&arf::ar_norm_split_kernel<arf::%s, %d, "
+                            "%d, true>)" % (t, w, v))
             for u in SUM_U:
                 refs.append("reinterpret_cast<const void*>(&arf::ar_sum_kernel<arf::%s, %d, %d, "
                             "true>)" % (t, w, u))
@@ -96,11 +100,11 @@ def _norm_symbol(t: str, w: int, v: int) -> str:
     return "_ZN3arf14ar_norm_kernelINS_%sELi%dELi%dELb1E" % (TN[t], w, v)
 
 
-def _norm_streaming_loads(asm: str) -> dict:
-    """Per norm kernel symbol: its streaming (non-temporal) global loads."""
+def _norm_streaming_loads(asm: str, kernel: str = "ar_norm_kernel") -> dict:
+    """Per kernel symbol: its streaming (non-temporal) global loads."""
     out, name = {}, None
     for line in asm.splitlines():
-        m = re.match(r"^(_Z\S*ar_norm_kernel\S*):", line)
+        m = re.match(r"^(_Z\S*%s\S*):" % kernel, line)
         if m:
             name = m.group(1)
             out[name] = 0
@@ -111,12 +115,12 @@ def _norm_streaming_loads(asm: str) -> dict:
     return out
 
 
-def _waits_between_streaming_loads(asm: str) -> dict:
+def _waits_between_streaming_loads(asm: str, kernel: str = "ar_norm_kernel") -> dict:
     """Per kernel symbol: the number of s_waitcnt vmcnt(0) that lie between two streaming
     (non-temporal) global loads of its body."""
     out, name, nt, pending = {}, None, 0, False
     for line in asm.splitlines():
-        m = re.match(r"^(_Z\S*ar_norm_kernel\S*):", line)
+        m = re.match(r"^(_Z\S*%s\S*):" % kernel, line)
         if m:
             name, nt, pending = m.group(1), 0, False
             out[name] = 0
@@ -211,3 +215,13 @@ def test_checker_sees_a_serialized_load():
         "\ts_endpgm",
     ])
     assert _waits_between_streaming_loads(asm) == {"_ZN3arf14ar_norm_kernelIxEEvv": 1}
+
+
+def test_split_kernel_loads_not_serialized(norm_asm):
+    """The split (workspace) kernel, every W and one or two vectors per thread: at most one full
+    wait per 4 streaming loads (it measured 1-3 waits for up to 68 loads)."""
+    waits = _waits_between_streaming_loads(norm_asm, "ar_norm_split_kernel")
+    loads = _norm_streaming_loads(norm_asm, "ar_norm_split_kernel")
+    assert len(waits) == len(TYPES) * len(SUM_W) * 2, sorted(waits)
+    bad = {k: (loads[k], v) for k, v in waits.items() if loads[k] == 0 or v * 4 > loads[k]}
+    assert not bad, "(loads, full waits): %s" % bad
