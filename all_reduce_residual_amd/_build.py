@@ -21,13 +21,16 @@ PROBE_SOURCES = ["stream_probe.hip"]
 PROBE_LIB = os.path.join(PKG, "libar_probe.so")
 ARCH = "gfx950"
 
-# -packed-fp32-ops: keep the compiler from fusing binary32 adds/multiplies into packed
-# two-lane instructions; every add of the rank chain is a plain v_add_f32.
-HIPCC_FLAGS = [
-    "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
-    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-command-line-argument",
-]
+# -packed-fp32-ops (device code only): keep the compiler from fusing binary32 adds/multiplies
+# into packed two-lane instructions; every add of the rank chain is a plain v_add_f32.  Each
+# source is compiled in two passes -- the gfx950 code with that feature into a code-object
+# bundle, then the host code with the bundle embedded -- so the host compiler never sees the
+# target feature (it is not one of the host target's).
+COMMON_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
+                "-Wno-unused-command-line-argument"]
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# The device pass's flags in one list (the assembly checks compile device code with them).
+HIPCC_FLAGS = COMMON_FLAGS + DEVICE_FLAGS
 
 
 def hipcc() -> str:
@@ -44,10 +47,16 @@ def build(extra_flags=(), out: str = LIB, jobs: int = 0, probe: bool = True) -> 
     jobs = jobs or min(len(sources), os.cpu_count() or 1)
     with tempfile.TemporaryDirectory(prefix="ar_build_") as tmpdir:
         def compile_one(src):
-            obj = os.path.join(tmpdir, os.path.splitext(src)[0] + ".o")
-            subprocess.run([hipcc()] + HIPCC_FLAGS + list(extra_flags) +
-                           [inc, "-c", "-o", obj, os.path.join(CSRC, src)], check=True)
-            return obj
+            stem = os.path.join(tmpdir, os.path.splitext(src)[0])
+            path = os.path.join(CSRC, src)
+            subprocess.run([hipcc()] + COMMON_FLAGS + DEVICE_FLAGS + list(extra_flags) +
+                           [inc, "--cuda-device-only", "-c", "-o", stem + ".hipfb", path],
+                           check=True)
+            subprocess.run([hipcc()] + COMMON_FLAGS + list(extra_flags) +
+                           [inc, "--cuda-host-only", "-Xclang", "-fcuda-include-gpubinary",
+                            "-Xclang", stem + ".hipfb", "-c", "-o", stem + ".o", path],
+                           check=True)
+            return stem + ".o"
 
         def link(objs, target):
             tmp = target + ".tmp%d" % os.getpid()

@@ -178,6 +178,48 @@ __device__ inline float segment_sum(float x, int seg) {
   return x;
 }
 
+// ---- rows outside the binary32 range of the sum of squares ----------------------------------------
+//
+// The norm kernels reduce a row's sum of squares ss in binary32.  That meets the norm bar while
+// x = ss / H + eps is a normal number of at least 2^-100: a square that lost bits to the subnormal
+// range is off by at most 2^-150, so all of them together move x by at most 2^-134 (H <= 2^16),
+// a relative 2^-34.  Two kinds of finite rows fall outside: rows whose squares overflow (ss = inf
+// from an RMS of about 1.8e19 / sqrt(H), or one element above 1.8e19, on: rstd would be 0 and
+// norm_out 0), and rows with eps below 2^-100 whose squares underflow (eps = 0 and elements below
+// about 2^-63: rstd would be inf or far off).  Such a row is normalised again from the same
+// rounded values scaled by an exact power of two 2^k: the sum of squares S' of v 2^k is S 4^k,
+// so rstd' = 1 / sqrt(S' / H + eps 4^k) = rstd 2^-k, and y = (v 2^k * rstd') * gamma.
+//   * overflow (x = inf): k = -73.  Every |v| <= 2^128 becomes <= 2^55, so even 2^16 squares
+//     sum to at most 2^126; S >= 2^128, so S' >= 2^-18 and the squares that now underflow
+//     (|v| < 2^-1.5) change S' by at most 2^-133 in all, a relative 2^-115.
+//   * underflow (x < 2^-100, so eps < 2^-100 and every |v| < 2^-42): k = 90.  Every square
+//     of v 2^90 lies in [2^-118, 2^96] (from the smallest subnormal up), normal and exact to
+//     binary32 rounding, and eps 4^90 < 2^80.
+// The scaling is exact (ldexp) except where v 2^k underflows, and then y is tiny anyway.  The
+// test costs one compare per row and a branch the row's threads take together; rows inside the
+// range compute exactly what they computed without it.  A row holding an infinity also lands
+// here (x = inf) and gets the binary32 path's results (rstd' = 0); NaN compares false.
+__device__ inline bool outside_binary32_range(float x) {
+  return x < 0x1p-100f || x > 3.40282347e38f;
+}
+
+// The scale exponent k for a row outside the range (see above).
+__device__ inline int wide_scale(float x) { return x > 1.0f ? -73 : 90; }
+
+// v 2^k, exact unless the result is subnormal.
+__device__ inline float scaled(float v, int k) { return __builtin_amdgcn_ldexpf(v, k); }
+
+// One element normalised with rstd = m 2^E: (v 2^E * m) * gamma.  For E = 0 (every row inside
+// the range) this is (v * rstd) * gamma, bit for bit.
+__device__ inline float norm_elem_scaled(float v, float m, int E, float g) {
+  return (scaled(v, E) * m) * g;
+}
+
+// rstd' of a row whose values were scaled by 2^k, from their sum of squares S'.
+__device__ inline float rstd_of_scaled(float S, int k, float count_h, float eps) {
+  return rsqrtf(S / count_h + scaled(eps, 2 * k));
+}
+
 // ---- addressing ---------------------------------------------------------------------------------
 //
 // Every address is a wave-uniform base (a tensor pointer plus a uniform element offset, computed
@@ -468,6 +510,10 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_kernel(
     u32x4* norm_out, int64_t M, int V, int L, int R, float eps, float count_h, Src src) {
   constexpr int kVec = T::kVec;
   __shared__ float red[2][kMaxWavesPerBlock];
+  // The exchanges of rows outside the binary32 range.  A wave writes each of them again only
+  // after a later barrier that every wave passes only after reading them.
+  __shared__ float red_wide[2][kMaxWavesPerBlock];
+  __shared__ bool wide_sh[kMaxWavesPerBlock];
 
   const int tid = threadIdx.x;
   const int slot = tid / L;
@@ -503,7 +549,73 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_kernel(
     for (int k = 0; k < VPT; ++k) load_gamma(gamma, idx[k], gam[k]);
   }
 
+  // gamma of this thread's vector k (kept in registers, or re-read from L2).
+  auto gamma_of = [&](int k, float (&g)[kVec]) {
+    if constexpr (kKeepGamma) {
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) g[e] = gam[k][e];
+    } else {
+      // Opaque index: keeps the compiler from hoisting these loop-invariant loads out of
+      // the row loop, where all VPT x kVec values would stay live in registers.
+      int gi = idx[k];
+      asm volatile("" : "+v"(gi));
+      load_gamma(gamma, gi, g);
+    }
+  };
+
+  // The row's sum of squares of this thread's values scaled by 2^k, reduced over the row in the
+  // same tree as the loop's (inside the wave, then the row's waves in order through LDS bank
+  // `b`: two banks, so that two reductions in a row need no barrier between them).
+  auto scaled_row_sum = [&](const u32x4 (&vals)[VPT], const bool (&okv)[VPT], int k2,
+                            int b) -> float {
+    float s2 = 0.0f;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      if (okv[k]) {
+        float v[kVec];
+        T::widen(vals[k], v);
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) {
+          const float u = scaled(v[e], k2);
+          s2 += u * u;
+        }
+      }
+    }
+    s2 = segment_sum(s2, L);
+    if (L > 64) {
+      if ((tid & 63) == 0) red_wide[b][wave] = s2;
+      __syncthreads();
+      const int waves_per_row = L >> 6;
+      const int w0 = slot * waves_per_row;
+      float t = red_wide[b][w0];
+      for (int j = 1; j < waves_per_row; ++j) t += red_wide[b][w0 + j];
+      s2 = t;
+    }
+    return s2;
+  };
+  // norm_out of this thread's vectors with rstd = m 2^k2.
+  auto store_scaled = [&](const u32x4 (&vals)[VPT], const bool (&okv)[VPT], int64_t base,
+                          const uint32_t (&boff)[VPT], float m, int k2) {
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      if (okv[k]) {
+        float v[kVec];
+        T::widen(vals[k], v);
+        float g[kVec];
+        gamma_of(k, g);
+        float y[kVec];
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) y[e] = norm_elem_scaled(v[e], m, k2, g[e]);
+        store_vec<kNtStore>(at(norm_out + base, boff[k]), T::narrow(y));
+      }
+    }
+  };
+
   int bank = 0;
+  // Whether a row of this wave (of this block, for rows of several waves) was outside the
+  // binary32 range of the sum of squares: with the partials' sum those rows are normalised
+  // again after the loop (see below).
+  bool any_wide = false;
   for (int64_t grp = blockIdx.x; grp < groups; grp += gridDim.x) {
     const bool row_ok = grp * R + slot < M;
     const int64_t base = grp * R * static_cast<int64_t>(V);
@@ -601,27 +713,87 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_kernel(
       bank ^= 1;
     }
     const float rstd = rsqrtf(ss / count_h + eps);
-
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
       if (ok[k]) {
         float v[kVec];
         T::widen(rounded[k], v);
         float g[kVec];
-        if constexpr (kKeepGamma) {
-#pragma unroll
-          for (int e = 0; e < kVec; ++e) g[e] = gam[k][e];
-        } else {
-          // Opaque index: keeps the compiler from hoisting these loop-invariant loads out of
-          // the row loop, where all VPT x kVec values would stay live in registers.
-          int gi = idx[k];
-          asm volatile("" : "+v"(gi));
-          load_gamma(gamma, gi, g);
-        }
+        gamma_of(k, g);
         float y[kVec];
 #pragma unroll
         for (int e = 0; e < kVec; ++e) y[e] = (v[e] * rstd) * g[e];
         store_vec<kNtStore>(at(norm_out + base, boff[k]), T::narrow(y));
+      }
+    }
+
+    // Rows outside the binary32 range of the sum of squares get norm_out again, from the same
+    // rounded values scaled by 2^kw, stored over the values above.  The fused patterns do that
+    // after the chunk (re-reading residual_out), so that the row loop holds exactly the code it
+    // holds without it; the norm-only mode, whose output may overwrite its input, does it here.
+    const bool wide = row_ok && outside_binary32_range(ss / count_h + eps);
+    if constexpr (!kNormOnly) {
+      any_wide = any_wide || __builtin_amdgcn_ballot_w64(wide) != 0;
+    } else {
+      // wide_any: a row outside the range shares this wave (L <= 64) or, for rows of several
+      // waves, this block, whose barrier the second reduction below uses.  Several such rows
+      // per block (a shape the launch planner does not pick) need one more exchange for that.
+      bool wide_any;
+      if (L <= 64) {
+        wide_any = __builtin_amdgcn_ballot_w64(wide) != 0;
+      } else if (R == 1) {
+        wide_any = wide;
+      } else {
+        if ((tid & 63) == 0) wide_sh[wave] = wide;
+        __syncthreads();
+        wide_any = false;
+        for (int w = 0; w < static_cast<int>(blockDim.x >> 6); ++w)
+          wide_any = wide_any || wide_sh[w];
+      }
+      if (wide_any) {
+        const int kw = wide ? wide_scale(ss / count_h + eps) : 0;
+        const float s2 = scaled_row_sum(rounded, ok, kw, 1);
+        if (wide) {
+          const float m = rstd_of_scaled(s2, kw, count_h, eps);
+          store_scaled(rounded, ok, base, boff, m, kw);
+        }
+      }
+    }
+  }
+  if constexpr (!kNormOnly) {
+    // The rows outside the range, again.  Every wave that shares a barrier must take the same
+    // path, so rows of several waves agree on the block's flag first.
+    if (L > 64 && R > 1) {
+      if ((tid & 63) == 0) wide_sh[wave] = any_wide;
+      __syncthreads();
+      any_wide = false;
+      for (int w = 0; w < static_cast<int>(blockDim.x >> 6); ++w) any_wide = any_wide || wide_sh[w];
+    }
+    if (any_wide) {
+      // This thread's residual_out stores visible, then every row group of this block read
+      // back (the rounded values) and checked again: the same values in the same order give
+      // the same sums of squares, so exactly the rows found outside the range above.
+      __threadfence();
+      for (int64_t grp = blockIdx.x; grp < groups; grp += gridDim.x) {
+        const bool row_ok = grp * R + slot < M;
+        const int64_t base = grp * R * static_cast<int64_t>(V);
+        uint32_t boff[VPT];
+        group_offsets(grp, boff);
+        bool ok[VPT];
+        u32x4 rounded[VPT];
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+          ok[k] = row_ok && col_ok[k];
+          rounded[k] = *at(residual_out + base, boff[k]);
+        }
+        const float ss = scaled_row_sum(rounded, ok, 0, 0);
+        const bool wide = row_ok && outside_binary32_range(ss / count_h + eps);
+        const int kw = wide ? wide_scale(ss / count_h + eps) : 0;
+        const float s2 = scaled_row_sum(rounded, ok, kw, 1);
+        if (wide) {
+          const float m = rstd_of_scaled(s2, kw, count_h, eps);
+          store_scaled(rounded, ok, base, boff, m, kw);
+        }
       }
     }
   }
@@ -653,22 +825,22 @@ __device__ inline void load_row_vec(const void* x, int64_t e0, int64_t e1, int64
   }
 }
 
-// y = RN_T((f * rstd) * gamma) for the row's elements of vector v.
-template <class T>
+// y = RN_T(norm(f, gamma)) for the row's elements of vector v.
+template <class T, class Norm>
 __device__ inline void store_row_vec(void* y, const float* gamma, int64_t e0, int64_t e1,
-                                     int64_t v, const float (&f)[T::kVec], float rstd) {
+                                     int64_t v, const float (&f)[T::kVec], Norm norm) {
   const int64_t a = v * T::kVec;
   if (a >= e0 && a + T::kVec <= e1) {
     const float* g = gamma + (a - e0);
     float o[T::kVec];
 #pragma unroll
-    for (int e = 0; e < T::kVec; ++e) o[e] = (f[e] * rstd) * g[e];
+    for (int e = 0; e < T::kVec; ++e) o[e] = norm(f[e], g[e]);
     store_vec<true>(static_cast<u32x4*>(y) + v, T::narrow(o));
   } else {
 #pragma unroll
     for (int e = 0; e < T::kVec; ++e) {
       const int64_t idx = a + e;
-      if (idx >= e0 && idx < e1) T::store1(y, idx, (f[e] * rstd) * gamma[idx - e0]);
+      if (idx >= e0 && idx < e1) T::store1(y, idx, norm(f[e], gamma[idx - e0]));
     }
   }
 }
@@ -750,11 +922,28 @@ __global__ __launch_bounds__(kMaxThreads) void ar_rmsnorm_rows_kernel(const void
       }
       // gamma is read in the epilogue, per vector (L2): moving all of it before the barrier
       // measured slower (H = 7170: 15.9 -> 18.3 us), the other blocks on the CU hide its latency.
-      const float rstd = rsqrtf(block_sum(ss, red) / count_h + eps);
+      const float x32 = block_sum(ss, red) / count_h + eps;
+      float m = rsqrtf(x32);
+      int E = 0;
+      if (outside_binary32_range(x32)) {
+        // The sum of squares again, of the values in registers (zeros outside the row) scaled.
+        E = wide_scale(x32);
+        float s2 = 0.0f;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+#pragma unroll
+          for (int e = 0; e < kVec; ++e) {
+            const float u = scaled(f[k][e], E);
+            s2 += u * u;
+          }
+        }
+        m = rstd_of_scaled(block_sum(s2, red), E, count_h, eps);
+      }
+      auto norm = [&](float a, float g) { return norm_elem_scaled(a, m, E, g); };
 #pragma unroll
       for (int k = 0; k < K; ++k) {
         const int64_t j = threadIdx.x + k * nthreads;
-        if (j < nv) store_row_vec<T>(y, gamma, e0, e1, v0 + j, f[k], rstd);
+        if (j < nv) store_row_vec<T>(y, gamma, e0, e1, v0 + j, f[k], norm);
       }
     } else {
       for (int64_t j = threadIdx.x; j < nv; j += nthreads) {
@@ -763,11 +952,30 @@ __global__ __launch_bounds__(kMaxThreads) void ar_rmsnorm_rows_kernel(const void
 #pragma unroll
         for (int e = 0; e < kVec; ++e) ss += f[e] * f[e];
       }
-      const float rstd = rsqrtf(block_sum(ss, red) / count_h + eps);
+      const float x32 = block_sum(ss, red) / count_h + eps;
+      float m = rsqrtf(x32);
+      int E = 0;
+      if (outside_binary32_range(x32)) {
+        // The sum of squares again, scaled: one more pass over the row before any element is
+        // written.
+        E = wide_scale(x32);
+        float s2 = 0.0f;
+        for (int64_t j = threadIdx.x; j < nv; j += nthreads) {
+          float f[kVec];
+          load_row_vec<T, false>(x, e0, e1, v0 + j, f);
+#pragma unroll
+          for (int e = 0; e < kVec; ++e) {
+            const float u = scaled(f[e], E);
+            s2 += u * u;
+          }
+        }
+        m = rstd_of_scaled(block_sum(s2, red), E, count_h, eps);
+      }
+      auto norm = [&](float a, float g) { return norm_elem_scaled(a, m, E, g); };
       for (int64_t j = threadIdx.x; j < nv; j += nthreads) {
         float f[kVec];
         load_row_vec<T, false>(x, e0, e1, v0 + j, f);
-        store_row_vec<T>(y, gamma, e0, e1, v0 + j, f, rstd);
+        store_row_vec<T>(y, gamma, e0, e1, v0 + j, f, norm);
       }
     }
   }
@@ -809,12 +1017,32 @@ __device__ inline void split_offsets(int V, int seg, uint32_t (&boff)[VPT], bool
   }
 }
 
+// This thread's sum of squares of its rounded values scaled by 2^k (vectors in order, then
+// elements in order; k = 0 gives the sum of the unscaled squares).
+template <class T, int VPT>
+__device__ inline float sum_squares(const u32x4 (&rounded)[VPT], const bool (&ok)[VPT], int k) {
+  float ss = 0.0f;
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    if (ok[j]) {
+      float v[T::kVec];
+      T::widen(rounded[j], v);
+#pragma unroll
+      for (int e = 0; e < T::kVec; ++e) {
+        const float u = scaled(v[e], k);
+        ss += u * u;
+      }
+    }
+  }
+  return ss;
+}
+
 // Sums this thread's vectors of a segment in rank order with the residual last, rounds them to
 // T, and returns this thread's sum of squares of the rounded values.
 template <class T, int W, int VPT>
 __device__ inline float split_segment(const RankPtrs<W>& in, const u32x4* residual, int64_t base,
-                                      const uint32_t (&boff)[VPT], const bool (&ok)[VPT],
-                                      u32x4 (&rounded)[VPT]) {
+                                    const uint32_t (&boff)[VPT], const bool (&ok)[VPT],
+                                    u32x4 (&rounded)[VPT]) {
   constexpr int kVec = T::kVec;
   // A segment block is often the only wave on its CU, so its loads in flight are all the memory
   // parallelism there is: the residual loads go first and every rank batch is staged.  Left
@@ -936,6 +1164,40 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_split_kernel(
 #pragma unroll
       for (int e = 0; e < kVec; ++e) y[e] = (v[e] * rstd) * gam[k][e];
       store_vec<kNtStore>(at(norm_out + base, boff[k]), T::narrow(y));
+    }
+  }
+  // A row outside the binary32 range of the sum of squares (total_sh is the same in every thread
+  // of the block: the branch is uniform): norm_out again from the values scaled by 2^E, stored
+  // over the values above.  The exchange carries unscaled segment sums, so every block of the
+  // row recomputes the other segments (re-reading their inputs) and adds them in segment order
+  // the same way: all blocks reach the same sum.
+  const float x32 = total_sh / count_h + eps;
+  if (outside_binary32_range(x32)) {
+    const int E = wide_scale(x32);
+    float sq = 0.0f;
+    for (int j = 0; j < S; ++j) {
+      if (j != s) {
+        uint32_t bj[VPT];
+        bool okj[VPT];
+        u32x4 rj[VPT];
+        split_offsets<VPT>(V, j, bj, okj);
+        (void)split_segment<T, W, VPT>(in, residual, base, bj, okj, rj);
+        sq += sum_squares<T, VPT>(rj, okj, E);
+      } else {
+        sq += sum_squares<T, VPT>(rounded, ok, E);
+      }
+    }
+    const float m = rstd_of_scaled(block_sum(sq, red), E, count_h, eps);
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      if (ok[k]) {
+        float v[kVec];
+        T::widen(rounded[k], v);
+        float y[kVec];
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) y[e] = norm_elem_scaled(v[e], m, E, gam[k][e]);
+        store_vec<kNtStore>(at(norm_out + base, boff[k]), T::narrow(y));
+      }
     }
   }
 }

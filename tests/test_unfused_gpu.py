@@ -182,26 +182,39 @@ def test_rmsnorm_in_place(oracle_mod, H):
 @pytest.mark.parametrize("H", [256, 13])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
 def test_rmsnorm_special_values(oracle_mod, H, dtype):
-    """Rows holding infinities, NaN, subnormals and zeros, on both kernels (H = 256 is whole
-    vectors, H = 13 is not).  Finite values stay below 2^60 so that no sum of squares overflows
-    binary32 (the kernels accumulate squares in binary32, the oracle in binary64)."""
+    """Rows holding infinities, NaN, subnormals, zeros and the largest finite values, on both
+    kernels (H = 256 is whole vectors, H = 13 is not).  Row 1 holds no infinity or NaN, so its
+    finite values up to the largest of the type overflow a binary32 sum of squares (the oracle's
+    is binary64); row 2 holds only subnormals and zeros."""
     rng = np.random.default_rng(H)
     if dtype == "fp32":
-        pool = np.array([0.0, -0.0, 1e-45, 3.0, -2.5, np.inf, np.nan, 1e15], dtype=np.float32)
+        pool = np.array([0.0, -0.0, 1e-45, 3.0, -2.5, np.inf, np.nan, 1e15, 3.4028235e38,
+                         -1e30], dtype=np.float32)
+        finite = pool[np.isfinite(pool)]
         x = torch.from_numpy(rng.choice(pool, size=(6, H)).astype(np.float32))
+        x[1] = torch.from_numpy(rng.choice(finite, size=H).astype(np.float32))
+        x[2] = torch.from_numpy(rng.choice(np.array([0.0, 1e-45, -3e-45, 1e-40], dtype=np.float32),
+                                           size=H))
     else:
         pool = ([0x0000, 0x8000, 0x0001, 0x3C00, 0xC100, 0x7C00, 0x7E00, 0x7BFF] if dtype == "fp16"
-                else [0x0000, 0x8000, 0x0001, 0x3F80, 0xC020, 0x7F80, 0x7FC0, 0x5A00])
-        x = torch.from_numpy(rng.choice(np.array(pool, dtype=np.uint16), size=(6, H))
-                             .view(np.int16)).view(TD[dtype])
+                else [0x0000, 0x8000, 0x0001, 0x3F80, 0xC020, 0x7F80, 0x7FC0, 0x5A00, 0x7F7F,
+                      0xF0A0])
+        finite = [b for b in pool if (b & 0x7C00) != 0x7C00] if dtype == "fp16" else \
+            [b for b in pool if (b & 0x7F80) != 0x7F80]
+        sub = [0x0000, 0x0001, 0x8003, 0x0040] if dtype == "bf16" else [0x0000, 0x0001, 0x8003]
+        xs = rng.choice(np.array(pool, dtype=np.uint16), size=(6, H))
+        xs[1] = rng.choice(np.array(finite, dtype=np.uint16), size=H)
+        xs[2] = rng.choice(np.array(sub, dtype=np.uint16), size=H)
+        x = torch.from_numpy(xs.view(np.int16)).view(TD[dtype])
     x[0] = 1  # one ordinary row
     gam = torch.ones(H, dtype=torch.float32)
     d = dev(x)
-    y = torch.empty_like(d)
-    ar.ar_rmsnorm(d, dev(gam), 1e-6, y)
-    torch.cuda.synchronize()
-    want = oracle_mod.rmsnorm(host_np(x), gam.numpy(), 1e-6, dtype)
-    assert_norm_close(host_np(y.cpu()), want, dtype)
+    for eps in (1e-6, 0.0):
+        y = torch.empty_like(d)
+        ar.ar_rmsnorm(d, dev(gam), eps, y)
+        torch.cuda.synchronize()
+        want = oracle_mod.rmsnorm(host_np(x), gam.numpy(), eps, dtype)
+        assert_norm_close(host_np(y.cpu()), want, dtype, "norm_out eps=%g" % eps)
 
 
 # The residual sum at sizes its launch plan covers with one resident round of 256-thread blocks
