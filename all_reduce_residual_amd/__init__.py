@@ -123,6 +123,7 @@ def lib():
             "ar_workspace_clear": [vp, i64, vp],
             "ar_split_config": [i32, i64, i64, i32, i32, ctypes.POINTER(SplitConfig)],
             "ar_residual_rmsnorm_ws": [vp, i32, i64, i64, i32, vp, vp, f32, vp, vp, vp, i64, vp],
+            "ar_residual_rmsnorm_noalloc": [vp, i32, i64, i64, i32, vp, vp, f32, vp, vp, vp],
             "ar_residual_rmsnorm_split_with_config": [vp, i32, i64, i64, i32, vp, vp, f32, vp,
                                                       vp, vp, i64, vp,
                                                       ctypes.POINTER(SplitConfig)],
@@ -274,6 +275,25 @@ def ar_residual_rmsnorm_ws(inputs, residual, gamma, eps: float, residual_out, no
         cfg = SplitConfig.from_dict(config)
         _check(lib().ar_residual_rmsnorm_split_with_config(*args, ctypes.byref(cfg)),
                "ar_residual_rmsnorm_split_with_config")
+
+
+NOALLOC_MAX_ROWS = 512
+
+
+def ar_residual_rmsnorm_noalloc(inputs, residual, gamma, eps: float, residual_out, norm_out,
+                                stream=None) -> None:
+    """kARResidualRMSNorm with the split form's exchange slots inside the library (no workspace
+    argument, nothing allocated; at most NOALLOC_MAX_ROWS rows).  Calls that overlap in time on
+    one GPU share those slots and race: issue them on one stream."""
+    ptrs, W, M, H, dt = _marshal_inputs(inputs, residual_out)
+    _marshal_inputs([residual], norm_out)
+    _marshal_inputs([residual], residual_out)
+    _check_gamma(gamma, H, residual_out.device)
+    s = _stream_handle(stream, residual_out.device)
+    _check(lib().ar_residual_rmsnorm_noalloc(ptrs, W, M, H, dt, residual.data_ptr(),
+                                             gamma.data_ptr(), float(eps),
+                                             residual_out.data_ptr(), norm_out.data_ptr(), s),
+           "ar_residual_rmsnorm_noalloc")
 
 
 def _check_gamma(gamma, H, device):

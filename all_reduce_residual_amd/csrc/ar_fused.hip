@@ -14,6 +14,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "ar_dispatch.hpp"
 #include "ar_fused.h"
@@ -538,6 +539,57 @@ int run_workspace_clear(void* workspace, int64_t bytes, void* stream) {
   return e == hipSuccess ? AR_OK : AR_ERR_LAUNCH;
 }
 
+// ---- the split form without a caller workspace -----------------------------------------------------
+//
+// For callers that cannot allocate: the split kernel's exchange slots live in this file-scope
+// device array, one copy per GPU (zero-filled when the code object is loaded, and cleared again
+// by the first call on each device).  In host code `scratch` names a host-side stand-in, never
+// the device memory: the device address comes from hipGetSymbolAddress, once per device with that
+// device current, and only that address is passed to kernels.
+constexpr int64_t kScratchWords = int64_t(AR_NOALLOC_MAX_ROWS) * arf::kSplitSlots;
+static __device__ __align__(256) uint64_t scratch[kScratchWords];
+
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// This device's copy of `scratch` (set up on the first call on the device: the symbol's device
+// address, then a zero fill on `stream`).  AR_ERR_DEVICE if the device or symbol query fails.
+int device_scratch(hipStream_t stream, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return AR_ERR_DEVICE;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+      void* q = nullptr;
+      if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return AR_ERR_DEVICE;
+      const int st = run_workspace_clear(q, kScratchWords * kSplitSlotBytes, stream);
+      if (st != AR_OK) return st;
+      g_scratch_ptr[dev].store(q, std::memory_order_release);
+      p = q;
+    }
+  }
+  *out = p;
+  return AR_OK;
+}
+
+int run_norm_noalloc(const void* const* inputs, int W, int64_t M, int64_t H, int dtype,
+                     const void* residual, const float* gamma, float eps, void* residual_out,
+                     void* norm_out, void* stream) {
+  int st = check_shape(AR_PATTERN_AR_RESIDUAL_RMSNORM, W, M, H, dtype);
+  if (st != AR_OK) return st;
+  if (M > AR_NOALLOC_MAX_ROWS) return AR_ERR_UNSUPPORTED;  // more rows than `scratch` holds
+  st = validate_norm(inputs, W, M, H, dtype, residual, gamma, eps, residual_out, norm_out);
+  if (st != AR_OK) return st;
+  if (M == 0) return AR_OK;
+  void* ws = nullptr;
+  st = device_scratch(static_cast<hipStream_t>(stream), &ws);
+  if (st != AR_OK) return st;
+  return run_norm_ws(inputs, W, M, H, dtype, residual, gamma, eps, residual_out, norm_out, ws,
+                     kScratchWords * kSplitSlotBytes, stream, nullptr);
+}
+
 // ---- two-kernel (unfused) path and the stand-alone RMSNorm ----------------------------------------
 //
 // The route for kARResidualRMSNorm shapes the fused kernel does not take (rows that are not whole
@@ -999,6 +1051,13 @@ int ar_residual_rmsnorm_ws(const void* const* inputs, int W, int64_t M, int64_t 
                            int64_t workspace_bytes, void* stream) {
   return run_norm_ws(inputs, W, M, H, dtype, residual, gamma, eps, residual_out, norm_out,
                      workspace, workspace_bytes, stream, nullptr);
+}
+
+int ar_residual_rmsnorm_noalloc(const void* const* inputs, int W, int64_t M, int64_t H,
+                                int dtype, const void* residual, const float* gamma, float eps,
+                                void* residual_out, void* norm_out, void* stream) {
+  return run_norm_noalloc(inputs, W, M, H, dtype, residual, gamma, eps, residual_out, norm_out,
+                          stream);
 }
 
 int ar_residual_rmsnorm_split_with_config(const void* const* inputs, int W, int64_t M, int64_t H,

@@ -28,9 +28,10 @@
  *
  * Ownership: the caller owns every buffer.  `inputs` is a HOST array of W DEVICE pointers; it is
  * read during the call and not retained.  The library allocates no device memory and retains
- * no pointer (the one scratch buffer, the split form's workspace below, is the caller's), so
- * calls are safe to capture in a hipGraph and replay.  The
- * only state is a per-device cache of the compute-unit count.
+ * no pointer (the one scratch buffer, the split form's workspace below, is the caller's, except
+ * for ar_residual_rmsnorm_noalloc, whose slots are a fixed device array of the library), so
+ * calls are safe to capture in a hipGraph and replay.  The only other state is a per-device
+ * cache of the compute-unit count.
  *
  * Streams: `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue one kernel (two
  * for ar_residual_rmsnorm_unfused) and return without synchronising; the return code reports
@@ -210,6 +211,22 @@ int ar_residual_rmsnorm_ws(const void* const* inputs, int W, int64_t M, int64_t 
                            const void* residual, const float* gamma, float eps,
                            void* residual_out, void* norm_out, void* workspace,
                            int64_t workspace_bytes, void* stream);
+
+/* kARResidualRMSNorm for callers that cannot allocate: code under hipGraph capture, tight
+ * serving loops, harnesses that forbid allocation.  Arguments, results and rejections as
+ * ar_residual_rmsnorm; the launch as ar_residual_rmsnorm_ws, with the split kernel's exchange
+ * slots in a device array inside the library instead of a caller workspace: AR_NOALLOC_MAX_ROWS
+ * rows of AR_SPLIT_SLOTS 8-byte slots (256 KiB), one copy per GPU, held until the process ends.
+ * Nothing is allocated: the first call on a device looks up that array's address and clears it
+ * with a kernel on `stream` (no memset node).
+ *   M > AR_NOALLOC_MAX_ROWS : AR_ERR_UNSUPPORTED (ar_residual_rmsnorm needs no scratch at all)
+ * Every call on one GPU shares that GPU's array and leaves it valid for the next call; calls
+ * that overlap in time on one GPU (other streams, other threads) race on it and may produce
+ * wrong norm_out: issue them on one stream. */
+#define AR_NOALLOC_MAX_ROWS 512
+int ar_residual_rmsnorm_noalloc(const void* const* inputs, int W, int64_t M, int64_t H,
+                                int dtype, const void* residual, const float* gamma, float eps,
+                                void* residual_out, void* norm_out, void* stream);
 
 /* The split kernel with an explicit shape (tuning and tests).  AR_ERR_INVALID_ARG for a
  * malformed shape, AR_ERR_ALIAS if an output overlaps the residual or an input. */

@@ -22,7 +22,7 @@ def L():
 def test_exports_every_declared_function(L):
     names = ar.header_functions()
     assert set(names) == {"ar_sum", "ar_residual_rmsnorm", "ar_supports", "ar_launch_config",
-                          "ar_sum_with_config", "ar_residual_rmsnorm_with_config",
+                          "ar_residual_rmsnorm_noalloc", "ar_sum_with_config", "ar_residual_rmsnorm_with_config",
                           "ar_status_string", "ar_device_cu_count", "ar_row_partition",
                           "ar_all_gather", "ar_lamport_arm", "ar_lamport_push",
                           "ar_lamport_sum", "ar_lamport_residual_rmsnorm",
@@ -439,3 +439,25 @@ def test_split_validation_rejects_before_device_access(L):
     assert L.ar_workspace_clear(ws + 8, 64, None) == ar.AR_ERR_MISALIGNED
     assert L.ar_workspace_clear(ws, 12, None) == ar.AR_ERR_INVALID_ARG
     assert L.ar_workspace_clear(ws, 0, None) == ar.AR_OK
+
+
+def test_noalloc_validation_rejects_before_device_access(L):
+    """The no-allocation form validates like ar_residual_rmsnorm and rejects more rows than its
+    device array holds, all before any device access (fake pointers); M = 0 is a no-op."""
+    p = [0x10000 * (i + 1) for i in range(16)]
+    H = 7168
+    res, gam, ro, no = 0x1000000, 0x2000000, 0x3000000, 0x4000000
+
+    def call(M, ins=p[:8], W=8, eps=1e-6, r_out=ro, n_out=no):
+        return L.ar_residual_rmsnorm_noalloc(_ptrs(ins), W, M, H, BF16, res, gam, eps, r_out,
+                                             n_out, None)
+
+    assert ar.NOALLOC_MAX_ROWS == 512
+    assert call(ar.NOALLOC_MAX_ROWS + 1) == ar.AR_ERR_UNSUPPORTED
+    assert call(1 << 20) == ar.AR_ERR_UNSUPPORTED
+    assert call(4, ins=p[:12], W=12) == ar.AR_ERR_UNSUPPORTED
+    assert call(4, eps=-1.0) == ar.AR_ERR_INVALID_ARG
+    assert call(4, n_out=ro) == ar.AR_ERR_ALIAS
+    assert call(4, r_out=ro + 8) == ar.AR_ERR_MISALIGNED
+    assert L.ar_residual_rmsnorm_noalloc(None, 8, 0, H, BF16, None, None, 1e-6, None, None,
+                                         None) == ar.AR_OK

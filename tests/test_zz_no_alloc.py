@@ -1,0 +1,59 @@
+"""The no-allocation entry point against the workspace form it shares its kernels with.
+
+ar_residual_rmsnorm_noalloc keeps the split kernel's exchange slots in a device array of the
+library instead of a caller workspace.  Two calls in a row -- the second with fewer rows, so the
+array holds the first call's state -- must each give what ar_residual_rmsnorm_ws gives with a
+fresh caller workspace (residual_out and norm_out bit-identical: the same kernel and launch
+shape), and what the oracle gives (residual_out bit-identical, norm_out within the norm bar).
+"""
+import pytest
+import torch
+
+import all_reduce_residual_amd as ar
+import synth
+from gpu_util import assert_bit_exact, assert_norm_close, dev, host_np
+
+pytestmark = pytest.mark.gpu
+
+# (W, M, H, element type): the planner splits these rows over several blocks, then fewer rows.
+CALLS = [(8, 16, 7168, "bf16"), (8, 3, 7168, "bf16"), (16, 9, 8192, "fp16"), (8, 1, 7168, "fp32")]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+    ar.lib()
+
+
+def test_noalloc_matches_workspace_form(oracle_mod):
+    for i, (W, M, H, dtype) in enumerate(CALLS):
+        print("case noalloc call", i, W, M, H, dtype, flush=True)
+        code = {"bf16": ar.DTYPE_BF16, "fp16": ar.DTYPE_FP16, "fp32": ar.DTYPE_FP32}[dtype]
+        assert ar.ar_split_config(W, M, H, code)["segments"] > 1
+        parts, res, gam = synth.custom(W, M, H, dtype, seed=31 + i)
+        d_parts, d_res, d_gam = [dev(p) for p in parts], dev(res), dev(gam)
+        ro_a, no_a = torch.empty_like(d_res), torch.empty_like(d_res)
+        ro_b, no_b = torch.empty_like(d_res), torch.empty_like(d_res)
+        ws = ar.new_workspace(M, "cuda")
+        torch.cuda.synchronize()
+        ar.ar_residual_rmsnorm_ws(d_parts, d_res, d_gam, 1e-6, ro_a, no_a, ws)
+        ar.ar_residual_rmsnorm_noalloc(d_parts, d_res, d_gam, 1e-6, ro_b, no_b)
+        torch.cuda.synchronize()
+        assert_bit_exact(host_np(ro_b.cpu()), host_np(ro_a.cpu()), dtype, "residual_out")
+        assert_bit_exact(host_np(no_b.cpu()), host_np(no_a.cpu()), dtype, "norm_out")
+        want_ro, want_no = oracle_mod.ar_residual_rmsnorm([host_np(p) for p in parts],
+                                                          host_np(res), gam.numpy(), 1e-6, dtype)
+        assert_bit_exact(host_np(ro_b.cpu()), want_ro, dtype, "residual_out vs oracle")
+        assert_norm_close(host_np(no_b.cpu()), want_no, dtype)
+
+
+def test_noalloc_rows_beyond_the_array_rejected():
+    W, M, H = 2, ar.NOALLOC_MAX_ROWS + 1, 256
+    parts, res, gam = synth.custom(W, M, H, "bf16", seed=5)
+    d_parts, d_res = [dev(p) for p in parts], dev(res)
+    ro, no = torch.empty_like(d_res), torch.empty_like(d_res)
+    with pytest.raises(ar.ArError) as e:
+        ar.ar_residual_rmsnorm_noalloc(d_parts, d_res, dev(gam), 1e-6, ro, no)
+    assert e.value.status == ar.AR_ERR_UNSUPPORTED
