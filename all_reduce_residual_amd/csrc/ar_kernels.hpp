@@ -849,6 +849,7 @@ __device__ inline void store_row_vec(void* y, const float* gamma, int64_t e0, in
 // per wave and is free again when this returns.
 __device__ inline float block_sum(float v, float* red) {
   v = segment_sum(v, 64);
+  if (blockDim.x == 64) return v;  // one wave: its sum is the block's
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
   float t = red[0];
@@ -1107,6 +1108,8 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_split_kernel(
   }
   const float mine = block_sum(ss, red);
 
+  float total = 0.0f;  // the row's sum of squares (every thread, once known)
+  bool all = false;    // every segment's sum arrived
   if (tid < 64) {
     const int lane = tid;
     const uint32_t want =
@@ -1118,23 +1121,42 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_split_kernel(
     }
     if (s == S - 1 && lane >= S)
       __hip_atomic_store(row + lane, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // Polls with two loads in flight: each check waits for the older load only, so a value
+    // that lands between two polls is seen about half a round trip sooner than with one poll
+    // at a time.
     bool have = lane >= S || lane == s;
-    for (uint32_t n = 0; __builtin_amdgcn_ballot_w64(!have) != 0 && n < max_polls; ++n) {
-      if (n > 0) __builtin_amdgcn_s_sleep(1);
-      if (!have) {
-        slot = __hip_atomic_load(row + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        have = static_cast<uint32_t>(slot >> 32) == want;
+    if (__builtin_amdgcn_ballot_w64(!have) != 0 && max_polls > 0) {
+      uint64_t a = have ? slot : __hip_atomic_load(row + lane, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+      for (uint32_t n = 1;; ++n) {
+        const bool more = n < max_polls;
+        uint64_t b = a;
+        if (!have && more)
+          b = __hip_atomic_load(row + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (!have && static_cast<uint32_t>(a >> 32) == want) {
+          slot = a;
+          have = true;
+        }
+        if (__builtin_amdgcn_ballot_w64(!have) == 0 || !more) break;
+        a = b;
       }
     }
-    const bool all = __builtin_amdgcn_ballot_w64(!have) == 0;
-    if (all) {
-      const float p = segment_sum(lane < S ? __uint_as_float(static_cast<uint32_t>(slot)) : 0.0f, 64);
-      if (lane == 0) total_sh = p;
+    all = __builtin_amdgcn_ballot_w64(!have) == 0;
+    if (all) total = segment_sum(lane < S ? __uint_as_float(static_cast<uint32_t>(slot)) : 0.0f, 64);
+    if (blockDim.x > 64) {
+      if (lane == 0) {
+        total_sh = total;
+        missing_sh = all ? 0 : 1;
+      }
     }
-    if (lane == 0) missing_sh = all ? 0 : 1;
   }
-  __syncthreads();
-  if (missing_sh) {
+  // One wave: wave 0 is the block and holds the total already.
+  if (blockDim.x > 64) {
+    __syncthreads();
+    total = total_sh;
+    all = missing_sh == 0;
+  }
+  if (!all) {
     // Some segment did not arrive in time: compute every segment's partial sum here.
     for (int j = 0; j < S; ++j) {
       float pj = mine;
@@ -1153,8 +1175,9 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_split_kernel(
       if (tid == 0) total_sh = p;
     }
     __syncthreads();
+    total = total_sh;
   }
-  const float rstd = rsqrtf(total_sh / count_h + eps);
+  const float rstd = rsqrtf(total / count_h + eps);
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
     if (ok[k]) {
@@ -1171,7 +1194,7 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_split_kernel(
   // over the values above.  The exchange carries unscaled segment sums, so every block of the
   // row recomputes the other segments (re-reading their inputs) and adds them in segment order
   // the same way: all blocks reach the same sum.
-  const float x32 = total_sh / count_h + eps;
+  const float x32 = total / count_h + eps;
   if (outside_binary32_range(x32)) {
     const int E = wide_scale(x32);
     float sq = 0.0f;
