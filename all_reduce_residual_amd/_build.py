@@ -16,8 +16,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 SOURCES = ["ar_fused.hip", "inst_bf16.hip", "inst_f16.hip", "inst_f32.hip"]
 LIB = os.path.join(PKG, "libar_fused.so")
-# The benchmark's streaming-bandwidth calibration (include/ar_probe.h), a library of its own.
-PROBE_SOURCES = ["stream_probe.hip"]
+# The benchmark's probes (bench_probes/ar_probe.h: the streaming-bandwidth calibration and the
+# phase timing), a library of their own that the all-reduce library does not contain.
+PROBES = os.path.join(PKG, "bench_probes")
+PROBE_SOURCES = ["stream_probe.hip", "phase_probe.hip"]
 PROBE_LIB = os.path.join(PKG, "libar_probe.so")
 ARCH = "gfx950"
 
@@ -40,15 +42,16 @@ def hipcc() -> str:
 
 
 def build(extra_flags=(), out: str = LIB, jobs: int = 0, probe: bool = True) -> str:
-    """Build the library (and, with `probe`, the calibration probe library) and return the
+    """Build the library (and, with `probe`, the benchmark's probe library) and return the
     library's path (always recompiles)."""
     inc = "-I" + os.path.join(ROOT, "include")
-    sources = SOURCES + (PROBE_SOURCES if probe else [])
+    sources = [os.path.join(CSRC, x) for x in SOURCES]
+    if probe:
+        sources += [os.path.join(PROBES, x) for x in PROBE_SOURCES]
     jobs = jobs or min(len(sources), os.cpu_count() or 1)
     with tempfile.TemporaryDirectory(prefix="ar_build_") as tmpdir:
-        def compile_one(src):
-            stem = os.path.join(tmpdir, os.path.splitext(src)[0])
-            path = os.path.join(CSRC, src)
+        def compile_one(path):
+            stem = os.path.join(tmpdir, os.path.splitext(os.path.basename(path))[0])
             subprocess.run([hipcc()] + COMMON_FLAGS + DEVICE_FLAGS + list(extra_flags) +
                            [inc, "--cuda-device-only", "-c", "-o", stem + ".hipfb", path],
                            check=True)

@@ -37,6 +37,13 @@
 
 #include <type_traits>
 
+// Phase hooks: the benchmark's timing probe defines AR_PHASE(phase, value, tensor) before it
+// includes this header, to record when a block reaches each phase of a kernel (after `value` is
+// computed; `tensor` identifies the call); in the library they expand to nothing.
+#ifndef AR_PHASE
+#define AR_PHASE(phase, value, tensor) ((void)0)
+#endif
+
 namespace arf {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -437,10 +444,12 @@ template <class T, int W, int U, bool kNtStore, class Src = StreamSource>
 __global__ __launch_bounds__(kMaxThreads) void ar_sum_kernel(RankPtrs<W> in, u32x4* out,
                                                              int64_t nvec, int tail, Src src) {
   constexpr int kVec = T::kVec;
+  AR_PHASE(0, 0, in.p[0]);
   const int64_t chunk = static_cast<int64_t>(blockDim.x) * U;
   if (static_cast<int64_t>(gridDim.x) * chunk >= nvec) {
     const int64_t cbase = blockIdx.x * chunk;
     if (cbase < nvec) sum_chunk<T, W, U, kNtStore>(in, out, nvec, cbase, chunk, src);
+    AR_PHASE(7, 0, in.p[0]);
   } else {
     for (int64_t cbase = blockIdx.x * chunk; cbase < nvec; cbase += gridDim.x * chunk)
       sum_chunk<T, W, U, kNtStore>(in, out, nvec, cbase, chunk, src);
@@ -611,6 +620,7 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_kernel(
     }
   };
 
+  AR_PHASE(0, 0, in.p[0]);
   int bank = 0;
   // Whether a row of this wave (of this block, for rows of several waves) was outside the
   // binary32 range of the sum of squares: with the partials' sum those rows are normalised
@@ -688,6 +698,7 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_kernel(
         batch_fence(acc);
       }
     }
+    AR_PHASE(1, rounded[0].x, in.p[0]);
     float ss = 0.0f;
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
@@ -713,6 +724,7 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_kernel(
       bank ^= 1;
     }
     const float rstd = rsqrtf(ss / count_h + eps);
+    AR_PHASE(2, rstd, in.p[0]);
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
       if (ok[k]) {
@@ -727,6 +739,7 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_kernel(
       }
     }
 
+    AR_PHASE(7, 0, in.p[0]);
     // Rows outside the binary32 range of the sum of squares get norm_out again, from the same
     // rounded values scaled by 2^kw, stored over the values above.  The fused patterns do that
     // after the chunk (re-reading residual_out), so that the row loop holds exactly the code it
@@ -1083,6 +1096,7 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_split_kernel(
   __shared__ int missing_sh;
 
   const int tid = threadIdx.x;
+  AR_PHASE(0, 0, in.p[0]);
   const int m = blockIdx.x / S;
   const int s = blockIdx.x - m * S;
   const int64_t base = static_cast<int64_t>(m) * V;
@@ -1102,11 +1116,13 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_split_kernel(
   for (int k = 0; k < VPT; ++k) load_gamma(gamma, boff[k] / 16u, gam[k]);
   u32x4 rounded[VPT];
   const float ss = split_segment<T, W, VPT>(in, residual, base, boff, ok, rounded);
+  AR_PHASE(1, ss, in.p[0]);
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
     if (ok[k]) store_vec<kNtStore>(at(residual_out + base, boff[k]), rounded[k]);
   }
   const float mine = block_sum(ss, red);
+  AR_PHASE(2, mine, in.p[0]);
 
   float total = 0.0f;  // the row's sum of squares (every thread, once known)
   bool all = false;    // every segment's sum arrived
@@ -1124,6 +1140,7 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_split_kernel(
     // Polls with two loads in flight: each check waits for the older load only, so a value
     // that lands between two polls is seen about half a round trip sooner than with one poll
     // at a time.
+    AR_PHASE(3, slot, in.p[0]);
     bool have = lane >= S || lane == s;
     if (__builtin_amdgcn_ballot_w64(!have) != 0 && max_polls > 0) {
       uint64_t a = have ? slot : __hip_atomic_load(row + lane, __ATOMIC_RELAXED,
@@ -1142,6 +1159,7 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_split_kernel(
       }
     }
     all = __builtin_amdgcn_ballot_w64(!have) == 0;
+    AR_PHASE(4, static_cast<int>(all), in.p[0]);
     if (all) total = segment_sum(lane < S ? __uint_as_float(static_cast<uint32_t>(slot)) : 0.0f, 64);
     if (blockDim.x > 64) {
       if (lane == 0) {
@@ -1178,6 +1196,7 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_split_kernel(
     total = total_sh;
   }
   const float rstd = rsqrtf(total / count_h + eps);
+  AR_PHASE(5, rstd, in.p[0]);
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
     if (ok[k]) {
@@ -1189,6 +1208,7 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_split_kernel(
       store_vec<kNtStore>(at(norm_out + base, boff[k]), T::narrow(y));
     }
   }
+  AR_PHASE(7, 0, in.p[0]);
   // A row outside the binary32 range of the sum of squares (total_sh is the same in every thread
   // of the block: the branch is uniform): norm_out again from the values scaled by 2^E, stored
   // over the values above.  The exchange carries unscaled segment sums, so every block of the

@@ -24,6 +24,9 @@ Modes:
                          per-M median in-kernel duration of the wide-hidden sweep kernels from a
                          rocprofv3 --kernel-trace dir, beside the per-call graph times of a
                          bench JSON line
+  --phases               markdown table: where a decode-size call's time goes (the library's
+                         kernels rebuilt with their phase hooks stamping a clock, beside the
+                         same calls timed without them)
 """
 from __future__ import annotations
 
@@ -315,7 +318,7 @@ def lamport_lines(ar, torch, W=8, H=7168, Ms=(8, 128, 2048)) -> list:
 
 
 class ProbeCase(Case):
-    """The calibration probe (include/ar_probe.h): `nr` read streams and `nw` write streams of
+    """The calibration probe (bench_probes/ar_probe.h): `nr` read streams and `nw` write streams of
     M x H bf16 each with no arithmetic that matters, R rotated sets."""
 
     def __init__(self, torch, L, nr, nw, M, H):
@@ -368,6 +371,67 @@ def stream_ceiling(torch, H=None, Ms=(2048, 512)) -> list:
             del c
             torch.cuda.empty_cache()
     return lines
+
+
+PHASE_NAMES = {
+    0: ("loads done", "", "", "", ""),
+    1: ("loads done", "rstd (row reduced)", "", "", ""),
+    2: ("segment loaded", "segment sum of squares", "slot published", "all slots seen",
+        "rstd"),
+}
+
+
+def phase_table(ar, torch) -> str:
+    """Where the time of a decode-size call goes (markdown).  For each launch shape the library
+    plans: µs per call of the library call itself (hipGraph replay, rotated sets, no stamps),
+    then the same kernel rebuilt with its phase hooks storing the 100 MHz clock per block
+    (ar_probe_phases): per call, the kernel span (first block's entry to the last block's last
+    store issued), the gap from one kernel's last store issued to the next kernel's first
+    block, and each phase's latest block, from the kernel's first entry."""
+    path = os.path.join(ROOT, "all_reduce_residual_amd", "libar_probe.so")
+    P = ctypes.CDLL(path)
+    P.ar_probe_phases.argtypes = [ctypes.c_int] * 8 + [ctypes.POINTER(ctypes.c_double)]
+    P.ar_probe_phases.restype = ctypes.c_int
+    cases = []
+    for W, H, Ms in ((8, 7168, (1, 8, 32, 128)), (2, 4096, (128,))):
+        for M in Ms:
+            cs = ar.ar_launch_config(ar.PATTERN_ALLREDUCE, W, M, H, ar.DTYPE_BF16)
+            cn = ar.ar_launch_config(ar.PATTERN_AR_RESIDUAL_RMSNORM, W, M, H, ar.DTYPE_BF16)
+            sp = ar.ar_split_config(W, M, H, ar.DTYPE_BF16)
+            if W == 8 and M <= 32 and cs["vecs_per_thread"] in (1, 2):
+                cases.append(("kAllReduce", "sum", 0, W, M, H, cs["threads_per_block"],
+                              cs["vecs_per_thread"], cs["grid"], 0))
+            if cn["rows_per_block"] == 1 and cn["vecs_per_thread"] in (1, 2):
+                cases.append(("kARResidualRMSNorm, one block per row", "rms", 1, W, M, H,
+                              cn["threads_per_block"], cn["vecs_per_thread"], cn["grid"], 0))
+            if sp["segments"]:
+                cases.append(("kARResidualRMSNorm, %d segments per row" % sp["segments"],
+                              "rms_ws", 2, W, M, H, sp["threads_per_block"], 1,
+                              M * sp["segments"], sp["segments"]))
+    cases.insert(0, ("empty kernel (launch floor)", None, 3, 8, 1, 7168, 64, 1, 1, 0))
+    rows = ["| kernel | W | M | H | launch | per call, library (µs) | per call, stamped (µs) "
+            "| span (µs) | gap (µs) | phases (µs after the first block's entry) |",
+            "|---|---|---|---|---|---|---|---|---|---|"]
+    for name, pat, kind, W, M, H, threads, vpt, grid, seg in cases:
+        out = (ctypes.c_double * 11)()
+        st = P.ar_probe_phases(kind, W, M, H, threads, vpt, grid, seg, out)
+        if st != 0:
+            raise RuntimeError("ar_probe_phases failed (%d) for %s W=%d M=%d" % (st, name, W, M))
+        lib_us = None
+        if pat is not None:
+            c = Case(ar, torch, pat, W, M, H)
+            lib_us = c.time_graph(c.calls_per_batch(200), reps=7)
+            del c
+            torch.cuda.empty_cache()
+        names = PHASE_NAMES.get(kind, ())
+        ph = ", ".join("%s %.2f" % (names[i], out[3 + i]) for i in range(len(names))
+                       if names[i] and out[3 + i] >= 0)
+        launch = "%d x %d thr x %d vec" % (grid, threads, vpt)
+        rows.append("| %s | %d | %d | %d | %s | %s | %.2f | %.2f | %.2f | %s |" % (
+            name, W, M, H, launch, "%.2f" % lib_us if lib_us is not None else "—", out[0],
+            out[1], out[2], ph or "—"))
+        print("# phases %s" % rows[-1], file=sys.stderr, flush=True)
+    return "\n".join(rows)
 
 
 def two_shot_lines(ar, torch, W=8, H=7168, Ms=(128, 512, 2048)) -> list:
@@ -795,6 +859,7 @@ def main():
     ap.add_argument("--summarize-stats", metavar="DIR")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-sweep-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_JSON"))
+    ap.add_argument("--phases", action="store_true")
     args = ap.parse_args()
 
     if args.summarize_sweep_trace:
@@ -820,6 +885,9 @@ def main():
         return 1
     torch.cuda.set_device(0)
     ar.lib()
+    if args.phases:
+        print(phase_table(ar, torch))
+        return 0
 
     H, W, M = HEADLINE["H"], HEADLINE["W"], HEADLINE["M"]
     if args.mode == "pmc":

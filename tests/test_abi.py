@@ -319,15 +319,16 @@ def test_unfused_and_rmsnorm_validation(L):
 
 
 def test_probe_library_exports_and_rejects():
-    """The benchmark's calibration probe (include/ar_probe.h) is a library of its own; it exports
-    its one function and rejects malformed calls before any device access."""
+    """The benchmark's probes (bench_probes/ar_probe.h) are a library of their own; it exports
+    its two functions and rejects malformed calls before any device access."""
     import os
     import re
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     path = os.path.join(root, "all_reduce_residual_amd", "libar_probe.so")
-    with open(os.path.join(root, "include", "ar_probe.h")) as f:
+    with open(os.path.join(root, "all_reduce_residual_amd", "bench_probes", "ar_probe.h")) as f:
         text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
-    assert re.findall(r"^\s*int\s+(ar_\w+)\s*\(", text, flags=re.M) == ["ar_probe_stream"]
+    assert re.findall(r"^\s*int\s+(ar_\w+)\s*\(", text, flags=re.M) == ["ar_probe_stream",
+                                                                     "ar_probe_phases"]
     P = ctypes.CDLL(path)
     fn = P.ar_probe_stream
     fn.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p,
@@ -340,6 +341,18 @@ def test_probe_library_exports_and_rejects():
     assert fn(p, 9, 2, 64, 0x900008, 0xA00000, 64, None) == 1      # misaligned output
     assert fn(None, 9, 2, 64, 0x900000, 0xA00000, 64, None) == 1
     assert fn(p, 9, 2, 0, 0x900000, 0xA00000, 64, None) == 0       # nothing to do
+    ph = P.ar_probe_phases
+    ph.argtypes = [ctypes.c_int] * 8 + [ctypes.POINTER(ctypes.c_double)]
+    ph.restype = ctypes.c_int
+    out = (ctypes.c_double * 11)()
+    assert ph(0, 8, 1, 7168, 64, 2, 6, 0, out) == 1      # grid does not cover the row
+    assert ph(1, 8, 2, 7168, 448, 2, 1, 0, out) == 1     # one block per row: grid = M
+    assert ph(1, 8, 1, 7168, 256, 2, 1, 0, out) == 1     # 256 x 2 vectors < 896
+    assert ph(2, 8, 1, 7168, 64, 1, 14, 13, out) == 1    # segments x threads < 896
+    assert ph(2, 8, 1, 7168, 64, 1, 13, 14, out) == 1    # grid != M x segments
+    assert ph(1, 3, 1, 7168, 448, 2, 1, 0, out) == 1     # world size
+    assert ph(4, 8, 1, 7168, 448, 2, 1, 0, out) == 1     # kind
+    assert ph(1, 8, 1, 7168, 448, 2, 1, 0, None) == 1
 
 
 def test_split_workspace_bytes(L):
