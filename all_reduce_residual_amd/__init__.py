@@ -106,9 +106,9 @@ def lib():
             "ar_launch_config": [i32, i32, i64, i64, i32, i32, cfgp],
             "ar_status_string": [i32],
             "ar_lamport_arm": [vp, i32, i64, i64, i32, vp],
-            "ar_lamport_push": [vp, i32, vp, i32, i64, i64, i32, vp],
-            "ar_lamport_sum": [vp, i32, i64, i64, i32, vp, vp, ctypes.c_uint32, vp],
-            "ar_lamport_residual_rmsnorm": [vp, i32, i64, i64, i32, vp, vp, f32, vp, vp, vp,
+            "ar_lamport_push": [vp, i32, vp, i32, i64, i64, i32, i64, vp],
+            "ar_lamport_sum": [vp, i32, i64, i64, i32, i64, vp, vp, ctypes.c_uint32, vp],
+            "ar_lamport_residual_rmsnorm": [vp, i32, i64, i64, i32, i64, vp, vp, f32, vp, vp, vp,
                                             ctypes.c_uint32, vp],
             "ar_policy_default": [i32, ctypes.POINTER(Policy)],
             "ar_route": [i32, i32, i64, i64, i32, ctypes.POINTER(Policy),
@@ -361,13 +361,17 @@ def ar_all_gather(slices, out, stream=None) -> None:
     _check(st, "ar_all_gather")
 
 
+LAMPORT_BUFFERS = 3
+
+
 def _check_rbuf(rbuf, like=None):
-    if rbuf.dim() != 3 or not rbuf.is_cuda or not rbuf.is_contiguous():
-        raise ValueError("rbuf must be a contiguous [W, M, H] GPU tensor")
-    if like is not None and (like.dtype != rbuf.dtype or tuple(like.shape) != tuple(rbuf.shape[1:])
+    if rbuf.dim() != 4 or rbuf.shape[0] != LAMPORT_BUFFERS or not rbuf.is_cuda \
+            or not rbuf.is_contiguous():
+        raise ValueError("rbuf must be a contiguous [%d, W, M, H] GPU tensor" % LAMPORT_BUFFERS)
+    if like is not None and (like.dtype != rbuf.dtype or tuple(like.shape) != tuple(rbuf.shape[2:])
                              or like.device != rbuf.device or not like.is_contiguous()):
         raise ValueError("tensor must be a contiguous [M, H] %s on %s" % (rbuf.dtype, rbuf.device))
-    W, M, H = rbuf.shape
+    _, W, M, H = rbuf.shape
     return W, M, H, dtype_code(rbuf.dtype)
 
 
@@ -378,30 +382,32 @@ def _check_status(status, device):
 
 
 def ar_lamport_arm(rbuf, stream=None) -> None:
-    """Empty every slot of the receive buffer rbuf ([W, M, H])."""
+    """Empty every slot of the receive buffers rbuf ([3, W, M, H])."""
     W, M, H, dt = _check_rbuf(rbuf)
     _check(lib().ar_lamport_arm(rbuf.data_ptr(), W, M, H, dt, _stream_handle(stream, rbuf.device)),
            "ar_lamport_arm")
 
 
-def ar_lamport_push(partial, rank: int, rbuf, stream=None) -> None:
-    """Producer of `rank`: write `partial` ([M, H]) into its slot of rbuf."""
+def ar_lamport_push(partial, rank: int, rbuf, round: int, stream=None) -> None:
+    """Producer of `rank` in round `round`: write `partial` ([M, H]) into its slot of buffer
+    round % 3 and empty its slot of buffer (round + 1) % 3."""
     W, M, H, dt = _check_rbuf(rbuf, partial)
-    _check(lib().ar_lamport_push(partial.data_ptr(), rank, rbuf.data_ptr(), W, M, H, dt,
+    _check(lib().ar_lamport_push(partial.data_ptr(), rank, rbuf.data_ptr(), W, M, H, dt, round,
                                  _stream_handle(stream, rbuf.device)), "ar_lamport_push")
 
 
-def ar_lamport_sum(rbuf, out, status, spin_limit: int = 0, stream=None) -> None:
-    """Consumer, kAllReduce: out = sum of the W slots; re-empties them."""
+def ar_lamport_sum(rbuf, round: int, out, status, spin_limit: int = 0, stream=None) -> None:
+    """Consumer of round `round`, kAllReduce: out = sum of the W slots of buffer round % 3."""
     W, M, H, dt = _check_rbuf(rbuf, out)
     _check_status(status, rbuf.device)
-    _check(lib().ar_lamport_sum(rbuf.data_ptr(), W, M, H, dt, out.data_ptr(), status.data_ptr(),
-                                spin_limit, _stream_handle(stream, rbuf.device)), "ar_lamport_sum")
+    _check(lib().ar_lamport_sum(rbuf.data_ptr(), W, M, H, dt, round, out.data_ptr(),
+                                status.data_ptr(), spin_limit, _stream_handle(stream, rbuf.device)),
+           "ar_lamport_sum")
 
 
-def ar_lamport_residual_rmsnorm(rbuf, residual, gamma, eps: float, residual_out, norm_out, status,
-                                spin_limit: int = 0, stream=None) -> None:
-    """Consumer, kARResidualRMSNorm over the W slots; re-empties them."""
+def ar_lamport_residual_rmsnorm(rbuf, round: int, residual, gamma, eps: float, residual_out,
+                                norm_out, status, spin_limit: int = 0, stream=None) -> None:
+    """Consumer of round `round`, kARResidualRMSNorm over the W slots of buffer round % 3."""
     import torch
     W, M, H, dt = _check_rbuf(rbuf, residual)
     _check_rbuf(rbuf, residual_out)
@@ -411,7 +417,7 @@ def ar_lamport_residual_rmsnorm(rbuf, residual, gamma, eps: float, residual_out,
             or gamma.device != rbuf.device:
         raise ValueError("gamma must be a contiguous float32 [%d] tensor on %s" % (H, rbuf.device))
     st = lib().ar_lamport_residual_rmsnorm(
-        rbuf.data_ptr(), W, M, H, dt, residual.data_ptr(), gamma.data_ptr(), float(eps),
+        rbuf.data_ptr(), W, M, H, dt, round, residual.data_ptr(), gamma.data_ptr(), float(eps),
         residual_out.data_ptr(), norm_out.data_ptr(), status.data_ptr(), spin_limit,
         _stream_handle(stream, rbuf.device))
     _check(st, "ar_lamport_residual_rmsnorm")

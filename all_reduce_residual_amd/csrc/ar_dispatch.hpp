@@ -129,7 +129,7 @@ inline hipError_t launch_norm_t(const void* const* inputs, int W, const void* re
 }
 
 
-// ---- Lamport-style exchange (receive buffer of W slots, slot r at rbuf + r * slot_vecs) -----------
+// ---- Lamport-style exchange (one receive buffer of W slots, slot r at rbuf + r * slot_vecs) -------
 
 template <int W>
 RankPtrs<W> slot_ptrs(const void* rbuf, int64_t slot_vecs) {
@@ -235,11 +235,12 @@ inline hipError_t launch_lamport_norm_t(void* rbuf, int W, const void* residual,
 }
 
 template <class T>
-inline hipError_t launch_lamport_push_t(const void* partial, void* slot, int64_t nvec, int grid,
-                                        hipStream_t s) {
+inline hipError_t launch_lamport_push_t(const void* partial, void* slot, void* next, int64_t nvec,
+                                        int grid, hipStream_t s) {
   const u32x4* src = static_cast<const u32x4*>(partial);
   u32x4* dst = static_cast<u32x4*>(slot);
-  void* args[] = {&src, &dst, &nvec};
+  u32x4* nxt = static_cast<u32x4*>(next);
+  void* args[] = {&src, &dst, &nxt, &nvec};
   return hipLaunchKernel(reinterpret_cast<const void*>(&arf::ar_lamport_push_kernel<T>),
                          dim3(grid), dim3(256), args, 0, s);
 }
@@ -392,8 +393,8 @@ inline hipError_t launch_norm_split_t(const void* const* inputs, int W, const vo
                                           void* norm_out, int64_t M, int64_t H,               \
                                           const ar_launch_cfg_t& c, arf::LamportSource src,   \
                                           hipStream_t s);                                     \
-  hipError_t launch_lamport_push_##suffix(const void* partial, void* slot, int64_t nvec,      \
-                                          int grid, hipStream_t s);                           \
+  hipError_t launch_lamport_push_##suffix(const void* partial, void* slot, void* next,        \
+                                          int64_t nvec, int grid, hipStream_t s);             \
   hipError_t launch_sum_residual_##suffix(const void* const* inputs, int W,                   \
                                           const void* residual, void* out, int64_t nvec,      \
                                           int tail, const ar_launch_cfg_t& c, hipStream_t s); \

@@ -804,11 +804,13 @@ constexpr uint32_t kDefaultSpinLimit = 1u << 16;
 // spills at 8), so rows of up to 1024 lanes x that many 16-byte vectors.
 int lamport_max_vpt(int W) { return W <= 4 ? 8 : 4; }
 
+constexpr int kLamportBuffers = AR_LAMPORT_BUFFERS;
+
 int check_lamport_shape(int pattern, int W, int64_t M, int64_t H, int dtype) {
   int st = check_shape(AR_PATTERN_ALLREDUCE, W, M, H, dtype);
   if (st != AR_OK) return st;
-  // The receive buffer is W slots: keep W * M * H * es <= 2^60 as well.
-  if (M > 0 && H > ((int64_t(1) << 60) / (int64_t(W) * elem_size(dtype))) / M)
+  // The receive buffer is 3 x W slots: keep 3 W M H es <= 2^60 as well.
+  if (M > 0 && H > ((int64_t(1) << 60) / (int64_t(kLamportBuffers) * W * elem_size(dtype))) / M)
     return AR_ERR_UNSUPPORTED;
   const int64_t vec = kVecBytes / elem_size(dtype);
   if (H % vec != 0) return AR_ERR_UNSUPPORTED;
@@ -831,7 +833,7 @@ int run_lamport_arm(void* rbuf, int W, int64_t M, int64_t H, int dtype, void* st
   st = query_cu_count(&cu);
   if (st != AR_OK) return st;
   u32x4* buf = static_cast<u32x4*>(rbuf);
-  int64_t nvec = int64_t(W) * M * H * elem_size(dtype) / kVecBytes;
+  int64_t nvec = int64_t(kLamportBuffers) * W * M * H * elem_size(dtype) / kVecBytes;
   void* args[] = {&buf, &nvec};
   const hipError_t e =
       hipLaunchKernel(reinterpret_cast<const void*>(&arf::ar_lamport_arm_kernel<u32x4>),
@@ -840,20 +842,29 @@ int run_lamport_arm(void* rbuf, int W, int64_t M, int64_t H, int dtype, void* st
   return e == hipSuccess ? AR_OK : AR_ERR_LAUNCH;
 }
 
+// Byte offset of slot `rank` of the buffer round `round` uses.
+int64_t lamport_slot(int64_t round, int W, int rank, int64_t slot_bytes) {
+  return (int64_t(round % kLamportBuffers) * W + rank) * slot_bytes;
+}
+
 int run_lamport_push(const void* partial, int rank, void* rbuf, int W, int64_t M, int64_t H,
-                     int dtype, void* stream) {
+                     int dtype, int64_t round, void* stream) {
   int st = check_lamport_shape(AR_PATTERN_ALLREDUCE, W, M, H, dtype);
   if (st != AR_OK) return st;
-  if (rank < 0 || rank >= W) return AR_ERR_INVALID_ARG;
+  if (rank < 0 || rank >= W || round < 0) return AR_ERR_INVALID_ARG;
   if (M == 0) return AR_OK;
   if (!partial || !rbuf) return AR_ERR_INVALID_ARG;
   if (!aligned16(partial) || !aligned16(rbuf)) return AR_ERR_MISALIGNED;
   const int64_t slot_bytes = M * H * elem_size(dtype);
-  if (overlap(range_of(partial, slot_bytes), range_of(rbuf, slot_bytes * W))) return AR_ERR_ALIAS;
+  if (overlap(range_of(partial, slot_bytes), range_of(rbuf, slot_bytes * W * kLamportBuffers)))
+    return AR_ERR_ALIAS;
   int cu = 0;
   st = query_cu_count(&cu);
   if (st != AR_OK) return st;
-  void* slot = static_cast<char*>(rbuf) + rank * slot_bytes;
+  // This round's slot, and the same rank's slot of the next buffer (used two rounds ago), which
+  // this push empties.
+  void* slot = static_cast<char*>(rbuf) + lamport_slot(round, W, rank, slot_bytes);
+  void* next = static_cast<char*>(rbuf) + lamport_slot(round + 1, W, rank, slot_bytes);
   const int64_t nvec = slot_bytes / kVecBytes;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // One vector per thread and a grid that covers the slot: the kernel runs no loop.
@@ -861,9 +872,9 @@ int run_lamport_push(const void* partial, int rank, void* rbuf, int W, int64_t M
   const int grid = cap_grid(ceil_div(nvec, 256));
   hipError_t e;
   switch (dtype) {
-    case AR_DTYPE_FP32: e = arfh::launch_lamport_push_f32(partial, slot, nvec, grid, s); break;
-    case AR_DTYPE_FP16: e = arfh::launch_lamport_push_f16(partial, slot, nvec, grid, s); break;
-    default: e = arfh::launch_lamport_push_bf16(partial, slot, nvec, grid, s); break;
+    case AR_DTYPE_FP32: e = arfh::launch_lamport_push_f32(partial, slot, next, nvec, grid, s); break;
+    case AR_DTYPE_FP16: e = arfh::launch_lamport_push_f16(partial, slot, next, nvec, grid, s); break;
+    default: e = arfh::launch_lamport_push_bf16(partial, slot, next, nvec, grid, s); break;
   }
   return e == hipSuccess ? AR_OK : AR_ERR_LAUNCH;
 }
@@ -875,14 +886,16 @@ int check_lamport_buffers(void* rbuf, int W, int64_t M, int64_t H, int dtype, co
   if (!aligned16(rbuf)) return AR_ERR_MISALIGNED;
   if ((reinterpret_cast<uintptr_t>(status) & 3u) != 0) return AR_ERR_MISALIGNED;
   const int64_t slot_bytes = M * H * elem_size(dtype);
-  if (overlap(range_of(status, 4), range_of(rbuf, slot_bytes * W))) return AR_ERR_ALIAS;
+  if (overlap(range_of(status, 4), range_of(rbuf, slot_bytes * W * kLamportBuffers)))
+    return AR_ERR_ALIAS;
   return AR_OK;
 }
 
-int run_lamport_sum(void* rbuf, int W, int64_t M, int64_t H, int dtype, void* out, int* status,
-                    uint32_t spin_limit, void* stream) {
+int run_lamport_sum(void* rbuf, int W, int64_t M, int64_t H, int dtype, int64_t round, void* out,
+                    int* status, uint32_t spin_limit, void* stream) {
   int st = check_lamport_shape(AR_PATTERN_ALLREDUCE, W, M, H, dtype);
   if (st != AR_OK) return st;
+  if (round < 0) return AR_ERR_INVALID_ARG;
   if (M == 0) return AR_OK;
   if (!out) return AR_ERR_INVALID_ARG;
   st = check_lamport_buffers(rbuf, W, M, H, dtype, status);
@@ -890,8 +903,9 @@ int run_lamport_sum(void* rbuf, int W, int64_t M, int64_t H, int dtype, void* ou
   if (!aligned16(out)) return AR_ERR_MISALIGNED;
   const int64_t bytes = M * H * elem_size(dtype);
   const Range o = range_of(out, bytes);
-  if (overlap(o, range_of(rbuf, bytes * W)) || overlap(o, range_of(status, 4)))
+  if (overlap(o, range_of(rbuf, bytes * W * kLamportBuffers)) || overlap(o, range_of(status, 4)))
     return AR_ERR_ALIAS;
+  void* buf = static_cast<char*>(rbuf) + lamport_slot(round, W, 0, bytes);
   int cu = 0;
   st = query_cu_count(&cu);
   if (st != AR_OK) return st;
@@ -904,19 +918,19 @@ int run_lamport_sum(void* rbuf, int W, int64_t M, int64_t H, int dtype, void* ou
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   switch (dtype) {
-    case AR_DTYPE_FP32: e = arfh::launch_lamport_sum_f32(rbuf, W, M, H, out, cfg, src, s); break;
-    case AR_DTYPE_FP16: e = arfh::launch_lamport_sum_f16(rbuf, W, M, H, out, cfg, src, s); break;
-    default: e = arfh::launch_lamport_sum_bf16(rbuf, W, M, H, out, cfg, src, s); break;
+    case AR_DTYPE_FP32: e = arfh::launch_lamport_sum_f32(buf, W, M, H, out, cfg, src, s); break;
+    case AR_DTYPE_FP16: e = arfh::launch_lamport_sum_f16(buf, W, M, H, out, cfg, src, s); break;
+    default: e = arfh::launch_lamport_sum_bf16(buf, W, M, H, out, cfg, src, s); break;
   }
   return e == hipSuccess ? AR_OK : AR_ERR_LAUNCH;
 }
 
-int run_lamport_norm(void* rbuf, int W, int64_t M, int64_t H, int dtype, const void* residual,
-                     const float* gamma, float eps, void* residual_out, void* norm_out,
-                     int* status, uint32_t spin_limit, void* stream) {
+int run_lamport_norm(void* rbuf, int W, int64_t M, int64_t H, int dtype, int64_t round,
+                     const void* residual, const float* gamma, float eps, void* residual_out,
+                     void* norm_out, int* status, uint32_t spin_limit, void* stream) {
   int st = check_lamport_shape(AR_PATTERN_AR_RESIDUAL_RMSNORM, W, M, H, dtype);
   if (st != AR_OK) return st;
-  if (!std::isfinite(eps) || eps < 0.0f) return AR_ERR_INVALID_ARG;
+  if (!std::isfinite(eps) || eps < 0.0f || round < 0) return AR_ERR_INVALID_ARG;
   if (M == 0) return AR_OK;
   if (!residual || !gamma || !residual_out || !norm_out) return AR_ERR_INVALID_ARG;
   st = check_lamport_buffers(rbuf, W, M, H, dtype, status);
@@ -925,7 +939,7 @@ int run_lamport_norm(void* rbuf, int W, int64_t M, int64_t H, int dtype, const v
       !aligned16(norm_out))
     return AR_ERR_MISALIGNED;
   const int64_t bytes = M * H * elem_size(dtype);
-  const Range rb = range_of(rbuf, bytes * W);
+  const Range rb = range_of(rbuf, bytes * W * kLamportBuffers);
   const Range ro = range_of(residual_out, bytes);
   const Range no = range_of(norm_out, bytes);
   const Range res = range_of(residual, bytes);
@@ -969,19 +983,20 @@ int run_lamport_norm(void* rbuf, int W, int64_t M, int64_t H, int dtype, const v
   }
   cfg.nt_store = 1;
   arf::LamportSource src{status, spin_limit ? spin_limit : kDefaultSpinLimit};
+  void* buf = static_cast<char*>(rbuf) + lamport_slot(round, W, 0, bytes);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   switch (dtype) {
     case AR_DTYPE_FP32:
-      e = arfh::launch_lamport_norm_f32(rbuf, W, residual, gamma, eps, residual_out, norm_out, M,
+      e = arfh::launch_lamport_norm_f32(buf, W, residual, gamma, eps, residual_out, norm_out, M,
                                         H, cfg, src, s);
       break;
     case AR_DTYPE_FP16:
-      e = arfh::launch_lamport_norm_f16(rbuf, W, residual, gamma, eps, residual_out, norm_out, M,
+      e = arfh::launch_lamport_norm_f16(buf, W, residual, gamma, eps, residual_out, norm_out, M,
                                         H, cfg, src, s);
       break;
     default:
-      e = arfh::launch_lamport_norm_bf16(rbuf, W, residual, gamma, eps, residual_out, norm_out,
+      e = arfh::launch_lamport_norm_bf16(buf, W, residual, gamma, eps, residual_out, norm_out,
                                          M, H, cfg, src, s);
       break;
   }
@@ -1120,21 +1135,21 @@ int ar_lamport_arm(void* rbuf, int W, int64_t M, int64_t H, int dtype, void* str
 }
 
 int ar_lamport_push(const void* partial, int rank, void* rbuf, int W, int64_t M, int64_t H,
-                    int dtype, void* stream) {
-  return run_lamport_push(partial, rank, rbuf, W, M, H, dtype, stream);
+                    int dtype, int64_t round, void* stream) {
+  return run_lamport_push(partial, rank, rbuf, W, M, H, dtype, round, stream);
 }
 
-int ar_lamport_sum(void* rbuf, int W, int64_t M, int64_t H, int dtype, void* out, int* status,
-                   uint32_t spin_limit, void* stream) {
-  return run_lamport_sum(rbuf, W, M, H, dtype, out, status, spin_limit, stream);
+int ar_lamport_sum(void* rbuf, int W, int64_t M, int64_t H, int dtype, int64_t round, void* out,
+                   int* status, uint32_t spin_limit, void* stream) {
+  return run_lamport_sum(rbuf, W, M, H, dtype, round, out, status, spin_limit, stream);
 }
 
-int ar_lamport_residual_rmsnorm(void* rbuf, int W, int64_t M, int64_t H, int dtype,
+int ar_lamport_residual_rmsnorm(void* rbuf, int W, int64_t M, int64_t H, int dtype, int64_t round,
                                 const void* residual, const float* gamma, float eps,
                                 void* residual_out, void* norm_out, int* status,
                                 uint32_t spin_limit, void* stream) {
-  return run_lamport_norm(rbuf, W, M, H, dtype, residual, gamma, eps, residual_out, norm_out,
-                          status, spin_limit, stream);
+  return run_lamport_norm(rbuf, W, M, H, dtype, round, residual, gamma, eps, residual_out,
+                          norm_out, status, spin_limit, stream);
 }
 
 int ar_policy_default(int W, ar_policy_t* policy) {

@@ -1256,13 +1256,17 @@ __global__ __launch_bounds__(kMaxThreads) void ar_fill_zero_kernel(V* p, int64_t
 // ---- Lamport-style one-shot exchange (receive side) ---------------------------------------------
 //
 // The one-shot exchange of the MNNVL all-reduce (flashinfer pull request "Optimizations for
-// TRTLLM MNNVL Allreduce", Description and Summary: Lamport polling with vectorized loads, flags
-// kept in the data) needs no separate flag: a receive buffer holds one slot per rank, every
-// element of an empty slot holds a sentinel bit pattern (all ones: a NaN in every element type),
-// and a producer's data can never equal it because the producer replaces an all-ones element by
-// the same value with its lowest bit cleared (still a NaN).  The consumer polls each element until
-// it is not the sentinel, reduces, and writes the sentinel back so the slot is empty for the next
-// round.
+// TRTLLM MNNVL Allreduce", Description and Summary: Lamport polling with vectorized loads, buffer
+// state kept in the data) needs no separate flag: a receive slot per rank, every element of an
+// empty slot holding a sentinel bit pattern (all ones: a NaN in every element type), and a
+// producer's data can never equal it because the producer replaces an all-ones element by the same
+// value with its lowest bit cleared (still a NaN).  The consumer polls each element until it is not
+// the sentinel and reduces.  Three receive buffers rotate by round (round k uses buffer k mod 3):
+// the producer of round k writes its slot of buffer k mod 3 and empties its slot of buffer
+// (k + 1) mod 3, the one round k - 2 used, so the consumer only reads and the emptying is off its
+// path.  That buffer is free once every consumer of round k - 2 is done, which a rank's round-k
+// push implies when each rank pushes round k only after consuming round k - 1 (that consumer needed
+// every rank's round k - 1 push, made after its own consumer of round k - 2).
 //
 // Slots are moved as 16-byte buffer loads and stores carrying the device-coherence cache bit
 // (sc1, the form of a relaxed agent-scope atomic on this architecture) and the streaming hint:
@@ -1352,16 +1356,13 @@ struct LamportSource {
 
   // acc[k] = -0 + slot_0[k] + ... + slot_{W-1}[k]: all vectors of a batch are loaded first, then
   // only vectors still holding an empty element are polled again, then the batch is accumulated
-  // in rank order and re-armed with the sentinel.  Slots that are not real (ok[k] false) neither
-  // read nor re-arm anything: their clamped offset points at another lane's vector, which they
-  // must not empty.
+  // in rank order.  Slots that are not real (ok[k] false) read nothing.
   // (kStage is accepted for the common interface; the polled batch is staged already.)
   template <class T, int W, int N, int kMaxLoads = default_max_loads<T, N>(), bool kStage = false>
   __device__ inline void sum(const RankPtrs<W>& in, int64_t base, const uint32_t (&boff)[N],
                              const bool (&ok)[N], float (&acc)[N][T::kVec]) const {
     // Polled vectors stay live until accumulated: half the stream source's batch.
     constexpr int kBatch = rank_batch<W, N, (kMaxLoads / 2 > 0 ? kMaxLoads / 2 : 1)>();
-    const u32x4 empty = {~0u, ~0u, ~0u, ~0u};
     bool gave_up = false;
 #pragma unroll
     for (int k = 0; k < N; ++k) {
@@ -1392,17 +1393,6 @@ struct LamportSource {
           for (int e = 0; e < T::kVec; ++e) acc[k][e] = acc[k][e] + x[e];
         }
       }
-      // Re-arm the batch only after all of it is read: a store between two polls would make
-      // every later check wait for that store's round trip.
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        if (r0 + j >= W) break;
-        u32x4* slot = const_cast<u32x4*>(in.p[r0 + j] + base);
-#pragma unroll
-        for (int k = 0; k < N; ++k) {
-          if (ok[k]) store_coherent(slot, boff[k], empty);
-        }
-      }
       if (r0 + kBatch < W) batch_fence(acc);
     }
   }
@@ -1412,19 +1402,30 @@ struct LamportSource {
   __device__ inline float tail_extra(float a, int64_t) const { return a; }
 };
 
-// Producer: slot[i] = canonicalize(src[i]) for nvec 16-byte vectors, device-coherent stores.
-// One 16-byte vector per thread; a grid that covers every vector runs no loop.
+// Producer: next[i] = empty, then slot[i] = canonicalize(src[i]), for nvec 16-byte vectors,
+// device-coherent stores.  The thread waits for its emptying store to complete before it stores
+// the data, so the emptied vector is visible no later than the data: a consumer that has seen
+// this round's data, and every later kernel on its stream, sees next[i] empty, never the older
+// round's value.  One 16-byte
+// vector per thread; a grid that covers every vector runs no loop.
 template <class T>
 __global__ __launch_bounds__(kMaxThreads) void ar_lamport_push_kernel(const u32x4* src,
-                                                                      u32x4* slot, int64_t nvec) {
+                                                                      u32x4* slot, u32x4* next,
+                                                                      int64_t nvec) {
   const int64_t chunk = blockDim.x;
   const uint32_t boff = threadIdx.x * 16u;
+  const u32x4 empty = {~0u, ~0u, ~0u, ~0u};
   auto one = [&](int64_t cbase) {
     if (cbase + threadIdx.x < nvec) {
       const u32x4 v = load_stream(at(src + cbase, boff));
+      store_coherent(next + cbase, boff, empty);
       const uint64_t lo = canonicalize<T>(lo64(v)), hi = canonicalize<T>(hi64(v));
       const u32x4 c = {static_cast<uint32_t>(lo), static_cast<uint32_t>(lo >> 32),
                        static_cast<uint32_t>(hi), static_cast<uint32_t>(hi >> 32)};
+      // The emptying store must be visible before the data is.  A device-coherent store is
+      // acknowledged once it is visible device-wide, so waiting for the memory counter orders the
+      // two; an agent-scope release fence would do the same but also write back the whole L2.
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       store_coherent(slot + cbase, boff, c);
     }
   };

@@ -29,9 +29,9 @@ hipError_t launch_lamport_norm_bf16(void* rbuf, int W, const void* residual, con
                                       H, c, src, s);
 }
 
-hipError_t launch_lamport_push_bf16(const void* partial, void* slot, int64_t nvec, int grid,
-                                   hipStream_t s) {
-  return launch_lamport_push_t<Bf16>(partial, slot, nvec, grid, s);
+hipError_t launch_lamport_push_bf16(const void* partial, void* slot, void* next, int64_t nvec,
+                                   int grid, hipStream_t s) {
+  return launch_lamport_push_t<Bf16>(partial, slot, next, nvec, grid, s);
 }
 
 hipError_t launch_sum_residual_bf16(const void* const* inputs, int W, const void* residual,

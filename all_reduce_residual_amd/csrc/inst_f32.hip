@@ -29,9 +29,9 @@ hipError_t launch_lamport_norm_f32(void* rbuf, int W, const void* residual, cons
                                       H, c, src, s);
 }
 
-hipError_t launch_lamport_push_f32(const void* partial, void* slot, int64_t nvec, int grid,
-                                   hipStream_t s) {
-  return launch_lamport_push_t<F32>(partial, slot, nvec, grid, s);
+hipError_t launch_lamport_push_f32(const void* partial, void* slot, void* next, int64_t nvec,
+                                   int grid, hipStream_t s) {
+  return launch_lamport_push_t<F32>(partial, slot, next, nvec, grid, s);
 }
 
 hipError_t launch_sum_residual_f32(const void* const* inputs, int W, const void* residual,

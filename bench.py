@@ -233,10 +233,11 @@ class GatherCase(Case):
 
 
 class LamportCase(Case):
-    """Lamport-style one-shot exchange on one GPU: per step, W producer pushes into the sentinel-
-    armed receive slots, then the polling consumer (which re-arms the slots).  `mode` "push"
-    times the W pushes alone, "step" pushes + consumer; the consumer's share is the difference.
-    One buffer set (the receive buffer is state), so small shapes are cache-warm."""
+    """Lamport-style one-shot exchange on one GPU: per round, W producer pushes (each writes its
+    slot of this round's buffer and empties its slot of the next), then the polling consumer,
+    which only reads.  `mode` "push" times the W pushes alone, "step" pushes + consumer; the
+    consumer's share is the difference.  The three rotating buffers are the only input set (the
+    receive buffers are state), so small shapes are cache-warm."""
 
     def __init__(self, ar, torch, pattern, W, M, H, dtype="bf16", eps=1e-6):
         self.ar, self.torch = ar, torch
@@ -250,7 +251,7 @@ class LamportCase(Case):
         g.manual_seed(99)
         self.parts = [torch.empty((M, H), dtype=torch.float32, device="cuda")
                       .normal_(0.0, 0.05, generator=g).to(tdt) for _ in range(W)]
-        self.rbuf = torch.empty((W, M, H), dtype=tdt, device="cuda")
+        self.rbuf = torch.empty((ar.LAMPORT_BUFFERS, W, M, H), dtype=tdt, device="cuda")
         self.status = torch.zeros(1, dtype=torch.int32, device="cuda")
         self.dt = ar.dtype_code(tdt)
         L = ar.lib()
@@ -263,14 +264,14 @@ class LamportCase(Case):
             self.gamma = torch.empty(H, dtype=torch.float32, device="cuda").uniform_(
                 0.8, 1.2, generator=g)
             self.ro, self.no = torch.empty_like(self.res), torch.empty_like(self.res)
-            self.consume = lambda h: L.ar_lamport_residual_rmsnorm(
-                self.rbuf.data_ptr(), W, M, H, self.dt, self.res.data_ptr(),
+            self.consume = lambda rnd, h: L.ar_lamport_residual_rmsnorm(
+                self.rbuf.data_ptr(), W, M, H, self.dt, rnd, self.res.data_ptr(),
                 self.gamma.data_ptr(), ctypes.c_float(eps), self.ro.data_ptr(),
                 self.no.data_ptr(), self.status.data_ptr(), 0, ctypes.c_void_p(h))
         else:
             self.out = torch.empty((M, H), dtype=tdt, device="cuda")
-            self.consume = lambda h: L.ar_lamport_sum(
-                self.rbuf.data_ptr(), W, M, H, self.dt, self.out.data_ptr(),
+            self.consume = lambda rnd, h: L.ar_lamport_sum(
+                self.rbuf.data_ptr(), W, M, H, self.dt, rnd, self.out.data_ptr(),
                 self.status.data_ptr(), 0, ctypes.c_void_p(h))
         st = L.ar_lamport_arm(self.rbuf.data_ptr(), W, M, H, self.dt,
                               ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
@@ -279,13 +280,15 @@ class LamportCase(Case):
         torch.cuda.synchronize()
 
     def call(self, i: int, stream_handle: int) -> None:
+        """Round i: W pushes, then (in "step" mode) the consumer.  A graph holds a multiple of 3
+        rounds, so that its replays keep the buffer rotation."""
         h = ctypes.c_void_p(stream_handle)
         for a in self.push_args:
-            st = self.L.ar_lamport_push(*a, h)
+            st = self.L.ar_lamport_push(*a, i, h)
             if st != 0:
                 raise RuntimeError("ar_lamport_push failed: %s" % self.ar.status_string(st))
         if self.mode == "step":
-            st = self.consume(stream_handle)
+            st = self.consume(i, stream_handle)
             if st != 0:
                 raise RuntimeError("Lamport consumer failed: %s" % self.ar.status_string(st))
 
@@ -296,7 +299,7 @@ def lamport_lines(ar, torch, W=8, H=7168, Ms=(8, 128, 2048)) -> list:
     for m in Ms:
         for pattern in ("rms", "sum"):
             c = LamportCase(ar, torch, pattern, W, m, H)
-            calls = 20 if m >= 1024 else 100
+            calls = 21 if m >= 1024 else 99              # whole rotations of the 3 buffers
             c.mode = "step"
             us_step = c.time_graph(calls)
             c.mode = "push"

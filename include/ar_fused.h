@@ -266,36 +266,52 @@ int ar_all_gather(const void* const* slices, int W, int64_t M, int64_t H, int dt
  *
  * The one-shot exchange of the MNNVL all-reduce (flashinfer pull request "Optimizations for
  * TRTLLM MNNVL Allreduce", Description and Summary: Lamport polling with vectorized loads,
- * buffer state kept in the data) carries no separate flag: a receive buffer `rbuf` holds W slots
- * of [M, H] elements of type `dtype` (slot r at byte offset r * M * H * sizeof(T)); an empty
- * element holds the all-ones bit pattern (a NaN in every type).  Producers write their partial
- * into their slot; consumers poll each element until it is not all ones, reduce exactly as
- * ar_sum / ar_residual_rmsnorm, and write all ones back, leaving the buffer empty for the next
- * round.  A partial element that is itself all ones is delivered with its lowest bit cleared (a
- * NaN either way).  Producers and the consumer may run concurrently (on other streams, or, with
- * peer-mapped memory, other GPUs): slots move as 16-byte device-coherent accesses (each aligned
- * dword single-copy atomic; elements are tested one by one).
+ * buffer state kept in the data) carries no separate flag.  A receive buffer `rbuf` holds
+ * AR_LAMPORT_BUFFERS (3) buffers of W slots of [M, H] elements of type `dtype`: slot r of buffer b
+ * sits at byte offset (b * W + r) * M * H * sizeof(T).  An empty element holds the all-ones bit
+ * pattern (a NaN in every type).  Rounds are numbered 0, 1, 2, ... by the caller; round k uses
+ * buffer k mod 3.  The producer of rank r in round k writes its partial into slot r of buffer
+ * k mod 3 and empties slot r of buffer (k + 1) mod 3 (the one round k - 2 used); consumers poll
+ * each element of buffer k mod 3 until it is not all ones and reduce exactly as ar_sum /
+ * ar_residual_rmsnorm, reading only.  A partial element that is itself all ones is delivered
+ * with its lowest bit cleared (a NaN either way).
+ *
+ * Ordering contract: every rank calls, per round, push then a consumer, on one stream (or with
+ * the consumer of round k - 1 complete before the push of round k).  Then the push of round k
+ * empties a slot no consumer still reads: its rank finished consuming round k - 1, which needed
+ * every rank's push of round k - 1, made after that rank consumed round k - 2.  Producers and
+ * consumers of one round may run concurrently (on other streams, or, with peer-mapped memory,
+ * other GPUs): slots move as 16-byte device-coherent accesses (each aligned dword single-copy
+ * atomic; elements are tested one by one), and each producer thread empties its vector of the
+ * next buffer, and waits for that store to complete, before it stores its vector of the current
+ * one.  A captured graph replays the same round numbers: capture 3 consecutive rounds (or a
+ * multiple of 3) so that replays keep the rotation.
+ *
  * Every wait is bounded: after `spin_limit` polls of one 16-byte vector (0 = 65536) the consumer
  * gives up on it, sets bit 0 of *status (a device int the caller clears) and carries on; the
- * outputs are then meaningless and the buffer is not left empty.  H must be a multiple of
+ * outputs are then meaningless and the exchange must be re-armed.  H must be a multiple of
  * 16 / sizeof(T); the fused consumer takes rows of at most 8192 16-byte vectors for W <= 4
- * and 4096 for W >= 8 (H <= 65536 / 32768 at 16 bits). */
+ * and 4096 for W >= 8 (H <= 65536 / 32768 at 16 bits).  round < 0 is AR_ERR_INVALID_ARG. */
 
-/* Empties all W slots (every element all ones).  Call once before the first round. */
+#define AR_LAMPORT_BUFFERS 3
+
+/* Empties every slot of the 3 buffers (every element all ones).  Call once before round 0, and
+ * again after a consumer reported a time-out. */
 int ar_lamport_arm(void* rbuf, int W, int64_t M, int64_t H, int dtype, void* stream);
 
-/* Producer of rank `rank`: copies `partial` ([M, H], must not overlap rbuf) into slot `rank`. */
+/* Producer of rank `rank` in round `round`: copies `partial` ([M, H], must not overlap rbuf)
+ * into slot `rank` of buffer round mod 3 and empties slot `rank` of buffer (round + 1) mod 3. */
 int ar_lamport_push(const void* partial, int rank, void* rbuf, int W, int64_t M, int64_t H,
-                    int dtype, void* stream);
+                    int dtype, int64_t round, void* stream);
 
-/* Consumer, kAllReduce: out = sum of the W slots (as ar_sum); re-empties the slots.
- * out must not overlap rbuf or *status. */
-int ar_lamport_sum(void* rbuf, int W, int64_t M, int64_t H, int dtype, void* out, int* status,
-                   uint32_t spin_limit, void* stream);
+/* Consumer of round `round`, kAllReduce: out = sum of the W slots of buffer round mod 3 (as
+ * ar_sum).  out must not overlap rbuf or *status. */
+int ar_lamport_sum(void* rbuf, int W, int64_t M, int64_t H, int dtype, int64_t round, void* out,
+                   int* status, uint32_t spin_limit, void* stream);
 
-/* Consumer, kARResidualRMSNorm (as ar_residual_rmsnorm); re-empties the slots.  residual,
- * gamma and both outputs must not overlap rbuf; outputs must not overlap *status. */
-int ar_lamport_residual_rmsnorm(void* rbuf, int W, int64_t M, int64_t H, int dtype,
+/* Consumer of round `round`, kARResidualRMSNorm (as ar_residual_rmsnorm) over buffer round mod 3.
+ * residual, gamma and both outputs must not overlap rbuf; outputs must not overlap *status. */
+int ar_lamport_residual_rmsnorm(void* rbuf, int W, int64_t M, int64_t H, int dtype, int64_t round,
                                 const void* residual, const float* gamma, float eps,
                                 void* residual_out, void* norm_out, int* status,
                                 uint32_t spin_limit, void* stream);

@@ -208,13 +208,14 @@ def test_graph_replay_matches_eager(oracle_mod):
 
 
 def test_graph_replay_of_exchange_gather_and_fallback(oracle_mod):
-    """The Lamport exchange (W pushes + the polling consumer, which re-arms the slots), the
-    all-gather of a two-shot round and the two-kernel path, each captured once and replayed with
-    new inputs and eager work in between: every replay equals the oracle, and the exchange's
-    status word stays clear (each replay finds its slots re-armed by the previous one)."""
+    """The Lamport exchange (three rounds of W pushes + the polling consumer, so that replays keep
+    the buffer rotation), the all-gather of a two-shot round and the two-kernel path, captured
+    once and replayed with new inputs and eager work in between: every replay equals the oracle,
+    and the exchange's status word stays clear (each round finds its buffer emptied by the pushes
+    of the round before)."""
     W, M, H, dtype = 8, 24, 7168, "bf16"
     parts, res, gam, dp, dr, dg = _inputs(W, M, H, dtype, 21)
-    rbuf = torch.empty((W, M, H), dtype=torch.bfloat16, device="cuda")
+    rbuf = torch.empty((ar.LAMPORT_BUFFERS, W, M, H), dtype=torch.bfloat16, device="cuda")
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     ar.ar_lamport_arm(rbuf)
     lro, lno = torch.empty_like(dr), torch.empty_like(dr)
@@ -232,9 +233,10 @@ def test_graph_replay_of_exchange_gather_and_fallback(oracle_mod):
     uro, uno = torch.empty_like(dur), torch.empty_like(dur)
 
     def calls():
-        for r in range(W):
-            ar.ar_lamport_push(dp[r], r, rbuf)
-        ar.ar_lamport_residual_rmsnorm(rbuf, dr, dg, 1e-6, lro, lno, status)
+        for rnd in range(ar.LAMPORT_BUFFERS):
+            for r in range(W):
+                ar.ar_lamport_push(dp[r], r, rbuf, rnd)
+            ar.ar_lamport_residual_rmsnorm(rbuf, rnd, dr, dg, 1e-6, lro, lno, status)
         ar.ar_all_gather(slices, gout)
         ar.ar_residual_rmsnorm_unfused(dup, dur, dug, 1e-6, uro, uno)
 
@@ -269,8 +271,8 @@ def test_graph_replay_of_exchange_gather_and_fallback(oracle_mod):
             [host_np(p) for p in u2], host_np(ur2), ug.numpy(), 1e-6, dtype)
         assert_bit_exact(host_np(uro.cpu()), want_ro, dtype, "replay %d unfused residual_out" % rep)
         assert_norm_close(host_np(uno.cpu()), want_no, dtype, "replay %d unfused norm_out" % rep)
-    # Every slot is armed again after the last replay.
-    assert bool((rbuf.view(torch.int16) == -1).all())
+    # The last round (2) emptied buffer 0 for the next replay's round 0.
+    assert bool((rbuf[0].view(torch.int16) == -1).all())
 
 
 def test_device_facts():

@@ -165,22 +165,23 @@ def test_all_gather_past_4gib():
 
 @pytest.mark.parametrize("pattern", ["sum", "rms"])
 def test_lamport_past_4gib(oracle_mod, pattern):
-    """Receive slots of 4.1 GiB each (the second slot starts past 4 GiB of the buffer)."""
+    """Receive slots of 4.1 GiB each; round 2 uses the last of the three buffers, which starts
+    past 16 GiB, and its push empties buffer 0."""
     W, M, H, dtype = 2, 300000, 7168, "bf16"
     print("case lamport %s past 4 GiB W=%d M=%d H=%d" % (pattern, W, M, H), flush=True)
     g = torch.Generator(device="cuda")
     g.manual_seed(4404)
     parts = [_big(M, H, torch.bfloat16, g, 0.05) for _ in range(W)]
-    rbuf = torch.empty((W, M, H), dtype=torch.bfloat16, device="cuda")
+    rbuf = torch.empty((ar.LAMPORT_BUFFERS, W, M, H), dtype=torch.bfloat16, device="cuda")
     ar.ar_lamport_arm(rbuf)
     for r, p in enumerate(parts):
-        ar.ar_lamport_push(p, r, rbuf)
+        ar.ar_lamport_push(p, r, rbuf, 2)
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     rows = _sample_rows(M, H)
     hp = [_rows_at(p, rows) for p in parts]
     if pattern == "sum":
         out = torch.empty_like(parts[0])
-        ar.ar_lamport_sum(rbuf, out, status)
+        ar.ar_lamport_sum(rbuf, 2, out, status)
         torch.cuda.synchronize()
         assert int(status.item()) == 0
         assert_bit_exact(_rows_at(out, rows), oracle_mod.ar_sum(hp, dtype), dtype,
@@ -190,7 +191,7 @@ def test_lamport_past_4gib(oracle_mod, pattern):
         res = _big(M, H, torch.bfloat16, g)
         gam = torch.empty(H, dtype=torch.float32, device="cuda").uniform_(0.5, 1.5, generator=g)
         ro, no = torch.empty_like(res), torch.empty_like(res)
-        ar.ar_lamport_residual_rmsnorm(rbuf, res, gam, 1e-6, ro, no, status)
+        ar.ar_lamport_residual_rmsnorm(rbuf, 2, res, gam, 1e-6, ro, no, status)
         torch.cuda.synchronize()
         assert int(status.item()) == 0
         want_ro, want_no = oracle_mod.ar_residual_rmsnorm(hp, _rows_at(res, rows),
@@ -198,9 +199,12 @@ def test_lamport_past_4gib(oracle_mod, pattern):
         assert_bit_exact(_rows_at(ro, rows), want_ro, dtype, "lamport residual_out")
         assert_norm_close(_rows_at(no, rows), want_no, dtype, "lamport norm_out")
         del res, ro, no
-    # The consumer left every slot empty again (all-ones), at the sampled rows of both slots.
+    # Buffer 0 was emptied by the push (all ones at the sampled rows of both slots) and buffer 2
+    # holds the partials.
     iv = rbuf.view(torch.int16)
     idx = torch.tensor(rows, device="cuda")
-    assert bool((iv[:, idx] == -1).all())
+    assert bool((iv[0][:, idx] == -1).all())
+    for r, p in enumerate(parts):
+        assert torch.equal(iv[2, r][idx], p.view(torch.int16)[idx])
     del parts, rbuf, iv
     torch.cuda.empty_cache()

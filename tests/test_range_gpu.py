@@ -213,13 +213,13 @@ def test_lamport_consumer(oracle_mod, kind, dtype):
     want = want_rms(oracle_mod, parts, res, gam, eps, dtype)
     M = res.shape[0]
     d_parts, d_res = [dev(p) for p in parts], dev(res)
-    rbuf = torch.empty((W, M, H), dtype=TD[dtype], device="cuda")
+    rbuf = torch.empty((ar.LAMPORT_BUFFERS, W, M, H), dtype=TD[dtype], device="cuda")
     ar.ar_lamport_arm(rbuf)
     for r, p in enumerate(d_parts):
-        ar.ar_lamport_push(p, r, rbuf)
+        ar.ar_lamport_push(p, r, rbuf, 0)
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     ro, no = torch.empty_like(d_res), torch.empty_like(d_res)
-    ar.ar_lamport_residual_rmsnorm(rbuf, d_res, dev(gam), eps, ro, no, status)
+    ar.ar_lamport_residual_rmsnorm(rbuf, 0, d_res, dev(gam), eps, ro, no, status)
     torch.cuda.synchronize()
     assert int(status.item()) == 0
     check(ro, no, want, dtype)
