@@ -113,6 +113,8 @@ def lib():
             "ar_policy_default": [i32, ctypes.POINTER(Policy)],
             "ar_route": [i32, i32, i64, i64, i32, ctypes.POINTER(Policy),
                          ctypes.POINTER(ctypes.c_int)],
+            "ar_allreduce_routed": [i32, vp, i32, i64, i64, i32, vp, vp, f32, vp, vp, i32,
+                                    ctypes.POINTER(Policy), ctypes.POINTER(ctypes.c_int), vp],
             "ar_row_partition": [i32, i64, i32, ctypes.POINTER(ctypes.c_int64),
                                  ctypes.POINTER(ctypes.c_int64)],
             "ar_all_gather": [vp, i32, i64, i64, i32, vp, vp],
@@ -436,6 +438,36 @@ def ar_route(pattern: int, W: int, M: int, H: int, dtype: int,
     p = Policy(**(policy if policy is not None else ar_policy_default(W if W >= 1 else 1)))
     r = ctypes.c_int(-1)
     _check(lib().ar_route(pattern, W, M, H, dtype, ctypes.byref(p), ctypes.byref(r)), "ar_route")
+    return int(r.value)
+
+
+def ar_allreduce_routed(inputs, out, residual=None, gamma=None, eps: float = 1e-6,
+                        norm_out=None, rank: int = 0, policy: Optional[Dict[str, int]] = None,
+                        stream=None) -> int:
+    """Run the call on the path ar_route picks (kARResidualRMSNorm when `residual` is given,
+    `out` then being residual_out; else kAllReduce) and return the route taken.  A two-shot route
+    writes only this rank's row slice; a fallback route raises ArError (AR_ERR_UNSUPPORTED)."""
+    import torch
+    ptrs, W, M, H, dt = _marshal_inputs(inputs, out)
+    pattern = PATTERN_ALLREDUCE
+    res_p = gam_p = no_p = None
+    if residual is not None:
+        pattern = PATTERN_AR_RESIDUAL_RMSNORM
+        if norm_out is None or gamma is None:
+            raise ValueError("kARResidualRMSNorm needs gamma and norm_out")
+        _marshal_inputs([residual], norm_out)
+        _marshal_inputs([residual], out)
+        if gamma.dtype != torch.float32 or tuple(gamma.shape) != (H,) \
+                or not gamma.is_contiguous() or gamma.device != out.device:
+            raise ValueError("gamma must be a contiguous float32 [%d] tensor on %s"
+                             % (H, out.device))
+        res_p, gam_p, no_p = residual.data_ptr(), gamma.data_ptr(), norm_out.data_ptr()
+    p = Policy(**(policy if policy is not None else ar_policy_default(W)))
+    r = ctypes.c_int(-1)
+    st = lib().ar_allreduce_routed(pattern, ptrs, W, M, H, dt, res_p, gam_p, float(eps),
+                                   out.data_ptr(), no_p, rank, ctypes.byref(p), ctypes.byref(r),
+                                   _stream_handle(stream, out.device))
+    _check(st, "ar_allreduce_routed")
     return int(r.value)
 
 

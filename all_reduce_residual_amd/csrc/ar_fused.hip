@@ -1195,6 +1195,51 @@ int ar_route(int pattern, int W, int64_t M, int64_t H, int dtype, const ar_polic
   return AR_OK;
 }
 
+int ar_allreduce_routed(int pattern, const void* const* inputs, int W, int64_t M, int64_t H,
+                        int dtype, const void* residual, const float* gamma, float eps, void* out,
+                        void* norm_out, int rank, const ar_policy_t* policy, int* route,
+                        void* stream) {
+  if (!route) return AR_ERR_INVALID_ARG;
+  int r = AR_ROUTE_FALLBACK;
+  const int st = ar_route(pattern, W, M, H, dtype, policy, &r);
+  if (st != AR_OK) return st;
+  if (rank < 0 || rank >= W) return AR_ERR_INVALID_ARG;
+  *route = r;
+  const bool norm = pattern == AR_PATTERN_AR_RESIDUAL_RMSNORM;
+  switch (r) {
+    case AR_ROUTE_ONE_SHOT:
+      return norm ? run_norm(inputs, W, M, H, dtype, residual, gamma, eps, out, norm_out, stream,
+                             nullptr)
+                  : run_sum(inputs, W, M, H, dtype, out, stream, nullptr);
+    case AR_ROUTE_UNFUSED:
+      return run_unfused(inputs, W, M, H, dtype, residual, gamma, eps, out, norm_out, stream);
+    case AR_ROUTE_TWO_SHOT: {
+      // This rank's reduce-scatter share: the same reduction on its row slice, in place in the
+      // outputs.  The route guarantees whole 16-byte vectors per row, so every slice stays
+      // aligned.
+      if (!inputs) return AR_ERR_INVALID_ARG;
+      int64_t b = 0, c = 0;
+      row_slice(W, M, rank, &b, &c);
+      const int64_t off = b * H * elem_size(dtype);
+      auto shift = [off](const void* p) -> const void* {
+        return p ? static_cast<const char*>(p) + off : nullptr;
+      };
+      auto shift_out = [off](void* p) -> void* { return p ? static_cast<char*>(p) + off : nullptr; };
+      const void* rows[AR_MAX_W];
+      for (int j = 0; j < W; ++j) {
+        if (!inputs[j]) return AR_ERR_INVALID_ARG;
+        rows[j] = shift(inputs[j]);
+      }
+      if (!out || (norm && (!residual || !norm_out))) return AR_ERR_INVALID_ARG;
+      return norm ? run_norm(rows, W, c, H, dtype, shift(residual), gamma, eps, shift_out(out),
+                             shift_out(norm_out), stream, nullptr)
+                  : run_sum(rows, W, c, H, dtype, shift_out(out), stream, nullptr);
+    }
+    default:
+      return AR_ERR_UNSUPPORTED;  // the caller's own collective takes this call
+  }
+}
+
 const char* ar_status_string(int status) {
   switch (status) {
     case AR_OK: return "ok";

@@ -132,7 +132,11 @@ int ar_residual_rmsnorm(const void* const* inputs, int W, int64_t M, int64_t H, 
                         void* norm_out, void* stream);
 
 /* Shape-level support check, no device access: AR_OK if the pattern accepts (W, M, H, dtype),
- * else the status the entry point would return.  Lets a caller pick its fallback first. */
+ * else the status the entry point would return.  Lets a caller pick its fallback first.  This is
+ * the supports() of the tokenspeed pull request (Summary, Memory), which also bounds a call by
+ * the buffer bytes it actually needs: ar_sum and ar_residual_rmsnorm need no workspace, so the
+ * shape is the whole check here (the split form's bound is ar_split_workspace_bytes, the
+ * no-alloc form's AR_NOALLOC_MAX_ROWS). */
 int ar_supports(int pattern, int W, int64_t M, int64_t H, int dtype);
 
 /* Launch-shape heuristic: maps (pattern, W, M, H, dtype) and the compute-unit count to a launch
@@ -388,6 +392,29 @@ int ar_policy_default(int W, ar_policy_t* policy);
  * AR_ERR_INVALID_ARG for a null pointer, a negative threshold or a bad pattern. */
 int ar_route(int pattern, int W, int64_t M, int64_t H, int dtype, const ar_policy_t* policy,
              int* route);
+
+/* One call on the path ar_route picks, on this GPU: the tokenspeed pull request (Summary and
+ * Routing) has a dispatch check the shape (supports()) and a token threshold before choosing a
+ * path, each path serving as the other's shape fallback, and an unsupported call leaves the
+ * library.  `pattern` is AR_PATTERN_ALLREDUCE (`out` receives the sum; residual, gamma, eps and
+ * norm_out are ignored and may be null) or AR_PATTERN_AR_RESIDUAL_RMSNORM (`out` is
+ * residual_out).  Arguments, layouts and aliasing rules are those of the entry point the route
+ * runs; `policy` is as for ar_route; 0 <= rank < W is the calling rank.
+ *   AR_ROUTE_ONE_SHOT : ar_sum / ar_residual_rmsnorm over all M rows
+ *   AR_ROUTE_UNFUSED  : ar_residual_rmsnorm_unfused over all M rows
+ *   AR_ROUTE_TWO_SHOT : this rank's reduce-scatter share only: the same reduction over the rows
+ *                       [row_begin, row_begin + row_count) of ar_row_partition(W, M, rank),
+ *                       written to those rows of the outputs; the caller completes the call with
+ *                       ar_all_gather once every rank's share is done
+ *   AR_ROUTE_FALLBACK : nothing is launched; returns AR_ERR_UNSUPPORTED (the caller's own
+ *                       collective takes the call)
+ * *route is set to the route taken whenever ar_route succeeds and rank is valid; the status is
+ * that of the entry point run, or ar_route's error, or AR_ERR_INVALID_ARG for a null `route` or a
+ * bad rank. */
+int ar_allreduce_routed(int pattern, const void* const* inputs, int W, int64_t M, int64_t H,
+                        int dtype, const void* residual, const float* gamma, float eps, void* out,
+                        void* norm_out, int rank, const ar_policy_t* policy, int* route,
+                        void* stream);
 
 /* Static, human-readable name of a status code ("unknown status" for anything else). */
 const char* ar_status_string(int status);

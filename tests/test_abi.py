@@ -22,11 +22,12 @@ def L():
 def test_exports_every_declared_function(L):
     names = ar.header_functions()
     assert set(names) == {"ar_sum", "ar_residual_rmsnorm", "ar_supports", "ar_launch_config",
-                          "ar_residual_rmsnorm_noalloc", "ar_sum_with_config", "ar_residual_rmsnorm_with_config",
+                          "ar_residual_rmsnorm_noalloc", "ar_sum_with_config",
+                          "ar_residual_rmsnorm_with_config",
                           "ar_status_string", "ar_device_cu_count", "ar_row_partition",
                           "ar_all_gather", "ar_lamport_arm", "ar_lamport_push",
                           "ar_lamport_sum", "ar_lamport_residual_rmsnorm",
-                          "ar_policy_default", "ar_route", "ar_rmsnorm",
+                          "ar_policy_default", "ar_route", "ar_allreduce_routed", "ar_rmsnorm",
                           "ar_residual_rmsnorm_unfused", "ar_split_workspace_bytes",
                           "ar_workspace_clear", "ar_split_config", "ar_residual_rmsnorm_ws",
                           "ar_residual_rmsnorm_split_with_config"}

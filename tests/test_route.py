@@ -79,3 +79,53 @@ def test_route_rejects_bad_arguments():
     with pytest.raises(ar.ArError):
         ar.ar_route(RMS, 8, 32, 256, BF16, dict(min_tokens=-1, two_shot_min_bytes=0,
                                                 max_payload_bytes=0))
+
+
+def test_routed_entry_validates_before_any_launch():
+    """The routed entry point on fake pointers: every case here returns before a launch (the
+    pointers are never dereferenced)."""
+    import ctypes
+    L = ar.lib()
+    bf16 = ar.DTYPE_BF16
+    pol = ar.Policy(**ar.ar_policy_default(8))
+    route = ctypes.c_int(-7)
+    ins = (ctypes.c_void_p * 12)(*[0x1000000 * (j + 1) for j in range(12)])
+    out = 0x40000000
+    # World size 12: the fallback route, AR_ERR_UNSUPPORTED, *route set.
+    st = L.ar_allreduce_routed(ar.PATTERN_ALLREDUCE, ins, 12, 64, 7168, bf16, None, None, 1e-6,
+                               out, None, 0, ctypes.byref(pol), ctypes.byref(route), None)
+    assert st == ar.AR_ERR_UNSUPPORTED and route.value == ar.ROUTE_FALLBACK
+    # A payload above the policy's cutoff: fallback as well.
+    small = ar.Policy(min_tokens=32, two_shot_min_bytes=0, max_payload_bytes=1024)
+    route.value = -7
+    st = L.ar_allreduce_routed(ar.PATTERN_ALLREDUCE, ins, 8, 64, 7168, bf16, None, None, 1e-6,
+                               out, None, 0, ctypes.byref(small), ctypes.byref(route), None)
+    assert st == ar.AR_ERR_UNSUPPORTED and route.value == ar.ROUTE_FALLBACK
+    # Bad rank, null route, null policy, bad pattern.
+    for rank in (-1, 8):
+        route.value = -7
+        st = L.ar_allreduce_routed(ar.PATTERN_ALLREDUCE, ins, 8, 64, 7168, bf16, None, None,
+                                   1e-6, out, None, rank, ctypes.byref(pol), ctypes.byref(route),
+                                   None)
+        assert st == ar.AR_ERR_INVALID_ARG and route.value == -7
+    assert L.ar_allreduce_routed(ar.PATTERN_ALLREDUCE, ins, 8, 64, 7168, bf16, None, None, 1e-6,
+                                 out, None, 0, ctypes.byref(pol), None, None) == \
+        ar.AR_ERR_INVALID_ARG
+    assert L.ar_allreduce_routed(ar.PATTERN_ALLREDUCE, ins, 8, 64, 7168, bf16, None, None, 1e-6,
+                                 out, None, 0, None, ctypes.byref(route), None) == \
+        ar.AR_ERR_INVALID_ARG
+    assert L.ar_allreduce_routed(7, ins, 8, 64, 7168, bf16, None, None, 1e-6, out, None, 0,
+                                 ctypes.byref(pol), ctypes.byref(route), None) == \
+        ar.AR_ERR_INVALID_ARG
+    # Two-shot share (2048 rows of 7168 bf16 at W = 8) with a null partial or a null norm output:
+    # rejected before the row pointers are formed.
+    ins[3] = None
+    route.value = -7
+    st = L.ar_allreduce_routed(ar.PATTERN_ALLREDUCE, ins, 8, 2048, 7168, bf16, None, None, 1e-6,
+                               out, None, 2, ctypes.byref(pol), ctypes.byref(route), None)
+    assert st == ar.AR_ERR_INVALID_ARG and route.value == ar.ROUTE_TWO_SHOT
+    ins[3] = 0x4000000
+    st = L.ar_allreduce_routed(ar.PATTERN_AR_RESIDUAL_RMSNORM, ins, 8, 2048, 7168, bf16,
+                               0x50000000, 0x60000000, 1e-6, out, None, 2, ctypes.byref(pol),
+                               ctypes.byref(route), None)
+    assert st == ar.AR_ERR_INVALID_ARG and route.value == ar.ROUTE_TWO_SHOT
