@@ -6,7 +6,8 @@ residual added, residual_out and norm_out written) on the wide-hidden prefill wo
 W=8 partials, M=2048 tokens, H=7168, bf16.  Inputs are resident in HBM before the timed region.
 Buffer sets are rotated so that the bytes a timed batch touches exceed the 256 MB Infinity
 Cache (the numbers are HBM numbers, not cache numbers).  Steps are timed with HIP events on the
-stream the kernel is launched on.
+stream the kernel is launched on; events cut the timed steps into up to 5 windows, and the
+headline is the median window's rate, with the windows' spread beside it.
 
 Output: ONE JSON line with the metric (effective HBM GB/s = algorithmic bytes / time, bytes =
 (W + 3) * M * H * 2: W partial reads, residual read, residual_out and norm_out writes), the
@@ -291,6 +292,19 @@ class LamportCase(Case):
             st = self.consume(i, stream_handle)
             if st != 0:
                 raise RuntimeError("Lamport consumer failed: %s" % self.ar.status_string(st))
+
+
+def headline_windows(steps: int, count: int = 5) -> list:
+    """Step indices that cut `steps` timed steps into min(count, steps) windows of near-equal
+    length: window j holds steps [b[j], b[j + 1])."""
+    n = max(1, min(count, steps))
+    return [(j * steps) // n for j in range(n + 1)]
+
+
+def median(xs) -> float:
+    v = sorted(xs)
+    k = len(v) // 2
+    return v[k] if len(v) % 2 else 0.5 * (v[k - 1] + v[k])
 
 
 def lamport_lines(ar, torch, W=8, H=7168, Ms=(8, 128, 2048)) -> list:
@@ -923,7 +937,9 @@ def main():
         box["gpu"], box["arch"], box["compute_units"], box["device_memory_GiB"], box["host_cpu"],
         box["host_threads"]), file=sys.stderr, flush=True)
 
-    # Headline: warm-up, then exactly `steps` timed steps on rotated buffer sets.
+    # Headline: warm-up, then exactly `steps` timed steps on rotated buffer sets, split by
+    # events into (up to) 5 windows of consecutive steps; the value is the median window's
+    # rate and the spread of the windows is reported beside it.
     case = Case(ar, torch, "rms", W, M, H)
     sample = headline_sample(torch, case)
     s = torch.cuda.current_stream()
@@ -931,15 +947,19 @@ def main():
     for i in range(args.warmup):
         case.call(i, hnd)
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(s)
-    for i in range(args.steps):
-        case.call(i, hnd)
-    b.record(s)
-    b.synchronize()
+    win = headline_windows(args.steps)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in win]
+    ev[0].record(s)
+    for j in range(1, len(win)):
+        for i in range(win[j - 1], win[j]):
+            case.call(i, hnd)
+        ev[j].record(s)
+    ev[-1].synchronize()
     torch.cuda.synchronize()
-    ms_total = a.elapsed_time(b)
-    us_per_call = ms_total * 1000.0 / args.steps
+    ms_total = ev[0].elapsed_time(ev[-1])
+    us_windows = [ev[j - 1].elapsed_time(ev[j]) * 1000.0 / (win[j] - win[j - 1])
+                  for j in range(1, len(win))]
+    us_per_call = median(us_windows)
     gbs = case.bytes / (us_per_call * 1e-6) / 1e9
     launch_cfg = ar.ar_launch_config(ar.PATTERN_AR_RESIDUAL_RMSNORM, W, M, H, ar.DTYPE_BF16)
     print("# headline: %.2f us/call, %.1f GB/s (%.1f%% of peak), R=%d sets, cfg=%s" % (
@@ -957,6 +977,13 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_total / args.steps, 6),
         "us_per_call": round(us_per_call, 3),
+        "windows": {"count": len(us_windows), "steps": [win[j] - win[j - 1]
+                                                        for j in range(1, len(win))],
+                    "us_per_call": [round(u, 3) for u in us_windows],
+                    "median": round(us_per_call, 3), "min": round(min(us_windows), 3),
+                    "max": round(max(us_windows), 3),
+                    "spread_pct": round(100.0 * (max(us_windows) - min(us_windows)) /
+                                        us_per_call, 2)},
         "pct_of_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "higher_is_better": True,
         "scaling": "weak",

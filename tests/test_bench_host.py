@@ -129,3 +129,14 @@ def test_headline_parity_check_accepts_and_rejects(oracle_mod):
         raise RuntimeError("a norm_out 2 ulp away was accepted")
     except AssertionError:
         pass
+
+
+def test_headline_windows_cover_exactly_the_timed_steps():
+    for steps in (1, 3, 5, 7, 20, 200, 201):
+        b = bench.headline_windows(steps)
+        assert b[0] == 0 and b[-1] == steps
+        assert len(b) - 1 == min(5, steps)
+        lens = [b[j + 1] - b[j] for j in range(len(b) - 1)]
+        assert min(lens) >= 1 and max(lens) - min(lens) <= 1
+    assert bench.median([3.0, 1.0, 2.0]) == 2.0
+    assert bench.median([4.0, 1.0, 2.0, 3.0]) == 2.5
