@@ -312,10 +312,14 @@ inline hipError_t launch_rmsnorm_t(const void* x, const float* gamma, float eps,
 }
 
 // vecs_per_thread: 1, 2, 4 or 8 (row values kept in registers) or 0 (two passes over memory).
+// The register forms need H / vec + 9 slots per block (a row's vectors from the start of its
+// first 128-byte line); a smaller shape is refused rather than run.
 template <class T>
 inline hipError_t launch_rmsnorm_rows_t(const void* x, const float* gamma, float eps, void* y,
                                         int64_t M, int64_t H, int grid, int threads,
                                         int vecs_per_thread, hipStream_t s) {
+  if (vecs_per_thread > 0 && int64_t(vecs_per_thread) * threads < H / T::kVec + 9)
+    return hipErrorInvalidValue;
   float count_h = static_cast<float>(H);
   void* args[] = {&x, &gamma, &y, &M, &H, &eps, &count_h};
   const void* fn;

@@ -635,13 +635,15 @@ int launch_rmsnorm(const void* x, int64_t M, int64_t H, int dtype, const float* 
     }
   } else {
     // One block per row, grid stride over rows (at most 8 blocks per CU).  A row spans at most
-    // H / vec + 2 aligned vectors; the fewest vectors per thread (1, 2, 4 or 8) that keep the
+    // H / vec + 2 aligned vectors, and the kernel's slots start at the 128-byte line that holds
+    // the row's first element, up to 7 vectors earlier: H / vec + 9 slots.  The fewest vectors
+    // per thread (1, 2, 4 or 8) that keep the
     // block at <= 512 threads (640 for 4, 1024 for 8) hold the row in registers, else two
     // passes.  (Rows of 2049-2560 vectors: 4 vectors over up to 640 threads ran 8-39 % faster
     // than 8 over 320 at M = 768 ... 4096, bf16 H = 16386 / 20002, fp16 18434, binary32 9002;
     // bf16 H = 16386, M = 2048: 41.1 -> 30.0 us.)
     const int vec = kVecBytes / elem_size(dtype);
-    const int64_t nv = H / vec + 2;
+    const int64_t nv = H / vec + 9;
     int vpt = 0;
     int64_t threads = 1024;
     for (int k = 1; k <= 8; k *= 2) {

@@ -49,6 +49,8 @@ namespace arf {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// Four floats at a 4-byte-aligned address (a 16-byte load the hardware splits as needed).
+typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
@@ -871,11 +873,12 @@ __device__ inline float block_sum(float v, float* red) {
   return t;
 }
 
-// One block per row (grid stride over rows).  K > 0: thread t owns vectors t + k * blockDim.x
-// (k < K) and keeps their values in registers between the sum of squares and the scaling, so x
-// is read once.  Every one of those K vectors is loaded whole and unconditionally first (a lane
-// with no vector re-reads an in-range one), so the K loads are in flight together; elements of a
-// vector that belong to a neighbouring row are then masked to zero.  Only a vector that runs
+// One block per row (grid stride over rows).  K > 0: thread t owns slots t + k * blockDim.x
+// (k < K), slot j being the j-th 16-byte vector from the 128-byte line that holds the row's
+// first element, and keeps their values in registers between the sum of squares and the scaling,
+// so x is read once.  Every one of those K vectors is loaded whole and unconditionally first (a
+// slot outside the row re-reads the row's first vector), so the K loads are in flight together;
+// elements of a vector that belong to a neighbouring row are then masked to zero.  Only a vector that runs
 // past the end of the tensor (the last row's last vector when M * H is not a multiple of the
 // vector width) is read element by element.  K = 0 (rows longer than 8 vectors per thread of a
 // 1024-thread block): the row is read twice, the second time normally from cache.  y may be x
@@ -901,23 +904,42 @@ __global__ __launch_bounds__(kMaxThreads) void ar_rmsnorm_rows_kernel(const void
     const int64_t nv = (e1 + kVec - 1) / kVec - v0;
     float ss = 0.0f;
     if constexpr (K > 0) {
+      // Slot j of the block holds vector vb + j, vb the first vector of the 128-byte line that
+      // holds the row's first element, so every wave-wide access covers whole lines (a row of
+      // an odd width starts anywhere in a line).  The row's vectors are slots [off, off + nv);
+      // only its first and last can be partial: elements [lo, hi) belong to the row, lo = s
+      // in the first, hi = t in the last, whole vectors otherwise.  (The launch gives the block
+      // K * blockDim.x >= nv + 7 slots.)
+      const int64_t vb = v0 & ~int64_t(7);
+      const int64_t off = v0 - vb;
+      const int s = static_cast<int>(e0 - v0 * kVec);
+      const int t = static_cast<int>(e1 - (v0 + nv - 1) * kVec);
+      auto live = [&](int64_t j) { return j >= off && j < off + nv; };
+      auto lo_of = [&](int64_t j) { return j == off ? s : 0; };
+      auto hi_of = [&](int64_t j) { return j == off + nv - 1 ? t : kVec; };
       float f[K][kVec];
       if (nfull > 0) {
+        // Uniform base and 32-bit lane offsets.  A slot outside the row re-reads the row's first
+        // vector (a line the wave loads anyway) rather than a neighbouring row's data.
+        const int64_t bidx = vb < nfull ? vb : nfull - 1;
+        const u32x4* xb = xv + bidx;
         u32x4 raw[K];
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-          const int64_t v = v0 + threadIdx.x + k * nthreads;
-          raw[k] = load_stream(xv + (v < nfull ? v : nfull - 1));
+          const int64_t j = threadIdx.x + k * nthreads;
+          int64_t vi = live(j) ? vb + j : v0;
+          vi = vi < nfull ? vi : nfull - 1;
+          raw[k] = load_stream(at(xb, static_cast<uint32_t>(vi - bidx) * 16u));
         }
 #pragma unroll
         for (int k = 0; k < K; ++k) {
           const int64_t j = threadIdx.x + k * nthreads;
-          const int64_t a = (v0 + j) * kVec;
+          if (!live(j)) raw[k] = u32x4{0, 0, 0, 0};
           T::widen(raw[k], f[k]);
+          const int lo = lo_of(j), hi = hi_of(j);
+          if (lo > 0 || hi < kVec) {
 #pragma unroll
-          for (int e = 0; e < kVec; ++e) {
-            const bool in_row = j < nv && a + e >= e0 && a + e < e1;
-            f[k][e] = in_row ? f[k][e] : 0.0f;
+            for (int e = 0; e < kVec; ++e) f[k][e] = (e >= lo && e < hi) ? f[k][e] : 0.0f;
           }
         }
       } else {
@@ -930,7 +952,7 @@ __global__ __launch_bounds__(kMaxThreads) void ar_rmsnorm_rows_kernel(const void
 #pragma unroll
       for (int k = 0; k < K; ++k) {
         const int64_t j = threadIdx.x + k * nthreads;
-        if (j < nv && v0 + j >= nfull) load_row_vec<T, false>(x, e0, e1, v0 + j, f[k]);
+        if (live(j) && vb + j >= nfull) load_row_vec<T, false>(x, e0, e1, vb + j, f[k]);
 #pragma unroll
         for (int e = 0; e < kVec; ++e) ss += f[k][e] * f[k][e];
       }
@@ -954,10 +976,31 @@ __global__ __launch_bounds__(kMaxThreads) void ar_rmsnorm_rows_kernel(const void
         m = rstd_of_scaled(block_sum(s2, red), E, count_h, eps);
       }
       auto norm = [&](float a, float g) { return norm_elem_scaled(a, m, E, g); };
+      u32x4* yb = static_cast<u32x4*>(y) + vb;
 #pragma unroll
       for (int k = 0; k < K; ++k) {
         const int64_t j = threadIdx.x + k * nthreads;
-        if (j < nv) store_row_vec<T>(y, gamma, e0, e1, v0 + j, f[k], norm);
+        if (!live(j)) continue;
+        if (lo_of(j) == 0 && hi_of(j) == kVec) {
+          // A whole vector of the row (so wholly inside the tensor): gamma[(j - off) kVec - s ...]
+          // as dword-aligned 16-byte loads, the vector as one 16-byte store.
+          const float* g = gamma + ((j - off) * kVec - s);
+          float gv[kVec];
+#pragma unroll
+          for (int q = 0; q < kVec; q += 4) {
+            const f32x4u g4 = *reinterpret_cast<const f32x4u*>(g + q);
+            gv[q] = g4.x;
+            gv[q + 1] = g4.y;
+            gv[q + 2] = g4.z;
+            gv[q + 3] = g4.w;
+          }
+          float o[kVec];
+#pragma unroll
+          for (int e = 0; e < kVec; ++e) o[e] = norm(f[k][e], gv[e]);
+          store_vec<true>(at(yb, static_cast<uint32_t>(j) * 16u), T::narrow(o));
+        } else {
+          store_row_vec<T>(y, gamma, e0, e1, vb + j, f[k], norm);
+        }
       }
     } else {
       for (int64_t j = threadIdx.x; j < nv; j += nthreads) {
