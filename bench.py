@@ -777,6 +777,27 @@ def _pmc_by_kernel(d: str, counter: str):
 # The plain-sum workload whose counters the pmc mode also collects (80 MiB per partial).
 PMC_SUM = {"W": 4, "M": 5120, "H": 8192}
 
+# `--mode pmc --pmc-set kernels`: the other kernels' counter workloads.  Each entry: a name, the
+# Case arguments, a pattern that picks its kernel out of the counter data, and the algorithmic
+# bytes one dispatch reads and writes.
+PMC_KERNELS = [
+    dict(name="norm kernel, fp16 W=16 M=512 H=8192 (TP16 8 MiB)", pattern="rms", W=16, M=512,
+         H=8192, dtype="fp16", kernel=r"ar_norm_kernel<arf::F16, 16, .*StreamSource",
+         read=17 * 512 * 8192 * 2, write=2 * 512 * 8192 * 2),
+    dict(name="split kernel, W=8 M=8 H=7168 bf16 (workspace form)", pattern="rms_ws", W=8, M=8,
+         H=7168, dtype="bf16", kernel=r"ar_norm_split_kernel<arf::Bf16, 8,",
+         read=9 * 8 * 7168 * 2, write=2 * 8 * 7168 * 2),
+    dict(name="RMSNorm rows kernel, odd width M=2048 H=7170 bf16", pattern="rmsnorm", W=1,
+         M=2048, H=7170, dtype="bf16", kernel=r"ar_rmsnorm_rows_kernel<arf::Bf16, 8",
+         read=2048 * 7170 * 2, write=2048 * 7170 * 2),
+    dict(name="Lamport fused consumer, W=8 M=2048 H=7168 bf16", pattern="lamport", W=8, M=2048,
+         H=7168, dtype="bf16", kernel=r"ar_norm_kernel<arf::Bf16, 8, .*LamportSource",
+         read=9 * 2048 * 7168 * 2, write=2 * 2048 * 7168 * 2),
+    dict(name="Lamport push (one rank), W=8 M=2048 H=7168 bf16", pattern="lamport", W=8, M=2048,
+         H=7168, dtype="bf16", kernel=r"ar_lamport_push_kernel<arf::Bf16>",
+         read=2048 * 7168 * 2, write=2 * 2048 * 7168 * 2),
+]
+
 
 def summarize_pmc(fetch_dir: str, write_dir: str) -> str:
     """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the norm kernel, scaled by what the same
@@ -849,6 +870,41 @@ def summarize_pmc(fetch_dir: str, write_dir: str) -> str:
     return "\n".join(lines)
 
 
+def summarize_pmc_kernels(fetch_dir: str, write_dir: str) -> str:
+    """The PMC_KERNELS table: per kernel, FETCH_SIZE / WRITE_SIZE per dispatch scaled by the copy
+    calibration, against the algorithmic bytes."""
+    fetch = _pmc_by_kernel(fetch_dir, "FETCH_SIZE")
+    write = _pmc_by_kernel(write_dir, "WRITE_SIZE")
+
+    def mean_of(d, pat):
+        ks = [k for k in d if re.search(pat, k)]
+        vals = [v for k in ks for v in d[k]]
+        return (ks[0] if ks else None), (sum(vals) / len(vals) if vals else None), len(vals)
+
+    _, f_copy, _ = mean_of(fetch, r"^__amd_rocclr_copyBuffer")
+    _, w_copy, _ = mean_of(write, r"^__amd_rocclr_copyBuffer")
+    if not f_copy or not w_copy:
+        raise SystemExit("copy calibration kernel not found in counter data")
+    f_factor = COPY_CAL_BYTES / (f_copy * 1024.0)
+    w_factor = COPY_CAL_BYTES / (w_copy * 1024.0)
+    lines = ["copy calibration: FETCH_SIZE scale %.4f, WRITE_SIZE scale %.4f (bytes per counter "
+             "KiB * 1024)" % (f_factor, w_factor), "",
+             "| kernel | dispatches | fetch bytes | algorithmic read | ratio | write bytes | "
+             "algorithmic write | ratio |", "|---|---|---|---|---|---|---|---|"]
+    for kc in PMC_KERNELS:
+        kn, f, nf = mean_of(fetch, kc["kernel"])
+        _, w, nw = mean_of(write, kc["kernel"])
+        if kn is None or w is None:
+            lines.append("| %s | not found | | | | | | |" % kc["name"])
+            continue
+        fb, wb = f * 1024.0 * f_factor, w * 1024.0 * w_factor
+        lines.append("| %s (`%s`) | %d + %d | %.0f | %d | %.3f | %.0f | %d | %.3f |" % (
+            kc["name"], re.sub(r"\(.*", "", kn)[:90], nf, nw, fb, kc["read"], fb / kc["read"],
+            wb, kc["write"], wb / kc["write"]))
+    lines += ["", "kernel_hash: " + kernel_source_hash()]
+    return "\n".join(lines)
+
+
 def read_traffic():
     """Traffic from the committed counter summary, if it was taken on the current kernel."""
     try:
@@ -871,10 +927,12 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--mode", choices=["bench", "pmc"], default="bench")
+    ap.add_argument("--pmc-set", choices=["headline", "kernels"], default="headline")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--summarize-stats", metavar="DIR")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-pmc-kernels", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-sweep-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_JSON"))
     ap.add_argument("--phases", action="store_true")
     args = ap.parse_args()
@@ -887,6 +945,9 @@ def main():
         return 0
     if args.summarize_pmc:
         print(summarize_pmc(*args.summarize_pmc))
+        return 0
+    if args.summarize_pmc_kernels:
+        print(summarize_pmc_kernels(*args.summarize_pmc_kernels))
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -913,8 +974,31 @@ def main():
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
-        case = Case(ar, torch, "rms", W, M, H)
         h = torch.cuda.current_stream().cuda_stream
+        if args.pmc_set == "kernels":
+            del src, dst
+            done = set()
+            for kc in PMC_KERNELS:
+                key = (kc["pattern"], kc["W"], kc["M"], kc["H"], kc["dtype"])
+                if key in done:
+                    continue
+                done.add(key)
+                if kc["pattern"] == "lamport":
+                    case = LamportCase(ar, torch, "rms", kc["W"], kc["M"], kc["H"], kc["dtype"])
+                else:
+                    case = Case(ar, torch, kc["pattern"], kc["W"], kc["M"], kc["H"],
+                                dtype=kc["dtype"])
+                for i in range(max(3, args.steps)):
+                    case.call(i, h)
+                torch.cuda.synchronize()
+                print("# pmc %s: %d calls" % (kc["name"], max(3, args.steps)), file=sys.stderr,
+                      flush=True)
+                del case
+                torch.cuda.empty_cache()
+            print(json.dumps({"mode": "pmc", "set": "kernels", "copy_bytes": COPY_CAL_BYTES,
+                              "calls": max(3, args.steps)}))
+            return 0
+        case = Case(ar, torch, "rms", W, M, H)
         for i in range(max(2, args.steps)):
             case.call(i, h)
         torch.cuda.synchronize()
