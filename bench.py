@@ -177,7 +177,9 @@ class Case:
         return sorted(res)[len(res) // 2]
 
     def time_graph(self, calls: int, reps: int = 5) -> float:
-        """Median µs/call of a hipGraph replay holding `calls` launches."""
+        """Median µs/call of a hipGraph replay holding `calls` launches.  The first `reps`
+        replays are not timed: a newly built case ran its first replays up to 8 % slower
+        (W = 8 H = 7168 M = 128: 6.69 against 6.2 µs), the next ones steadily."""
         torch = self.torch
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
@@ -191,7 +193,8 @@ class Case:
             h = torch.cuda.current_stream().cuda_stream
             for i in range(calls):
                 self.call(i, h)
-        graph.replay()
+        for _ in range(reps):
+            graph.replay()
         torch.cuda.synchronize()
         res = []
         s = torch.cuda.current_stream()
