@@ -19,7 +19,7 @@ extern "C" {
  * combines them with XOR and writes the result to out0[i] and, when nw == 2, out0[i] + 1 to
  * out1[i] (non-temporal stores).  One vector per thread, `threads` per block (a multiple of 64,
  * at most 1024), a grid that covers nvec.
- *   inputs : host array of nr device pointers (16-byte aligned), nr = 8 or 9
+ *   inputs : host array of nr device pointers (16-byte aligned), nr in {1, 2, 4, 8, 9, 16}
  *   nw     : 1 or 2 output streams (out1 is ignored for nw == 1)
  * Returns 0, 1 for a bad argument (nothing launched), 2 if the launch failed. */
 int ar_probe_stream(const void* const* inputs, int nr, int nw, int64_t nvec, void* out0,

@@ -10,7 +10,7 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct Streams {
-  const u32x4* p[9];
+  const u32x4* p[16];
 };
 
 template <int NR, int NW>
@@ -30,11 +30,22 @@ __global__ __launch_bounds__(1024) void probe_kernel(Streams in, int64_t nvec, u
 
 bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+template <int NR>
+void launch(unsigned blocks, int threads, hipStream_t st, const Streams& s, int64_t nvec, int nw,
+            u32x4* o0, u32x4* o1) {
+  if (nw == 2) {
+    probe_kernel<NR, 2><<<dim3(blocks), dim3(threads), 0, st>>>(s, nvec, o0, o1);
+  } else {
+    probe_kernel<NR, 1><<<dim3(blocks), dim3(threads), 0, st>>>(s, nvec, o0, o1);
+  }
+}
+
 }  // namespace
 
 extern "C" int ar_probe_stream(const void* const* inputs, int nr, int nw, int64_t nvec, void* out0,
                                void* out1, int threads, void* stream) {
-  if (!inputs || (nr != 8 && nr != 9) || (nw != 1 && nw != 2) || nvec < 0) return 1;
+  const bool nr_ok = nr == 1 || nr == 2 || nr == 4 || nr == 8 || nr == 9 || nr == 16;
+  if (!inputs || !nr_ok || (nw != 1 && nw != 2) || nvec < 0) return 1;
   if (threads < 64 || threads > 1024 || threads % 64 != 0) return 1;
   if (nvec == 0) return 0;
   Streams s{};
@@ -48,14 +59,14 @@ extern "C" int ar_probe_stream(const void* const* inputs, int nr, int nw, int64_
   hipStream_t st = static_cast<hipStream_t>(stream);
   u32x4* o0 = static_cast<u32x4*>(out0);
   u32x4* o1 = static_cast<u32x4*>(nw == 2 ? out1 : out0);
-  if (nr == 9 && nw == 2) {
-    probe_kernel<9, 2><<<dim3(static_cast<unsigned>(blocks)), dim3(threads), 0, st>>>(s, nvec, o0, o1);
-  } else if (nr == 8 && nw == 1) {
-    probe_kernel<8, 1><<<dim3(static_cast<unsigned>(blocks)), dim3(threads), 0, st>>>(s, nvec, o0, o1);
-  } else if (nr == 9 && nw == 1) {
-    probe_kernel<9, 1><<<dim3(static_cast<unsigned>(blocks)), dim3(threads), 0, st>>>(s, nvec, o0, o1);
-  } else {
-    probe_kernel<8, 2><<<dim3(static_cast<unsigned>(blocks)), dim3(threads), 0, st>>>(s, nvec, o0, o1);
+  const unsigned b = static_cast<unsigned>(blocks);
+  switch (nr) {
+    case 1: launch<1>(b, threads, st, s, nvec, nw, o0, o1); break;
+    case 2: launch<2>(b, threads, st, s, nvec, nw, o0, o1); break;
+    case 4: launch<4>(b, threads, st, s, nvec, nw, o0, o1); break;
+    case 8: launch<8>(b, threads, st, s, nvec, nw, o0, o1); break;
+    case 9: launch<9>(b, threads, st, s, nvec, nw, o0, o1); break;
+    default: launch<16>(b, threads, st, s, nvec, nw, o0, o1); break;
   }
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }

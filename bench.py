@@ -28,6 +28,8 @@ Modes:
   --phases               markdown table: where a decode-size call's time goes (the library's
                          kernels rebuilt with their phase hooks stamping a clock, beside the
                          same calls timed without them)
+  --stream-counts        markdown table: the streaming probe's rate for 2 to 17 streams at the
+                         headline's bytes per call
 """
 from __future__ import annotations
 
@@ -391,6 +393,35 @@ def stream_ceiling(torch, H=None, Ms=(2048, 512)) -> list:
             del c
             torch.cuda.empty_cache()
     return lines
+
+
+def stream_count_table(torch, H=None) -> str:
+    """How the memory system's rate depends on the number of streams (markdown): the probe with
+    nr read and nw write streams, M chosen so that every line moves the headline's bytes
+    ((W + 3) M H 2 at W = 8, M = 2048), hipGraph replay over rotated sets."""
+    H = H or HEADLINE["H"]
+    path = os.path.join(ROOT, "all_reduce_residual_amd", "libar_probe.so")
+    if not os.path.exists(path):
+        raise SystemExit("calibration probe library not built")
+    L = ctypes.CDLL(path)
+    L.ar_probe_stream.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                  ctypes.c_void_p]
+    L.ar_probe_stream.restype = ctypes.c_int
+    total = metric_bytes("rms", HEADLINE["W"], HEADLINE["M"], H, 2)
+    out = ["| streams | rows per stream | bytes per call | µs per call | GB/s | % of 8 TB/s |",
+           "|---|---|---|---|---|---|"]
+    for nr, nw in ((1, 1), (2, 1), (4, 1), (4, 2), (8, 1), (9, 2), (16, 1)):
+        m = total // ((nr + nw) * H * 2)
+        c = ProbeCase(torch, L, nr, nw, m, H)
+        us = c.time_graph(c.calls_per_batch(60))
+        gbs = c.bytes / (us * 1e-6) / 1e9
+        out.append("| %dR+%dW | %d | %d | %.2f | %.0f | %.1f |" % (
+            nr, nw, m, c.bytes, us, gbs, 100 * gbs / HBM_PEAK_GBS))
+        print("# streams %s" % out[-1], file=sys.stderr, flush=True)
+        del c
+        torch.cuda.empty_cache()
+    return "\n".join(out)
 
 
 PHASE_NAMES = {
@@ -938,6 +969,7 @@ def main():
     ap.add_argument("--summarize-pmc-kernels", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-sweep-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_JSON"))
     ap.add_argument("--phases", action="store_true")
+    ap.add_argument("--stream-counts", action="store_true")
     args = ap.parse_args()
 
     if args.summarize_sweep_trace:
@@ -968,6 +1000,9 @@ def main():
     ar.lib()
     if args.phases:
         print(phase_table(ar, torch))
+        return 0
+    if args.stream_counts:
+        print(stream_count_table(torch))
         return 0
 
     H, W, M = HEADLINE["H"], HEADLINE["W"], HEADLINE["M"]
