@@ -57,3 +57,42 @@ def test_noalloc_rows_beyond_the_array_rejected():
     with pytest.raises(ar.ArError) as e:
         ar.ar_residual_rmsnorm_noalloc(d_parts, d_res, dev(gam), 1e-6, ro, no)
     assert e.value.status == ar.AR_ERR_UNSUPPORTED
+
+
+def test_noalloc_replayed_from_a_graph(oracle_mod):
+    """Captured once (after an eager call, the usual warm-up before capture) and replayed with
+    new inputs, with eager no-alloc calls of another shape between the replays: the array keeps
+    whatever the last call left and every replay still matches the oracle."""
+    W, M, H, dtype = 8, 16, 7168, "bf16"
+    parts, res, gam = synth.custom(W, M, H, dtype, seed=71)
+    d_parts, d_res, d_gam = [dev(p) for p in parts], dev(res), dev(gam)
+    ro, no = torch.empty_like(d_res), torch.empty_like(d_res)
+    o_parts, o_res, o_gam = synth.custom(W, 5, H, dtype, seed=72)
+    do_parts, do_res, do_gam = [dev(p) for p in o_parts], dev(o_res), dev(o_gam)
+    o_ro, o_no = torch.empty_like(do_res), torch.empty_like(do_res)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        ar.ar_residual_rmsnorm_noalloc(d_parts, d_res, d_gam, 1e-6, ro, no)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ar.ar_residual_rmsnorm_noalloc(d_parts, d_res, d_gam, 1e-6, ro, no)
+    for rep in range(3):
+        print("case noalloc graph replay", rep, flush=True)
+        p2, r2, _ = synth.custom(W, M, H, dtype, seed=80 + rep)
+        for d, h in zip(d_parts + [d_res], p2 + [r2]):
+            d.copy_(h)
+        ar.ar_residual_rmsnorm_noalloc(do_parts, do_res, do_gam, 1e-6, o_ro, o_no)
+        graph.replay()
+        torch.cuda.synchronize()
+        want_ro, want_no = oracle_mod.ar_residual_rmsnorm([host_np(p) for p in p2], host_np(r2),
+                                                          gam.numpy(), 1e-6, dtype)
+        assert_bit_exact(host_np(ro.cpu()), want_ro, dtype, "replay %d residual_out" % rep)
+        assert_norm_close(host_np(no.cpu()), want_no, dtype, "replay %d norm_out" % rep)
+        want_ro, want_no = oracle_mod.ar_residual_rmsnorm([host_np(p) for p in o_parts],
+                                                          host_np(o_res), o_gam.numpy(), 1e-6,
+                                                          dtype)
+        assert_bit_exact(host_np(o_ro.cpu()), want_ro, dtype, "eager call %d residual_out" % rep)
+        assert_norm_close(host_np(o_no.cpu()), want_no, dtype, "eager call %d norm_out" % rep)
