@@ -312,7 +312,7 @@ def median(xs) -> float:
     return v[k] if len(v) % 2 else 0.5 * (v[k - 1] + v[k])
 
 
-def lamport_lines(ar, torch, W=8, H=7168, Ms=(8, 128, 2048)) -> list:
+def lamport_lines(ar, torch, W=8, H=7168, Ms=(1, 8, 128, 512, 2048)) -> list:
     """hipGraph-replayed µs of the Lamport exchange steps (pushes + consumer, pushes alone)."""
     lines = []
     for m in Ms:
