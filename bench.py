@@ -287,7 +287,14 @@ class LamportCase(Case):
 
     def call(self, i: int, stream_handle: int) -> None:
         """Round i: W pushes, then (in "step" mode) the consumer.  A graph holds a multiple of 3
-        rounds, so that its replays keep the buffer rotation."""
+        rounds, so that its replays keep the buffer rotation.  "consume" mode: the consumer of
+        round 0 alone, again and again (it only reads, so a pushed round can be consumed any
+        number of times; its data is in place and no poll waits)."""
+        if self.mode == "consume":
+            st = self.consume(0, stream_handle)
+            if st != 0:
+                raise RuntimeError("Lamport consumer failed: %s" % self.ar.status_string(st))
+            return
         h = ctypes.c_void_p(stream_handle)
         for a in self.push_args:
             st = self.L.ar_lamport_push(*a, i, h)
@@ -313,7 +320,8 @@ def median(xs) -> float:
 
 
 def lamport_lines(ar, torch, W=8, H=7168, Ms=(1, 8, 128, 512, 2048)) -> list:
-    """hipGraph-replayed µs of the Lamport exchange steps (pushes + consumer, pushes alone)."""
+    """hipGraph-replayed µs of the Lamport exchange: a round (W pushes + the consumer), the W
+    pushes alone, and the consumer alone on a round already pushed (its data in place)."""
     lines = []
     for m in Ms:
         for pattern in ("rms", "sum"):
@@ -325,13 +333,17 @@ def lamport_lines(ar, torch, W=8, H=7168, Ms=(1, 8, 128, 512, 2048)) -> list:
             us_push = c.time_graph(calls)
             c.mode = "step"
             us_step = min(us_step, c.time_graph(calls))
+            c.call(0, torch.cuda.current_stream().cuda_stream)   # round 0, for "consume"
+            c.mode = "consume"
+            us_alone = c.time_graph(calls)
             torch.cuda.synchronize()
             status = int(c.status.item())
-            us_cons = us_step - us_push
             lines.append({"pattern": "kARResidualRMSNorm" if pattern == "rms" else "kAllReduce",
                           "W": W, "M": m, "H": H, "us_pushes": round(us_push, 3),
-                          "us_step": round(us_step, 3), "us_consumer": round(us_cons, 3),
-                          "consumer_GBs_metric": round(c.bytes / (us_cons * 1e-6) / 1e9, 1),
+                          "us_step": round(us_step, 3),
+                          "us_step_minus_pushes": round(us_step - us_push, 3),
+                          "us_consumer_alone": round(us_alone, 3),
+                          "consumer_GBs_metric": round(c.bytes / (us_alone * 1e-6) / 1e9, 1),
                           "status": status})
             print("# lamport %s" % json.dumps(lines[-1]), file=sys.stderr, flush=True)
             del c
