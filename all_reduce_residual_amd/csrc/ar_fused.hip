@@ -637,11 +637,10 @@ int launch_rmsnorm(const void* x, int64_t M, int64_t H, int dtype, const float* 
     // One block per row, grid stride over rows (at most 8 blocks per CU).  A row spans at most
     // H / vec + 2 aligned vectors, and the kernel's slots start at the 128-byte line that holds
     // the row's first element, up to 7 vectors earlier: H / vec + 9 slots.  The fewest vectors
-    // per thread (1, 2, 4 or 8) that keep the
-    // block at <= 512 threads (640 for 4, 1024 for 8) hold the row in registers, else two
-    // passes.  (Rows of 2049-2560 vectors: 4 vectors over up to 640 threads ran 8-39 % faster
-    // than 8 over 320 at M = 768 ... 4096, bf16 H = 16386 / 20002, fp16 18434, binary32 9002;
-    // bf16 H = 16386, M = 2048: 41.1 -> 30.0 us.)
+    // per thread (1, 2, 4 or 8) that keep the block at <= 512 threads (640 for 4, 1024 for 8)
+    // hold the row in registers, else two passes.  (Rows of 2049-2560 vectors: 4 vectors over
+    // up to 640 threads ran 8-39 % faster than 8 over 320 at M = 768 ... 4096, bf16
+    // H = 16386 / 20002, fp16 18434, binary32 9002; bf16 H = 16386, M = 2048: 41.1 -> 30.0 us.)
     const int vec = kVecBytes / elem_size(dtype);
     const int64_t nv = H / vec + 9;
     int vpt = 0;
@@ -844,10 +843,14 @@ int run_lamport_arm(void* rbuf, int W, int64_t M, int64_t H, int dtype, void* st
   return e == hipSuccess ? AR_OK : AR_ERR_LAUNCH;
 }
 
-// Byte offset of slot `rank` of the buffer round `round` uses.
-int64_t lamport_slot(int64_t round, int W, int rank, int64_t slot_bytes) {
-  return (int64_t(round % kLamportBuffers) * W + rank) * slot_bytes;
+// Byte offset of slot `rank` of buffer `buffer` (0, 1 or 2).
+int64_t lamport_slot(int buffer, int W, int rank, int64_t slot_bytes) {
+  return (int64_t(buffer) * W + rank) * slot_bytes;
 }
+// The buffer round `round` (>= 0) uses, and the next one (computed without round + 1, which
+// overflows at the largest round).
+int lamport_buffer(int64_t round) { return static_cast<int>(round % kLamportBuffers); }
+int lamport_next_buffer(int64_t round) { return (lamport_buffer(round) + 1) % kLamportBuffers; }
 
 int run_lamport_push(const void* partial, int rank, void* rbuf, int W, int64_t M, int64_t H,
                      int dtype, int64_t round, void* stream) {
@@ -865,8 +868,9 @@ int run_lamport_push(const void* partial, int rank, void* rbuf, int W, int64_t M
   if (st != AR_OK) return st;
   // This round's slot, and the same rank's slot of the next buffer (used two rounds ago), which
   // this push empties.
-  void* slot = static_cast<char*>(rbuf) + lamport_slot(round, W, rank, slot_bytes);
-  void* next = static_cast<char*>(rbuf) + lamport_slot(round + 1, W, rank, slot_bytes);
+  char* base = static_cast<char*>(rbuf);
+  void* slot = base + lamport_slot(lamport_buffer(round), W, rank, slot_bytes);
+  void* next = base + lamport_slot(lamport_next_buffer(round), W, rank, slot_bytes);
   const int64_t nvec = slot_bytes / kVecBytes;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // One vector per thread and a grid that covers the slot: the kernel runs no loop.
@@ -907,7 +911,7 @@ int run_lamport_sum(void* rbuf, int W, int64_t M, int64_t H, int dtype, int64_t 
   const Range o = range_of(out, bytes);
   if (overlap(o, range_of(rbuf, bytes * W * kLamportBuffers)) || overlap(o, range_of(status, 4)))
     return AR_ERR_ALIAS;
-  void* buf = static_cast<char*>(rbuf) + lamport_slot(round, W, 0, bytes);
+  void* buf = static_cast<char*>(rbuf) + lamport_slot(lamport_buffer(round), W, 0, bytes);
   int cu = 0;
   st = query_cu_count(&cu);
   if (st != AR_OK) return st;
@@ -985,7 +989,7 @@ int run_lamport_norm(void* rbuf, int W, int64_t M, int64_t H, int dtype, int64_t
   }
   cfg.nt_store = 1;
   arf::LamportSource src{status, spin_limit ? spin_limit : kDefaultSpinLimit};
-  void* buf = static_cast<char*>(rbuf) + lamport_slot(round, W, 0, bytes);
+  void* buf = static_cast<char*>(rbuf) + lamport_slot(lamport_buffer(round), W, 0, bytes);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   switch (dtype) {

@@ -293,3 +293,29 @@ def test_few_rows_fewest_vectors_per_thread(oracle_mod, W, M, H, dtype):
             [host_np(p) for p in parts], host_np(res), gam.numpy(), 1e-6, dtype)
         assert_bit_exact(host_np(ro.cpu()), want_ro, dtype, "lamport residual_out")
         assert_norm_close(host_np(no.cpu()), want_no, dtype, "lamport norm_out")
+
+
+def test_largest_round_number(oracle_mod):
+    """Round 2^63 - 1 (buffer 1; its push empties buffer 2): the buffer arithmetic does not
+    overflow at the largest round the ABI takes."""
+    W, M, H, dtype = 4, 3, 1024, "bf16"
+    rnd = 2 ** 63 - 1
+    parts, res, gam = synth.custom(W, M, H, dtype, seed=63)
+    tdt = synth.TORCH_DTYPES[dtype]
+    d_parts = [dev(p) for p in parts]
+    rbuf = _new_rbuf(W, M, H, tdt)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for r, p in enumerate(d_parts):
+        ar.ar_lamport_push(p, r, rbuf, rnd)
+    d_res = dev(res)
+    ro, no = torch.empty_like(d_res), torch.empty_like(d_res)
+    ar.ar_lamport_residual_rmsnorm(rbuf, rnd, d_res, dev(gam), 1e-6, ro, no, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert rnd % NBUF == 1
+    check_round_state(rbuf, rnd, d_parts)
+    assert _empty(rbuf[0])
+    want_ro, want_no = oracle_mod.ar_residual_rmsnorm([host_np(p) for p in parts], host_np(res),
+                                                      gam.numpy(), 1e-6, dtype)
+    assert_bit_exact(host_np(ro.cpu()), want_ro, dtype, "residual_out")
+    assert_norm_close(host_np(no.cpu()), want_no, dtype, "norm_out")
