@@ -161,8 +161,9 @@ def test_fused_grid_stride(oracle_mod, kind, dtype):
 @pytest.mark.parametrize("kind", ["big", "tiny"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_split_rows(oracle_mod, kind, dtype):
-    """ar_residual_rmsnorm_ws on a few-row shape the planner splits (W = 8, H = 7168), and the
-    split kernel with an explicit shape of 4 segments."""
+    """ar_residual_rmsnorm_ws on a few-row shape the planner splits (W = 8, H = 7168), the split
+    kernel with an explicit shape of 4 segments, and the same shape with no polls at all (every
+    block computes every segment's sum itself before the range branch)."""
     W, H = 8, 7168
     parts, res, gam, eps = range_inputs(W, H, dtype, kind, seed=11)
     M = res.shape[0]
@@ -171,9 +172,12 @@ def test_split_rows(oracle_mod, kind, dtype):
     want = want_rms(oracle_mod, parts, res, gam, eps, dtype)
     d_parts, d_res, d_gam = [dev(p) for p in parts], dev(res), dev(gam)
     ws = ar.new_workspace(M, "cuda")
-    for cfg in (None, {"threads_per_block": 256, "vecs_per_thread": 1,
-                       "segments": -(-(H * (4 if dtype == "fp32" else 2) // 16) // 256),
-                       "max_polls": 1 << 14}):
+    seg4 = -(-(H * (4 if dtype == "fp32" else 2) // 16) // 256)
+    for cfg in (None,
+                {"threads_per_block": 256, "vecs_per_thread": 1, "segments": seg4,
+                 "max_polls": 1 << 14},
+                {"threads_per_block": 256, "vecs_per_thread": 1, "segments": seg4,
+                 "max_polls": 0}):
         print("case split", kind, dtype, cfg, flush=True)
         ro, no = torch.empty_like(d_res), torch.empty_like(d_res)
         ar.ar_residual_rmsnorm_ws(d_parts, d_res, d_gam, eps, ro, no, ws, config=cfg)
