@@ -222,7 +222,8 @@ int ar_residual_rmsnorm_ws(const void* const* inputs, int W, int64_t M, int64_t 
  * slots in a device array inside the library instead of a caller workspace: AR_NOALLOC_MAX_ROWS
  * rows of AR_SPLIT_SLOTS 8-byte slots (256 KiB), one copy per GPU, held until the process ends.
  * Nothing is allocated: the first call on a device looks up that array's address and clears it
- * with a kernel on `stream` (no memset node).
+ * with a kernel on `stream` (no memset node); make that first call outside graph capture (a
+ * warm-up call, as before any capture).
  *   M > AR_NOALLOC_MAX_ROWS : AR_ERR_UNSUPPORTED (ar_residual_rmsnorm needs no scratch at all)
  * Every call on one GPU shares that GPU's array and leaves it valid for the next call; calls
  * that overlap in time on one GPU (other streams, other threads) race on it and may produce
@@ -284,11 +285,12 @@ int ar_all_gather(const void* const* slices, int W, int64_t M, int64_t H, int dt
  * the consumer of round k - 1 complete before the push of round k).  Then the push of round k
  * empties a slot no consumer still reads: its rank finished consuming round k - 1, which needed
  * every rank's push of round k - 1, made after that rank consumed round k - 2.  Producers and
- * consumers of one round may run concurrently (on other streams, or, with peer-mapped memory,
- * other GPUs): slots move as 16-byte device-coherent accesses (each aligned dword single-copy
- * atomic; elements are tested one by one), and each producer thread empties its vector of the
- * next buffer, and waits for that store to complete, before it stores its vector of the current
- * one.  A captured graph replays the same round numbers: capture 3 consecutive rounds (or a
+ * consumers of one round may run concurrently on other streams of the same GPU: slots move as
+ * 16-byte device-coherent accesses (agent scope; each aligned dword single-copy atomic; elements
+ * are tested one by one), and each producer thread empties its vector of the next buffer, and
+ * waits for that store to complete, before it stores its vector of the current one.  (Producers
+ * on other GPUs writing through peer mappings would need system-scope accesses; this library
+ * runs the exchange on one GPU.)  A captured graph replays the same round numbers: capture 3 consecutive rounds (or a
  * multiple of 3) so that replays keep the rotation.
  *
  * Every wait is bounded: after `spin_limit` polls of one 16-byte vector (0 = 65536) the consumer
