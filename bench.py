@@ -241,9 +241,10 @@ class GatherCase(Case):
 class LamportCase(Case):
     """Lamport-style one-shot exchange on one GPU: per round, W producer pushes (each writes its
     slot of this round's buffer and empties its slot of the next), then the polling consumer,
-    which only reads.  `mode` "push" times the W pushes alone, "step" pushes + consumer; the
-    consumer's share is the difference.  The three rotating buffers are the only input set (the
-    receive buffers are state), so small shapes are cache-warm."""
+    which only reads.  `mode` "push" times the W pushes alone, "step" pushes + consumer (the
+    three rotating buffers are the only set: the receive buffers are state, so small shapes are
+    cache-warm), "consume" the consumer alone over the receive-buffer sets of prepare_consume,
+    each holding a pushed round 0, in turn."""
 
     def __init__(self, ar, torch, pattern, W, M, H, dtype="bf16", eps=1e-6):
         self.ar, self.torch = ar, torch
@@ -270,28 +271,55 @@ class LamportCase(Case):
             self.gamma = torch.empty(H, dtype=torch.float32, device="cuda").uniform_(
                 0.8, 1.2, generator=g)
             self.ro, self.no = torch.empty_like(self.res), torch.empty_like(self.res)
-            self.consume = lambda rnd, h: L.ar_lamport_residual_rmsnorm(
-                self.rbuf.data_ptr(), W, M, H, self.dt, rnd, self.res.data_ptr(),
-                self.gamma.data_ptr(), ctypes.c_float(eps), self.ro.data_ptr(),
-                self.no.data_ptr(), self.status.data_ptr(), 0, ctypes.c_void_p(h))
         else:
             self.out = torch.empty((M, H), dtype=tdt, device="cuda")
-            self.consume = lambda rnd, h: L.ar_lamport_sum(
-                self.rbuf.data_ptr(), W, M, H, self.dt, rnd, self.out.data_ptr(),
-                self.status.data_ptr(), 0, ctypes.c_void_p(h))
-        st = L.ar_lamport_arm(self.rbuf.data_ptr(), W, M, H, self.dt,
-                              ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
-        if st != 0:
-            raise RuntimeError("ar_lamport_arm failed: %s" % ar.status_string(st))
+        self.sets = [self.rbuf]
+        self._arm(self.rbuf)
         torch.cuda.synchronize()
+
+    def _arm(self, rbuf) -> None:
+        st = self.L.ar_lamport_arm(rbuf.data_ptr(), self.W, self.M, self.H, self.dt,
+                                   ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream))
+        if st != 0:
+            raise RuntimeError("ar_lamport_arm failed: %s" % self.ar.status_string(st))
+
+    def consume(self, rnd: int, h: int, rbuf=None) -> int:
+        rb = (self.rbuf if rbuf is None else rbuf).data_ptr()
+        W, M, H = self.W, self.M, self.H
+        if self.pattern == "rms":
+            return self.L.ar_lamport_residual_rmsnorm(
+                rb, W, M, H, self.dt, rnd, self.res.data_ptr(), self.gamma.data_ptr(),
+                ctypes.c_float(self.eps), self.ro.data_ptr(), self.no.data_ptr(),
+                self.status.data_ptr(), 0, ctypes.c_void_p(h))
+        return self.L.ar_lamport_sum(rb, W, M, H, self.dt, rnd, self.out.data_ptr(),
+                                     self.status.data_ptr(), 0, ctypes.c_void_p(h))
+
+    def prepare_consume(self) -> int:
+        """Receive-buffer sets for "consume" mode, each armed and holding a pushed round 0:
+        enough that one pass over them reads at least ROTATE_BYTES of slots (at most 64 sets), so
+        the consumer's reads come from HBM as in the other timings.  Returns the set count."""
+        torch = self.torch
+        slot_bytes = self.W * self.M * self.H * self.esize        # the slots one round reads
+        n = max(1, min(64, math.ceil(ROTATE_BYTES / slot_bytes)))
+        self.sets = [self.rbuf] + [torch.empty_like(self.rbuf) for _ in range(n - 1)]
+        h = torch.cuda.current_stream().cuda_stream
+        for rb in self.sets:
+            self._arm(rb)
+            for r, p in enumerate(self.parts):
+                st = self.L.ar_lamport_push(p.data_ptr(), r, rb.data_ptr(), self.W, self.M,
+                                            self.H, self.dt, 0, ctypes.c_void_p(h))
+                if st != 0:
+                    raise RuntimeError("ar_lamport_push failed: %s" % self.ar.status_string(st))
+        torch.cuda.synchronize()
+        return n
 
     def call(self, i: int, stream_handle: int) -> None:
         """Round i: W pushes, then (in "step" mode) the consumer.  A graph holds a multiple of 3
         rounds, so that its replays keep the buffer rotation.  "consume" mode: the consumer of
-        round 0 alone, again and again (it only reads, so a pushed round can be consumed any
+        round 0 of set i mod (sets) alone (it only reads, so a pushed round can be consumed any
         number of times; its data is in place and no poll waits)."""
         if self.mode == "consume":
-            st = self.consume(0, stream_handle)
+            st = self.consume(0, stream_handle, self.sets[i % len(self.sets)])
             if st != 0:
                 raise RuntimeError("Lamport consumer failed: %s" % self.ar.status_string(st))
             return
@@ -333,16 +361,16 @@ def lamport_lines(ar, torch, W=8, H=7168, Ms=(1, 8, 128, 512, 2048)) -> list:
             us_push = c.time_graph(calls)
             c.mode = "step"
             us_step = min(us_step, c.time_graph(calls))
-            c.call(0, torch.cuda.current_stream().cuda_stream)   # round 0, for "consume"
+            sets = c.prepare_consume()
             c.mode = "consume"
-            us_alone = c.time_graph(calls)
+            us_alone = c.time_graph(sets * max(1, math.ceil(calls / sets)))
             torch.cuda.synchronize()
             status = int(c.status.item())
             lines.append({"pattern": "kARResidualRMSNorm" if pattern == "rms" else "kAllReduce",
                           "W": W, "M": m, "H": H, "us_pushes": round(us_push, 3),
                           "us_step": round(us_step, 3),
                           "us_step_minus_pushes": round(us_step - us_push, 3),
-                          "us_consumer_alone": round(us_alone, 3),
+                          "us_consumer_alone": round(us_alone, 3), "consume_sets": sets,
                           "consumer_GBs_metric": round(c.bytes / (us_alone * 1e-6) / 1e9, 1),
                           "status": status})
             print("# lamport %s" % json.dumps(lines[-1]), file=sys.stderr, flush=True)
