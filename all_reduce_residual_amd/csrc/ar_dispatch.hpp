@@ -83,6 +83,13 @@ hipError_t launch_norm_v(const void* const* inputs, const void* residual, const 
   const void* fn =
       c.nt_store ? reinterpret_cast<const void*>(&arf::ar_norm_kernel<T, W, VPT, true>)
                  : reinterpret_cast<const void*>(&arf::ar_norm_kernel<T, W, VPT, false>);
+  // One rank per batch: instantiated for the shapes the launch checks allow (2 vectors per
+  // thread for W = 4 ... 16, 4 for W = 2 and 4; non-temporal stores).
+  if constexpr ((VPT == 2 && W >= 4 && W <= 16) || (VPT == 4 && W >= 2 && W <= 4)) {
+    if (c.rank_at_a_time)
+      fn = reinterpret_cast<const void*>(
+          &arf::ar_norm_kernel<T, W, VPT, true, arf::StreamSource, false, true>);
+  }
   return hipLaunchKernel(fn, dim3(c.grid), dim3(c.threads_per_block), args, 0, s);
 }
 

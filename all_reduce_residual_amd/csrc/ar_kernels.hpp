@@ -515,7 +515,14 @@ __device__ inline void load_gamma(const f32x4* gamma, uint32_t vec, float (&g)[k
 // kNormOnly: the RMSNorm step alone on a stored tensor x = in.p[0] (W = 1; residual and
 // residual_out are unused): norm_out = RMSNorm(x) * gamma.  The second kernel of the two-kernel
 // path, and a stand-alone RMSNorm.
-template <class T, int W, int VPT, bool kNtStore, class Src = StreamSource, bool kNormOnly = false>
+//
+// kRankAtATime (rows whose chains are all held at once, below): one rank's vectors per batch
+// instead of up to 16 loads, so a block reads one tensor's row at a time.  The launch planner
+// takes it while every row of a call is resident at once (one to three rows per CU): all CUs
+// then run the same phase, and reading the W + 1 tensors one after another, rather than all
+// of them together, is what HBM serves faster there.  The arithmetic is the same.
+template <class T, int W, int VPT, bool kNtStore, class Src = StreamSource, bool kNormOnly = false,
+          bool kRankAtATime = false>
 __global__ __launch_bounds__(kMaxThreads) void ar_norm_kernel(
     RankPtrs<W> in, const u32x4* residual, const f32x4* gamma, u32x4* residual_out,
     u32x4* norm_out, int64_t M, int V, int L, int R, float eps, float count_h, Src src) {
@@ -651,15 +658,18 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_kernel(
       // those loads one rank at a time, each a round trip after the previous one.  The staged
       // form issues the residual's loads first (its fences would otherwise hold them back a
       // round trip); it is still added after the W partials.
-      constexpr bool kStageChains = (W == 2 || W == 4) && VPT == 2;
+      // One rank's 4 vectors per batch are staged too, with the residual first: left alone,
+      // the fp16 W = 4 form issued them a round trip apart.
+      constexpr bool kStageChains =
+          ((W == 2 || W == 4) && VPT == 2) || (kRankAtATime && VPT >= 4);
       u32x4 res_v[VPT];
       if constexpr (kStageChains) {
 #pragma unroll
         for (int k = 0; k < VPT; ++k) res_v[k] = load_stream(at(residual + base, boff[k]));
       }
       float acc[VPT][kVec];
-      src.template sum<T, W, VPT, default_max_loads<T, VPT>(), kStageChains>(in, base, boff, ok,
-                                                                             acc);
+      constexpr int kLoads = kRankAtATime ? VPT : default_max_loads<T, VPT>();
+      src.template sum<T, W, VPT, kLoads, kStageChains>(in, base, boff, ok, acc);
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {
         if constexpr (!kStageChains) res_v[k] = load_stream(at(residual + base, boff[k]));

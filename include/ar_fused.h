@@ -97,7 +97,11 @@ typedef enum {
  *   grid              : number of blocks (>= 1); blocks loop over the work with a grid stride
  *   flat              : 1 for the sum pattern (flat vector decomposition), 0 for the norm
  *   nt_store          : 1 = outputs are written with non-temporal stores, 0 = ordinary stores
- *                       (inputs are always read with non-temporal loads) */
+ *                       (inputs are always read with non-temporal loads)
+ *   rank_at_a_time    : norm pattern only: 1 = each thread loads one rank's vectors at a time
+ *                       instead of up to 16 loads of several ranks (same results); allowed with
+ *                       nt_store = 1 and 2 vectors per thread for 4 <= W <= 16, or 4 for W = 2
+ *                       and 4; 0 otherwise and for the sum pattern */
 typedef struct {
   int32_t threads_per_block;
   int32_t vecs_per_thread;
@@ -106,6 +110,7 @@ typedef struct {
   int32_t grid;
   int32_t flat;
   int32_t nt_store;
+  int32_t rank_at_a_time;
 } ar_launch_cfg_t;
 
 /* kAllReduce.  out[m, i] = RN_T(x_0[m, i] + ... + x_{W-1}[m, i]).

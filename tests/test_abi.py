@@ -99,6 +99,14 @@ def test_launch_config_invariants(cu):
             assert 64 <= t <= 1024 and t % 64 == 0, c
             assert c["nt_store"] in (0, 1)
             assert c["grid"] >= 1
+            assert c["rank_at_a_time"] in (0, 1)
+            if c["rank_at_a_time"]:
+                # Only where it is built: 2 vectors per thread up to W = 16, 4 up to W = 4, one
+                # row per block, non-temporal stores, one to three rows per CU.
+                vpt = c["vecs_per_thread"]
+                assert pat == RMS and c["nt_store"] == 1 and c["rows_per_block"] == 1, c
+                assert (vpt == 2 and 4 <= W <= 16) or (vpt == 4 and 2 <= W <= 4), c
+                assert cu < M <= 3 * cu, c
             if pat == SUM:
                 assert c["flat"] == 1 and c["vecs_per_thread"] in (1, 2, 4)
                 nvec = M * H // _vec(dt)
@@ -123,6 +131,22 @@ def test_launch_config_headline_shapes():
         c = ar.ar_launch_config(RMS, 8, M, 7168, BF16, cu_count=256)
         assert c["grid"] == M and c["rows_per_block"] == 1
         assert c["lanes_per_row"] * c["vecs_per_thread"] >= 896
+
+
+def test_launch_config_rank_at_a_time_band():
+    """One rank per batch exactly while every row is resident with one to three rows per CU."""
+    def rat(W, M, H, dt, cu=256):
+        return ar.ar_launch_config(RMS, W, M, H, dt, cu_count=cu)["rank_at_a_time"]
+    for M, want in ((1, 0), (128, 0), (256, 0), (257, 1), (512, 1), (768, 1), (769, 0),
+                    (1024, 0), (2048, 0)):
+        assert rat(8, M, 7168, BF16) == want, M
+    assert rat(16, 512, 8192, FP16) == 1          # the fp16 W = 16 workload (2 rows per CU)
+    assert rat(4, 512, 7168, BF16) == 1 and rat(2, 512, 7168, BF16) == 1   # W = 2: 4 vectors
+    assert rat(2, 512, 4096, BF16) == 0           # W = 2 with 2 vectors: staged chains already
+    assert rat(32, 512, 7168, BF16) == 0 and rat(1, 512, 7168, BF16) == 0
+    assert rat(8, 160, 7168, BF16, cu=80) == 1 and rat(8, 80, 7168, BF16, cu=80) == 0
+    for M in (1, 512, 2048):                      # never for the sum
+        assert ar.ar_launch_config(SUM, 8, M, 7168, BF16, cu_count=256)["rank_at_a_time"] == 0
 
 
 def test_launch_config_sum_resident_round():
@@ -280,6 +304,23 @@ def test_validation_rejects_before_device_access(L):
                                 ctypes.byref(bad)) == ar.AR_ERR_INVALID_ARG
     assert L.ar_sum_with_config(_ptrs(p[:2]), 2, 4, 256, BF16, out, None,
                                 None) == ar.AR_ERR_INVALID_ARG
+    # One rank per batch: never for the sum, and for the norm only where it is built.
+    sum_rat = ar.LaunchConfig(threads_per_block=64, vecs_per_thread=1, lanes_per_row=0,
+                              rows_per_block=0, grid=1, flat=1, nt_store=1, rank_at_a_time=1)
+    assert L.ar_sum_with_config(_ptrs(p[:2]), 2, 4, 256, BF16, out, None,
+                                ctypes.byref(sum_rat)) == ar.AR_ERR_INVALID_ARG
+    nargs = (_ptrs(p[:2]), 2, 4, 256, BF16, 0xA00000, 0xB00000, 1e-6, 0xC00000, 0xD00000, None)
+    for vpt, lanes, nt, rat in ((8, 64, 1, 1), (2, 64, 0, 1), (2, 64, 1, 2), (1, 64, 1, 1),
+                                (2, 64, 1, 1)):      # the last: W = 2 with 2 vectors
+        cfg = ar.LaunchConfig(threads_per_block=64, vecs_per_thread=vpt, lanes_per_row=lanes,
+                              rows_per_block=1, grid=4, flat=0, nt_store=nt, rank_at_a_time=rat)
+        assert L.ar_residual_rmsnorm_with_config(*nargs, ctypes.byref(cfg)) == \
+            ar.AR_ERR_INVALID_ARG, (vpt, nt, rat)
+    many = (_ptrs(p[:16] * 2), 32, 4, 256, BF16, 0xA00000, 0xB00000, 1e-6, 0xC00000, 0xD00000,
+            None)
+    cfg = ar.LaunchConfig(threads_per_block=64, vecs_per_thread=2, lanes_per_row=64,
+                          rows_per_block=1, grid=4, flat=0, nt_store=1, rank_at_a_time=1)
+    assert L.ar_residual_rmsnorm_with_config(*many, ctypes.byref(cfg)) == ar.AR_ERR_INVALID_ARG
 
 
 def test_zero_rows_returns_ok_without_device(L):

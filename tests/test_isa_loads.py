@@ -31,6 +31,9 @@ SHAPES = [(w, v) for w in (1, 2, 4, 8) for v in (1, 2)] + [(16, 1)]
 # Wide rows (many vectors per thread, one or a few chains per batch): waits between rank batches
 # are by design, but never one per load.
 WIDE = [(8, 8), (16, 8), (32, 8), (64, 8), (16, 4), (64, 4)]
+# One rank per batch (the planner's shapes for one to three rows per CU): a wait between rank
+# batches is the point, a wait inside one is not.
+RANK = [(w, 2) for w in (4, 8, 16)] + [(w, 4) for w in (2, 4)]
 TYPES = ("Bf16", "F16", "F32")
 TN = {"Bf16": "4Bf16", "F16": "3F16", "F32": "3F32"}
 
@@ -46,6 +49,9 @@ def _source() -> str:
         for w, v in SHAPES + WIDE:
             refs.append("reinterpret_cast<const void*>(&arf::ar_norm_kernel<arf::%s, %d, %d, true>)"
                         % (t, w, v))
+        for w, v in RANK:
+            refs.append("reinterpret_cast<const void*>(&arf::ar_norm_kernel<arf::%s, %d, %d, true, "
+                        "arf::StreamSource, false, true>)" % (t, w, v))
         for w in SUM_W:
             for v in (1, 2):
                 refs.append("reinterpret_cast<const void*>(&arf::ar_norm_split_kernel<arf::%s, %d, "
@@ -96,8 +102,9 @@ def _sum_symbol(t: str, w: int, u: int) -> str:
     return "_ZN3arf13ar_sum_kernelINS_%sELi%dELi%dELb1ENS_12StreamSourceEEE" % (tn, w, u)
 
 
-def _norm_symbol(t: str, w: int, v: int) -> str:
-    return "_ZN3arf14ar_norm_kernelINS_%sELi%dELi%dELb1E" % (TN[t], w, v)
+def _norm_symbol(t: str, w: int, v: int, rank_at_a_time: bool = False) -> str:
+    return ("_ZN3arf14ar_norm_kernelINS_%sELi%dELi%dELb1ENS_12StreamSourceELb0ELb%dE"
+            % (TN[t], w, v, int(rank_at_a_time)))
 
 
 def _norm_streaming_loads(asm: str, kernel: str = "ar_norm_kernel", stop: str = "") -> dict:
@@ -166,7 +173,7 @@ def norm_asm():
 
 def test_every_planned_shape_is_compiled(norm_asm):
     waits = _waits_between_streaming_loads(norm_asm)
-    assert len(waits) == len(TYPES) * (len(SHAPES) + len(WIDE)), sorted(waits)
+    assert len(waits) == len(TYPES) * (len(SHAPES) + len(WIDE) + len(RANK)), sorted(waits)
     assert len(_sum_fast_path_waits(norm_asm)) == len(TYPES) * len(SUM_W) * len(SUM_U)
 
 
@@ -205,6 +212,22 @@ def test_wide_rows_loads_not_serialized(norm_asm):
             sym = [k for k in waits if k.startswith(_norm_symbol(t, w, v))]
             assert len(sym) == 1, (t, w, v, sym)
             if loads[sym[0]] == 0 or waits[sym[0]] * 4 > loads[sym[0]]:
+                bad.append((t, w, v, loads[sym[0]], waits[sym[0]]))
+    assert not bad, "(type, W, vectors per thread, loads, full waits): %s" % bad
+
+
+def test_rank_at_a_time_waits_only_between_ranks(norm_asm):
+    """One rank per batch: every one of the (W + 1) x VPT streaming loads is issued, and full
+    waits fall only between rank batches (at most W of them), never between the VPT loads of one
+    rank's batch."""
+    waits = _waits_between_streaming_loads(norm_asm)
+    loads = _norm_streaming_loads(norm_asm)
+    bad = []
+    for t in TYPES:
+        for w, v in RANK:
+            sym = [k for k in waits if k.startswith(_norm_symbol(t, w, v, True))]
+            assert len(sym) == 1, (t, w, v, sym)
+            if loads[sym[0]] < (w + 1) * v or waits[sym[0]] > w:
                 bad.append((t, w, v, loads[sym[0]], waits[sym[0]]))
     assert not bad, "(type, W, vectors per thread, loads, full waits): %s" % bad
 

@@ -148,6 +148,43 @@ def test_norm_launch_shapes_agree(oracle_mod, H):
         run_rms_both(oracle_mod, parts, res, gam, 1e-6, dtype, config=cfg, oracle_out=want)
 
 
+RANK_CASES = [(W, H, dtype, vpt) for W in (2, 4, 8, 16) for dtype in ("bf16", "fp16", "fp32")
+              for H, vpt in ((1000 if dtype == "fp32" else 2000, 2), (2040, 4))
+              if (vpt == 2 and W >= 4) or (vpt == 4 and W <= 4)]
+
+
+@pytest.mark.parametrize("W,H,dtype,vpt", RANK_CASES,
+                         ids=["W%d-H%d-%s-v%d" % c for c in RANK_CASES])
+def test_rank_at_a_time_shapes_agree(oracle_mod, W, H, dtype, vpt):
+    """One rank per batch (the planner's form for one to three rows per CU) gives the oracle's
+    result: one and two rows per block, a ragged row (lanes past its last vector), grid stride."""
+    M = 13
+    parts, res, gam = synth.custom(W, M, H, dtype, seed=W * 7 + H + vpt)
+    want = oracle_mod.ar_residual_rmsnorm([host_np(p) for p in parts], host_np(res),
+                                          gam.numpy(), 1e-6, dtype)
+    V = H * (4 if dtype == "fp32" else 2) // 16
+    lanes = -(-(-(-V // vpt)) // 64) * 64
+    for rows, grid in ((1, M), (1, 4), (2, 3)):
+        if lanes * rows > 1024:
+            continue
+        cfg = dict(threads_per_block=lanes * rows, vecs_per_thread=vpt, lanes_per_row=lanes,
+                   rows_per_block=rows, grid=grid, flat=0, nt_store=1, rank_at_a_time=1)
+        print("case rank-at-a-time", W, H, dtype, cfg, flush=True)
+        run_rms_both(oracle_mod, parts, res, gam, 1e-6, dtype, config=cfg, oracle_out=want)
+
+
+def test_planned_rank_at_a_time_workloads(oracle_mod):
+    """The planned shape at one to three rows per CU is the rank-at-a-time form: the wide-hidden
+    call at M = 512 and 768 against the oracle on every row."""
+    cu = ar.ar_device_cu_count()
+    for M in (2 * cu, 3 * cu):
+        assert ar.ar_launch_config(ar.PATTERN_AR_RESIDUAL_RMSNORM, 8, M, 7168,
+                                   ar.DTYPE_BF16)["rank_at_a_time"] == 1
+        print("case planned rank-at-a-time M=%d" % M, flush=True)
+        parts, res, gam = synth.inputs(synth.WORKLOADS["wide_hidden"], M)
+        run_rms_both(oracle_mod, parts, res, gam, 1e-6, "bf16")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_sum_launch_shapes_agree(oracle_mod, dtype):
     parts, _, _ = synth.custom(8, 37, 1000, dtype, seed=77, with_norm=False)
