@@ -60,7 +60,7 @@ class LaunchConfig(ctypes.Structure):
     _fields_ = [("threads_per_block", ctypes.c_int32), ("vecs_per_thread", ctypes.c_int32),
                 ("lanes_per_row", ctypes.c_int32), ("rows_per_block", ctypes.c_int32),
                 ("grid", ctypes.c_int32), ("flat", ctypes.c_int32), ("nt_store", ctypes.c_int32),
-                ("rank_at_a_time", ctypes.c_int32)]
+                ("ranks_per_batch", ctypes.c_int32)]
 
     def as_dict(self) -> Dict[str, int]:
         return {name: int(getattr(self, name)) for name, _ in self._fields_}

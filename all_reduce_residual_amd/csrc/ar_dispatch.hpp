@@ -83,12 +83,21 @@ hipError_t launch_norm_v(const void* const* inputs, const void* residual, const 
   const void* fn =
       c.nt_store ? reinterpret_cast<const void*>(&arf::ar_norm_kernel<T, W, VPT, true>)
                  : reinterpret_cast<const void*>(&arf::ar_norm_kernel<T, W, VPT, false>);
-  // One rank per batch: instantiated for the shapes the launch checks allow (2 vectors per
-  // thread for W = 4 ... 16, 4 for W = 2 and 4; non-temporal stores).
-  if constexpr ((VPT == 2 && W >= 4 && W <= 16) || (VPT == 4 && W >= 2 && W <= 4)) {
-    if (c.rank_at_a_time)
+  // Fixed rank batches: instantiated for the shapes the launch checks allow.
+  if constexpr (arf::rank_batch_instantiated(W, VPT, 1)) {
+    if (c.ranks_per_batch == 1)
       fn = reinterpret_cast<const void*>(
-          &arf::ar_norm_kernel<T, W, VPT, true, arf::StreamSource, false, true>);
+          &arf::ar_norm_kernel<T, W, VPT, true, arf::StreamSource, false, 1>);
+  }
+  if constexpr (arf::rank_batch_instantiated(W, VPT, 2)) {
+    if (c.ranks_per_batch == 2)
+      fn = reinterpret_cast<const void*>(
+          &arf::ar_norm_kernel<T, W, VPT, true, arf::StreamSource, false, 2>);
+  }
+  if constexpr (arf::rank_batch_instantiated(W, VPT, 4)) {
+    if (c.ranks_per_batch == 4)
+      fn = reinterpret_cast<const void*>(
+          &arf::ar_norm_kernel<T, W, VPT, true, arf::StreamSource, false, 4>);
   }
   return hipLaunchKernel(fn, dim3(c.grid), dim3(c.threads_per_block), args, 0, s);
 }

@@ -155,7 +155,7 @@ void plan_sum(int W, int64_t n, int dtype, int cu, ar_launch_cfg_t* c, int max_r
   c->rows_per_block = 0;
   c->grid = cap_grid(ceil_div(nvec, int64_t(threads) * u));
   c->flat = 1;
-  c->rank_at_a_time = 0;
+  c->ranks_per_batch = 0;
   // Non-temporal stores measured faster except for outputs that are large next to the reads
   // (W <= 4 at 64 MiB and beyond, W = 8 at 160 MiB): there ordinary stores win by 3-8 %.
   const int64_t out_bytes = n * elem_size(dtype);
@@ -238,27 +238,43 @@ void plan_norm(int W, int64_t M, int64_t H, int dtype, int cu, ar_launch_cfg_t* 
   c->grid = cap_grid(ceil_div(M, c->rows_per_block));
   c->flat = 0;
   c->nt_store = 1;  // measured faster from decode to prefill sizes
-  // One rank per batch while every row is resident at once with one to three rows per CU
-  // (cu < M <= 3 cu; whole rows of 2 vectors per thread for 4 to 16 partials, or of 4 for 2 or
-  // 4): the CUs then run in the same phase, and reading the tensors one after another instead
-  // of all together is what HBM serves faster.  Interleaved A/B of the planned shapes: W = 8
-  // H = 7168 bf16 M = 384 / 512 / 768 2.7 / 6.1 / 4.1 % faster; W = 4 2.7 / 8.5 / 0.5 %
-  // (binary32 M = 512 / 768: 2.9 / 8.7 %); fp16 W = 16 H = 8192 11.3 / 4.0 / 3.8 %; W = 2 with
-  // 4 vectors (H = 7168, M = 512 / 768) 8.1 / 5.4 %.  W = 2 with 2 vectors, whose chains are
-  // staged already, lost up to 6 % (H = 4096, M = 512).  With fewer rows each row's chain of
-  // W + 1 round trips is the latency (W = 8 M = 128: 30 % slower); at 4 rows per CU it lost
-  // 5-7 % at H = 7168, and beyond it was even or mixed.
-  c->rank_at_a_time = (M > cu && M <= int64_t(cu) * 3 && c->rows_per_block == 1 &&
-                       ((vpt == 2 && W >= 4 && W <= 16) || (vpt == 4 && W >= 2 && W <= 4)))
-                          ? 1
-                          : 0;
+  // Fixed rank batches for whole rows (one row per block).  One rank per batch while every row
+  // is resident at once with one to three rows per CU (cu < M <= 3 cu; 2 vectors per thread for
+  // 4 to 16 partials, or 4 for 2 or 4): the CUs then run in the same phase, and reading the
+  // tensors one after another instead of all together is what HBM serves faster.  Interleaved
+  // A/B of the planned shapes: W = 8 H = 7168 bf16 M = 384 / 512 / 768 2.7 / 6.1 / 4.1 % faster;
+  // W = 4 2.7 / 8.5 / 0.5 % (binary32 M = 512 / 768: 2.9 / 8.7 %); fp16 W = 16 H = 8192
+  // 11.3 / 4.0 / 3.8 %; W = 2 with 4 vectors (H = 7168, M = 512 / 768) 8.1 / 5.4 %.  W = 2 with
+  // 2 vectors, whose chains are staged already, lost up to 6 % (H = 4096, M = 512).  With fewer
+  // rows each row's chain of W + 1 round trips is the latency (W = 8 M = 128: 30 % slower).
+  // From more than 3 rows per CU the blocks drift apart and one rank per batch lost 5-7 %, but
+  // batches of two ranks (four at W = 8 with 16-bit rows) still beat the default 16 loads over
+  // 8 ranks.  Two vectors per thread, M = 800 ... 4096, interleaved A/B of three rounds: W = 8
+  // H = 7168 bf16 1-2 % faster with 4 ranks (2 ranks were 1-3 % slower from M = 1536), fp16
+  // H = 8192 4-7 %, binary32 H = 4096 1-7 % (2 ranks); W = 4 H = 7168 bf16 1-4 %; W = 16 1-5 %
+  // (fp16 H = 8192 M = 3072: 1 % slower); W = 32 / 64 4-7 %.  One vector per thread at W >= 32 (the 1024-lane rows, and rows of up to
+  // 512 vectors), 2 ranks: 16-bit rows 2.5-10 % faster (W = 32 M = 2048 H = 8192 fp16:
+  // 203.5 -> 183.5 us), binary32 H = 2048 W = 32 M = 2048 10 % faster but W = 64 M = 1024 4 %
+  // slower, so binary32 takes it from 8 rows per CU.  One vector at W = 8 / 16 was mixed.
+  int rpb = 0;
+  if (c->rows_per_block == 1 && M > cu) {
+    if (M <= int64_t(cu) * 3) {
+      if ((vpt == 2 && W >= 4 && W <= 16) || (vpt == 4 && W >= 2 && W <= 4)) rpb = 1;
+    } else if (vpt == 2 && W >= 4) {
+      rpb = (W == 8 && elem_size(dtype) == 2) ? 4 : 2;
+    } else if (vpt == 1 && W >= 32 && (elem_size(dtype) == 2 || M >= int64_t(cu) * 8)) {
+      rpb = 2;
+    }
+  }
+  c->ranks_per_batch = rpb;
 }
 
 // A caller-supplied shape must be well formed and cover the row; then every kernel access is
 // in bounds for any grid.
 int check_cfg(int pattern, int W, int64_t H, int dtype, const ar_launch_cfg_t* c) {
   if (!c) return AR_ERR_INVALID_ARG;
-  if (c->rank_at_a_time != 0 && c->rank_at_a_time != 1) return AR_ERR_INVALID_ARG;
+  const int rpb = c->ranks_per_batch;
+  if (rpb != 0 && rpb != 1 && rpb != 2 && rpb != 4) return AR_ERR_INVALID_ARG;
   const int t = c->threads_per_block;
   if (t < 64 || t > arf::kMaxThreads || t % 64 != 0) return AR_ERR_INVALID_ARG;
   const int u = c->vecs_per_thread;
@@ -266,13 +282,11 @@ int check_cfg(int pattern, int W, int64_t H, int dtype, const ar_launch_cfg_t* c
   if (c->grid < 1) return AR_ERR_INVALID_ARG;
   if (c->nt_store != 0 && c->nt_store != 1) return AR_ERR_INVALID_ARG;
   if (pattern == AR_PATTERN_ALLREDUCE) {
-    if (c->flat != 1 || u == 8 || c->rank_at_a_time) return AR_ERR_INVALID_ARG;
+    if (c->flat != 1 || u == 8 || rpb) return AR_ERR_INVALID_ARG;
     return AR_OK;
   }
-  // One rank per batch exists for the shapes the planner uses it on.
-  if (c->rank_at_a_time &&
-      (!c->nt_store || !((u == 2 && W >= 4 && W <= 16) || (u == 4 && W >= 2 && W <= 4))))
-    return AR_ERR_INVALID_ARG;
+  // Fixed rank batches exist for the shapes the planner uses them on.
+  if (rpb && (!c->nt_store || !arf::rank_batch_instantiated(W, u, rpb))) return AR_ERR_INVALID_ARG;
   if (c->flat != 0) return AR_ERR_INVALID_ARG;
   const int L = c->lanes_per_row;
   const bool seg_ok = (L >= 1 && L <= 64 && is_pow2(L)) || (L > 64 && L % 64 == 0);

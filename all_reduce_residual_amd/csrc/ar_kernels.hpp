@@ -508,6 +508,15 @@ __device__ inline void load_gamma(const f32x4* gamma, uint32_t vec, float (&g)[k
   }
 }
 
+// The fixed rank batches the norm kernel is instantiated with (stream source, non-temporal
+// stores): one rank for two vectors per thread at W = 4 ... 16 and for four at W = 2 and 4; two
+// ranks for two vectors at W >= 4 and for one at W >= 32; four ranks for two vectors at W = 8.
+constexpr bool rank_batch_instantiated(int W, int vpt, int n) {
+  return (n == 1 && ((vpt == 2 && W >= 4 && W <= 16) || (vpt == 4 && (W == 2 || W == 4)))) ||
+         (n == 2 && ((vpt == 2 && W >= 4) || (vpt == 1 && W >= 32))) ||
+         (n == 4 && vpt == 2 && W == 8);
+}
+
 // One row = V vectors of 16 bytes.  Thread t of a block serves row slot t / L (R slots per
 // block) and, within the row, vectors lane + k * L for k < VPT.  L * VPT >= V.  Blocks walk
 // groups of R rows with a grid stride.
@@ -516,13 +525,16 @@ __device__ inline void load_gamma(const f32x4* gamma, uint32_t vec, float (&g)[k
 // residual_out are unused): norm_out = RMSNorm(x) * gamma.  The second kernel of the two-kernel
 // path, and a stand-alone RMSNorm.
 //
-// kRankAtATime (rows whose chains are all held at once, below): one rank's vectors per batch
-// instead of up to 16 loads, so a block reads one tensor's row at a time.  The launch planner
-// takes it while every row of a call is resident at once (one to three rows per CU): all CUs
-// then run the same phase, and reading the W + 1 tensors one after another, rather than all
-// of them together, is what HBM serves faster there.  The arithmetic is the same.
+// kRankBatch (whole-row chains of one or two vectors per thread, or one rank's four vectors; 0
+// = the default batches of up to 16 loads across ranks): each thread loads kRankBatch ranks'
+// vectors per batch, so a block reads that many tensors' rows at a time.  The launch planner
+// takes one rank per batch while every row of a call is resident at once (one to three rows per
+// CU): all CUs then run the same phase, and reading the W + 1 tensors one after another, rather
+// than all of them together, is what HBM serves faster there.  With more rows per CU the blocks
+// drift apart; there batches of two ranks (four at W = 8 with 16-bit rows) are the fastest
+// middle ground.  The arithmetic is the same.
 template <class T, int W, int VPT, bool kNtStore, class Src = StreamSource, bool kNormOnly = false,
-          bool kRankAtATime = false>
+          int kRankBatch = 0>
 __global__ __launch_bounds__(kMaxThreads) void ar_norm_kernel(
     RankPtrs<W> in, const u32x4* residual, const f32x4* gamma, u32x4* residual_out,
     u32x4* norm_out, int64_t M, int V, int L, int R, float eps, float count_h, Src src) {
@@ -661,14 +673,14 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_kernel(
       // One rank's 4 vectors per batch are staged too, with the residual first: left alone,
       // the fp16 W = 4 form issued them a round trip apart.
       constexpr bool kStageChains =
-          ((W == 2 || W == 4) && VPT == 2) || (kRankAtATime && VPT >= 4);
+          ((W == 2 || W == 4) && VPT == 2) || (kRankBatch == 1 && VPT >= 4);
       u32x4 res_v[VPT];
       if constexpr (kStageChains) {
 #pragma unroll
         for (int k = 0; k < VPT; ++k) res_v[k] = load_stream(at(residual + base, boff[k]));
       }
       float acc[VPT][kVec];
-      constexpr int kLoads = kRankAtATime ? VPT : default_max_loads<T, VPT>();
+      constexpr int kLoads = kRankBatch > 0 ? kRankBatch * VPT : default_max_loads<T, VPT>();
       src.template sum<T, W, VPT, kLoads, kStageChains>(in, base, boff, ok, acc);
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {

@@ -98,10 +98,12 @@ typedef enum {
  *   flat              : 1 for the sum pattern (flat vector decomposition), 0 for the norm
  *   nt_store          : 1 = outputs are written with non-temporal stores, 0 = ordinary stores
  *                       (inputs are always read with non-temporal loads)
- *   rank_at_a_time    : norm pattern only: 1 = each thread loads one rank's vectors at a time
- *                       instead of up to 16 loads of several ranks (same results); allowed with
- *                       nt_store = 1 and 2 vectors per thread for 4 <= W <= 16, or 4 for W = 2
- *                       and 4; 0 otherwise and for the sum pattern */
+ *   ranks_per_batch   : norm pattern only: 0 = each thread issues up to 16 loads across ranks
+ *                       per batch; 1, 2 or 4 = it loads that many ranks' vectors per batch
+ *                       (same results).  Allowed with nt_store = 1 for: 1 with 2 vectors per
+ *                       thread at 4 <= W <= 16 or 4 vectors at W = 2 and 4; 2 with 2 vectors
+ *                       at W >= 4 or 1 vector at W >= 32; 4 with 2 vectors at W = 8.  0 for the
+ *                       sum pattern */
 typedef struct {
   int32_t threads_per_block;
   int32_t vecs_per_thread;
@@ -110,7 +112,7 @@ typedef struct {
   int32_t grid;
   int32_t flat;
   int32_t nt_store;
-  int32_t rank_at_a_time;
+  int32_t ranks_per_batch;
 } ar_launch_cfg_t;
 
 /* kAllReduce.  out[m, i] = RN_T(x_0[m, i] + ... + x_{W-1}[m, i]).

@@ -99,14 +99,15 @@ def test_launch_config_invariants(cu):
             assert 64 <= t <= 1024 and t % 64 == 0, c
             assert c["nt_store"] in (0, 1)
             assert c["grid"] >= 1
-            assert c["rank_at_a_time"] in (0, 1)
-            if c["rank_at_a_time"]:
-                # Only where it is built: 2 vectors per thread up to W = 16, 4 up to W = 4, one
-                # row per block, non-temporal stores, one to three rows per CU.
+            n = c["ranks_per_batch"]
+            assert n in (0, 1, 2, 4)
+            if n:
+                # Only where it is built, one row per block, non-temporal stores: one rank per
+                # batch at one to three rows per CU, two or four from there on.
                 vpt = c["vecs_per_thread"]
                 assert pat == RMS and c["nt_store"] == 1 and c["rows_per_block"] == 1, c
-                assert (vpt == 2 and 4 <= W <= 16) or (vpt == 4 and 2 <= W <= 4), c
-                assert cu < M <= 3 * cu, c
+                assert _rank_batch_built(W, vpt, n), c
+                assert (cu < M <= 3 * cu) if n == 1 else M > 3 * cu, c
             if pat == SUM:
                 assert c["flat"] == 1 and c["vecs_per_thread"] in (1, 2, 4)
                 nvec = M * H // _vec(dt)
@@ -133,20 +134,37 @@ def test_launch_config_headline_shapes():
         assert c["lanes_per_row"] * c["vecs_per_thread"] >= 896
 
 
-def test_launch_config_rank_at_a_time_band():
-    """One rank per batch exactly while every row is resident with one to three rows per CU."""
-    def rat(W, M, H, dt, cu=256):
-        return ar.ar_launch_config(RMS, W, M, H, dt, cu_count=cu)["rank_at_a_time"]
-    for M, want in ((1, 0), (128, 0), (256, 0), (257, 1), (512, 1), (768, 1), (769, 0),
-                    (1024, 0), (2048, 0)):
-        assert rat(8, M, 7168, BF16) == want, M
-    assert rat(16, 512, 8192, FP16) == 1          # the fp16 W = 16 workload (2 rows per CU)
-    assert rat(4, 512, 7168, BF16) == 1 and rat(2, 512, 7168, BF16) == 1   # W = 2: 4 vectors
-    assert rat(2, 512, 4096, BF16) == 0           # W = 2 with 2 vectors: staged chains already
-    assert rat(32, 512, 7168, BF16) == 0 and rat(1, 512, 7168, BF16) == 0
-    assert rat(8, 160, 7168, BF16, cu=80) == 1 and rat(8, 80, 7168, BF16, cu=80) == 0
+def _rank_batch_built(W, vpt, n):
+    """The fixed rank batches the library is built with."""
+    return ((n == 1 and ((vpt == 2 and 4 <= W <= 16) or (vpt == 4 and W in (2, 4)))) or
+            (n == 2 and ((vpt == 2 and W >= 4) or (vpt == 1 and W >= 32))) or
+            (n == 4 and vpt == 2 and W == 8))
+
+
+def test_launch_config_rank_batch_bands():
+    """Whole rows load one rank per batch while every row is resident with one to three rows per
+    CU, then two ranks (four at W = 8 with 16-bit rows); never below one row per CU."""
+    def rpb(W, M, H, dt, cu=256):
+        return ar.ar_launch_config(RMS, W, M, H, dt, cu_count=cu)["ranks_per_batch"]
+    for M, want in ((1, 0), (128, 0), (256, 0), (257, 1), (512, 1), (768, 1), (769, 4),
+                    (1024, 4), (2048, 4), (8192, 4)):
+        assert rpb(8, M, 7168, BF16) == want, M
+    assert rpb(8, 2048, 8192, FP16) == 4
+    assert rpb(16, 512, 8192, FP16) == 1 and rpb(16, 2048, 8192, FP16) == 2
+    assert rpb(4, 512, 7168, BF16) == 1 and rpb(4, 2048, 7168, BF16) == 2
+    assert rpb(8, 2048, 4096, FP32) == 2          # binary32 rows at W = 8: two ranks
+    assert rpb(2, 512, 7168, BF16) == 1           # W = 2: 4 vectors
+    assert rpb(2, 512, 4096, BF16) == 0           # W = 2 with 2 vectors: staged chains already
+    assert rpb(2, 2048, 7168, BF16) == 0          # W = 2 keeps 8 vectors there
+    assert rpb(32, 512, 7168, BF16) == 0 and rpb(1, 512, 7168, BF16) == 0
+    assert rpb(32, 1024, 7168, BF16) == 2         # two vectors per thread
+    assert rpb(32, 2048, 7168, BF16) == 2 and rpb(64, 4096, 7168, BF16) == 2   # one vector
+    assert rpb(8, 2048, 4096, BF16) == 0          # one vector at W = 8: default batches
+    assert rpb(64, 1024, 2048, FP32) == 0 and rpb(32, 2048, 2048, FP32) == 2   # binary32, 1 vector
+    assert rpb(8, 160, 7168, BF16, cu=80) == 1 and rpb(8, 80, 7168, BF16, cu=80) == 0
+    assert rpb(8, 241, 7168, BF16, cu=80) == 4
     for M in (1, 512, 2048):                      # never for the sum
-        assert ar.ar_launch_config(SUM, 8, M, 7168, BF16, cu_count=256)["rank_at_a_time"] == 0
+        assert ar.ar_launch_config(SUM, 8, M, 7168, BF16, cu_count=256)["ranks_per_batch"] == 0
 
 
 def test_launch_config_sum_resident_round():
@@ -304,23 +322,32 @@ def test_validation_rejects_before_device_access(L):
                                 ctypes.byref(bad)) == ar.AR_ERR_INVALID_ARG
     assert L.ar_sum_with_config(_ptrs(p[:2]), 2, 4, 256, BF16, out, None,
                                 None) == ar.AR_ERR_INVALID_ARG
-    # One rank per batch: never for the sum, and for the norm only where it is built.
+    # Fixed rank batches: never for the sum, and for the norm only where they are built.
     sum_rat = ar.LaunchConfig(threads_per_block=64, vecs_per_thread=1, lanes_per_row=0,
-                              rows_per_block=0, grid=1, flat=1, nt_store=1, rank_at_a_time=1)
+                              rows_per_block=0, grid=1, flat=1, nt_store=1, ranks_per_batch=1)
     assert L.ar_sum_with_config(_ptrs(p[:2]), 2, 4, 256, BF16, out, None,
                                 ctypes.byref(sum_rat)) == ar.AR_ERR_INVALID_ARG
     nargs = (_ptrs(p[:2]), 2, 4, 256, BF16, 0xA00000, 0xB00000, 1e-6, 0xC00000, 0xD00000, None)
-    for vpt, lanes, nt, rat in ((8, 64, 1, 1), (2, 64, 0, 1), (2, 64, 1, 2), (1, 64, 1, 1),
-                                (2, 64, 1, 1)):      # the last: W = 2 with 2 vectors
+    for vpt, lanes, nt, n in ((8, 64, 1, 1), (2, 64, 0, 1), (2, 64, 1, 3), (1, 64, 1, 1),
+                              (2, 64, 1, 1), (2, 64, 1, 2), (2, 64, 1, 4), (4, 64, 1, 2),
+                              (2, 64, 1, -1), (2, 64, 1, 8)):   # W = 2: 2 vectors take none
         cfg = ar.LaunchConfig(threads_per_block=64, vecs_per_thread=vpt, lanes_per_row=lanes,
-                              rows_per_block=1, grid=4, flat=0, nt_store=nt, rank_at_a_time=rat)
+                              rows_per_block=1, grid=4, flat=0, nt_store=nt, ranks_per_batch=n)
         assert L.ar_residual_rmsnorm_with_config(*nargs, ctypes.byref(cfg)) == \
-            ar.AR_ERR_INVALID_ARG, (vpt, nt, rat)
+            ar.AR_ERR_INVALID_ARG, (vpt, nt, n)
     many = (_ptrs(p[:16] * 2), 32, 4, 256, BF16, 0xA00000, 0xB00000, 1e-6, 0xC00000, 0xD00000,
             None)
-    cfg = ar.LaunchConfig(threads_per_block=64, vecs_per_thread=2, lanes_per_row=64,
-                          rows_per_block=1, grid=4, flat=0, nt_store=1, rank_at_a_time=1)
-    assert L.ar_residual_rmsnorm_with_config(*many, ctypes.byref(cfg)) == ar.AR_ERR_INVALID_ARG
+    for vpt, nt, n in ((2, 1, 1), (2, 1, 4), (1, 1, 4), (4, 1, 2), (2, 0, 2), (1, 0, 2)):
+        cfg = ar.LaunchConfig(threads_per_block=64, vecs_per_thread=vpt, lanes_per_row=64,
+                              rows_per_block=1, grid=4, flat=0, nt_store=nt, ranks_per_batch=n)
+        assert L.ar_residual_rmsnorm_with_config(*many, ctypes.byref(cfg)) == \
+            ar.AR_ERR_INVALID_ARG, (vpt, nt, n)
+    eight = (_ptrs(p[:8]), 8, 4, 256, BF16, 0xA00000, 0xB00000, 1e-6, 0xC00000, 0xD00000, None)
+    for vpt, n in ((1, 2), (1, 4), (4, 4), (4, 2)):
+        cfg = ar.LaunchConfig(threads_per_block=64, vecs_per_thread=vpt, lanes_per_row=64,
+                              rows_per_block=1, grid=4, flat=0, nt_store=1, ranks_per_batch=n)
+        assert L.ar_residual_rmsnorm_with_config(*eight, ctypes.byref(cfg)) == \
+            ar.AR_ERR_INVALID_ARG, (vpt, n)
 
 
 def test_zero_rows_returns_ok_without_device(L):

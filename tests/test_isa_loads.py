@@ -10,7 +10,8 @@ chain per batch: W <= 8, and W = 16 with one vector) for the three element types
 that no full wait (`s_waitcnt vmcnt(0)`) falls between two of a kernel's streaming loads; for
 the wide-row shapes (4 or 8 vectors per thread, W >= 8) it allows waits between rank batches
 but at most one per 4 loads, and the same bound holds for the split (workspace) kernel at
-every W. For
+every W. The fixed rank batches (one, two or four ranks per batch) may wait between batches, at
+most once per batch. For
 the sum kernel it compiles every (W, vectors per thread) and checks its loop-free path (kernel
 entry to the first store): whole rank batches only, with exactly one full wait between
 consecutive batches and none inside one (16 loads per batch, 8 once a thread holds 32 or more
@@ -31,9 +32,10 @@ SHAPES = [(w, v) for w in (1, 2, 4, 8) for v in (1, 2)] + [(16, 1)]
 # Wide rows (many vectors per thread, one or a few chains per batch): waits between rank batches
 # are by design, but never one per load.
 WIDE = [(8, 8), (16, 8), (32, 8), (64, 8), (16, 4), (64, 4)]
-# One rank per batch (the planner's shapes for one to three rows per CU): a wait between rank
-# batches is the point, a wait inside one is not.
-RANK = [(w, 2) for w in (4, 8, 16)] + [(w, 4) for w in (2, 4)]
+# Fixed rank batches (W, vectors per thread, ranks per batch; the planner's shapes from one row
+# per CU on): a wait between rank batches is the point, a wait inside one is not.
+RANK = ([(w, 2, 1) for w in (4, 8, 16)] + [(w, 4, 1) for w in (2, 4)] +
+        [(w, 2, 2) for w in (4, 8, 16, 32, 64)] + [(w, 1, 2) for w in (32, 64)] + [(8, 2, 4)])
 TYPES = ("Bf16", "F16", "F32")
 TN = {"Bf16": "4Bf16", "F16": "3F16", "F32": "3F32"}
 
@@ -49,9 +51,9 @@ def _source() -> str:
         for w, v in SHAPES + WIDE:
             refs.append("reinterpret_cast<const void*>(&arf::ar_norm_kernel<arf::%s, %d, %d, true>)"
                         % (t, w, v))
-        for w, v in RANK:
+        for w, v, n in RANK:
             refs.append("reinterpret_cast<const void*>(&arf::ar_norm_kernel<arf::%s, %d, %d, true, "
-                        "arf::StreamSource, false, true>)" % (t, w, v))
+                        "arf::StreamSource, false, %d>)" % (t, w, v, n))
         for w in SUM_W:
             for v in (1, 2):
                 refs.append("reinterpret_cast<const void*>(&arf::ar_norm_split_kernel<arf::%s, %d, "
@@ -102,9 +104,9 @@ def _sum_symbol(t: str, w: int, u: int) -> str:
     return "_ZN3arf13ar_sum_kernelINS_%sELi%dELi%dELb1ENS_12StreamSourceEEE" % (tn, w, u)
 
 
-def _norm_symbol(t: str, w: int, v: int, rank_at_a_time: bool = False) -> str:
-    return ("_ZN3arf14ar_norm_kernelINS_%sELi%dELi%dELb1ENS_12StreamSourceELb0ELb%dE"
-            % (TN[t], w, v, int(rank_at_a_time)))
+def _norm_symbol(t: str, w: int, v: int, ranks_per_batch: int = 0) -> str:
+    return ("_ZN3arf14ar_norm_kernelINS_%sELi%dELi%dELb1ENS_12StreamSourceELb0ELi%dE"
+            % (TN[t], w, v, ranks_per_batch))
 
 
 def _norm_streaming_loads(asm: str, kernel: str = "ar_norm_kernel", stop: str = "") -> dict:
@@ -216,20 +218,21 @@ def test_wide_rows_loads_not_serialized(norm_asm):
     assert not bad, "(type, W, vectors per thread, loads, full waits): %s" % bad
 
 
-def test_rank_at_a_time_waits_only_between_ranks(norm_asm):
-    """One rank per batch: every one of the (W + 1) x VPT streaming loads is issued, and full
-    waits fall only between rank batches (at most W of them), never between the VPT loads of one
-    rank's batch."""
+def test_rank_batches_wait_only_between_batches(norm_asm):
+    """Fixed rank batches: every streaming load of the unrolled chains is issued (the W + 1
+    tensors' VPT vectors; the loop body of the 16-rank walk for W >= 32), and full waits number
+    at most the rank batches (min(W, 16) / ranks per batch), never one per load of a batch."""
     waits = _waits_between_streaming_loads(norm_asm)
     loads = _norm_streaming_loads(norm_asm)
     bad = []
     for t in TYPES:
-        for w, v in RANK:
-            sym = [k for k in waits if k.startswith(_norm_symbol(t, w, v, True))]
-            assert len(sym) == 1, (t, w, v, sym)
-            if loads[sym[0]] < (w + 1) * v or waits[sym[0]] > w:
-                bad.append((t, w, v, loads[sym[0]], waits[sym[0]]))
-    assert not bad, "(type, W, vectors per thread, loads, full waits): %s" % bad
+        for w, v, n in RANK:
+            sym = [k for k in waits if k.startswith(_norm_symbol(t, w, v, n))]
+            assert len(sym) == 1, (t, w, v, n, sym)
+            ranks = min(w, 16)
+            if loads[sym[0]] < (ranks + 1) * v or waits[sym[0]] > ranks // n:
+                bad.append((t, w, v, n, loads[sym[0]], waits[sym[0]]))
+    assert not bad, "(type, W, vectors per thread, ranks per batch, loads, full waits): %s" % bad
 
 
 def test_checker_sees_a_serialized_load():

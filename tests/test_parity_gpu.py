@@ -148,18 +148,29 @@ def test_norm_launch_shapes_agree(oracle_mod, H):
         run_rms_both(oracle_mod, parts, res, gam, 1e-6, dtype, config=cfg, oracle_out=want)
 
 
-RANK_CASES = [(W, H, dtype, vpt) for W in (2, 4, 8, 16) for dtype in ("bf16", "fp16", "fp32")
-              for H, vpt in ((1000 if dtype == "fp32" else 2000, 2), (2040, 4))
-              if (vpt == 2 and W >= 4) or (vpt == 4 and W <= 4)]
+def _rank_batch_built(W, vpt, n):
+    """The fixed rank batches the library is built with (the launch checks allow these only)."""
+    return ((n == 1 and ((vpt == 2 and 4 <= W <= 16) or (vpt == 4 and W in (2, 4)))) or
+            (n == 2 and ((vpt == 2 and W >= 4) or (vpt == 1 and W >= 32))) or
+            (n == 4 and vpt == 2 and W == 8))
 
 
-@pytest.mark.parametrize("W,H,dtype,vpt", RANK_CASES,
-                         ids=["W%d-H%d-%s-v%d" % c for c in RANK_CASES])
-def test_rank_at_a_time_shapes_agree(oracle_mod, W, H, dtype, vpt):
-    """One rank per batch (the planner's form for one to three rows per CU) gives the oracle's
-    result: one and two rows per block, a ragged row (lanes past its last vector), grid stride."""
+# Ragged rows: 250 vectors (H = 2000 at 16 bits, 1000 in binary32) over 128 lanes x 2 or 256 x 1,
+# and 255 / 510 vectors (H = 2040) over 64 / 128 lanes x 4.
+RANK_CASES = [(W, H if dtype != "fp32" or vpt == 4 else H // 2, dtype, vpt, n)
+              for W in (2, 4, 8, 16, 32, 64) for dtype in ("bf16", "fp16", "fp32")
+              for H, vpt in ((2000, 1), (2000, 2), (2040, 4)) for n in (1, 2, 4)
+              if _rank_batch_built(W, vpt, n)]
+
+
+@pytest.mark.parametrize("W,H,dtype,vpt,n", RANK_CASES,
+                         ids=["W%d-H%d-%s-v%d-r%d" % c for c in RANK_CASES])
+def test_rank_batch_shapes_agree(oracle_mod, W, H, dtype, vpt, n):
+    """Fixed rank batches (one rank per batch at one to three rows per CU, two or four beyond)
+    give the oracle's result: one and two rows per block, a ragged row (lanes past its last
+    vector), grid stride."""
     M = 13
-    parts, res, gam = synth.custom(W, M, H, dtype, seed=W * 7 + H + vpt)
+    parts, res, gam = synth.custom(W, M, H, dtype, seed=W * 7 + H + vpt + 1000 * n)
     want = oracle_mod.ar_residual_rmsnorm([host_np(p) for p in parts], host_np(res),
                                           gam.numpy(), 1e-6, dtype)
     V = H * (4 if dtype == "fp32" else 2) // 16
@@ -168,19 +179,20 @@ def test_rank_at_a_time_shapes_agree(oracle_mod, W, H, dtype, vpt):
         if lanes * rows > 1024:
             continue
         cfg = dict(threads_per_block=lanes * rows, vecs_per_thread=vpt, lanes_per_row=lanes,
-                   rows_per_block=rows, grid=grid, flat=0, nt_store=1, rank_at_a_time=1)
-        print("case rank-at-a-time", W, H, dtype, cfg, flush=True)
+                   rows_per_block=rows, grid=grid, flat=0, nt_store=1, ranks_per_batch=n)
+        print("case rank batch", W, H, dtype, cfg, flush=True)
         run_rms_both(oracle_mod, parts, res, gam, 1e-6, dtype, config=cfg, oracle_out=want)
 
 
-def test_planned_rank_at_a_time_workloads(oracle_mod):
-    """The planned shape at one to three rows per CU is the rank-at-a-time form: the wide-hidden
-    call at M = 512 and 768 against the oracle on every row."""
+def test_planned_rank_batch_workloads(oracle_mod):
+    """The planned shapes around the band edges: one rank per batch at two and three rows per CU,
+    four ranks just past three rows per CU (the wide-hidden call, W = 8 H = 7168 bf16), against
+    the oracle on every row."""
     cu = ar.ar_device_cu_count()
-    for M in (2 * cu, 3 * cu):
+    for M, n in ((2 * cu, 1), (3 * cu, 1), (3 * cu + 1, 4)):
         assert ar.ar_launch_config(ar.PATTERN_AR_RESIDUAL_RMSNORM, 8, M, 7168,
-                                   ar.DTYPE_BF16)["rank_at_a_time"] == 1
-        print("case planned rank-at-a-time M=%d" % M, flush=True)
+                                   ar.DTYPE_BF16)["ranks_per_batch"] == n
+        print("case planned rank batch M=%d n=%d" % (M, n), flush=True)
         parts, res, gam = synth.inputs(synth.WORKLOADS["wide_hidden"], M)
         run_rms_both(oracle_mod, parts, res, gam, 1e-6, "bf16")
 
