@@ -392,6 +392,43 @@ def test_many_ranks_many_rows_sampled(oracle_mod, W, M, H, dtype):
     assert_norm_close(host_np(no[rows].cpu()), want_no, dtype)
 
 
+# ---- planned rank batches at prefill sizes (more than three rows per CU) ------------------------
+
+PREFILL_BATCHES = [(4, 2048, 7168, "bf16", 2, 2), (8, 2048, 8192, "fp16", 2, 4),
+                   (8, 2048, 4096, "fp32", 2, 2), (16, 2048, 7168, "bf16", 2, 2),
+                   (32, 1024, 7168, "bf16", 2, 2), (64, 2048, 2048, "fp32", 1, 2)]
+
+
+@pytest.mark.parametrize("W,M,H,dtype,vpt,n", PREFILL_BATCHES,
+                         ids=["W%d-M%d-H%d-%s" % c[:4] for c in PREFILL_BATCHES])
+def test_planned_rank_batches_sampled(oracle_mod, W, M, H, dtype, vpt, n):
+    """The planned shapes that load two or four ranks per batch beyond three rows per CU: sampled
+    rows of both outputs against the oracle run on those rows (inputs drawn on the GPU by
+    torch's seeded generator)."""
+    tdt = TD[dtype]
+    cu = ar.ar_device_cu_count()
+    cfg = ar.ar_launch_config(ar.PATTERN_AR_RESIDUAL_RMSNORM, W, M, H, ar.dtype_code(tdt))
+    print("case", W, M, H, dtype, cfg, flush=True)
+    if M <= 3 * cu or (vpt == 1 and M < 8 * cu):
+        pytest.skip("rows per CU on this device fall outside the band")
+    assert cfg["vecs_per_thread"] == vpt and cfg["ranks_per_batch"] == n, cfg
+    g = torch.Generator(device="cuda")
+    g.manual_seed(W * 7 + M)
+    parts = [torch.empty((M, H), dtype=tdt, device="cuda").normal_(0.0, 0.05, generator=g)
+             for _ in range(W)]
+    res = torch.empty((M, H), dtype=tdt, device="cuda").normal_(0.0, 1.0, generator=g)
+    gam = torch.empty(H, dtype=torch.float32, device="cuda").uniform_(0.5, 1.5, generator=g)
+    ro, no = torch.empty_like(res), torch.empty_like(res)
+    ar.ar_residual_rmsnorm(parts, res, gam, 1e-6, ro, no)
+    torch.cuda.synchronize()
+    rows = torch.tensor(sorted({0, 1, 255, 256, 767, 768, M // 2, M - 2, M - 1}), device="cuda")
+    want_ro, want_no = oracle_mod.ar_residual_rmsnorm(
+        [host_np(p[rows].cpu()) for p in parts], host_np(res[rows].cpu()),
+        gam.cpu().numpy(), 1e-6, dtype)
+    assert_bit_exact(host_np(ro[rows].cpu()), want_ro, dtype, "residual_out")
+    assert_norm_close(host_np(no[rows].cpu()), want_no, dtype)
+
+
 # ---- seeded random shapes through every entry point, in the launch shapes the library picks -----
 
 def _random_cases(n=36, seed=20261202):
