@@ -160,7 +160,16 @@ hipError_t launch_lamport_sum_w(void* rbuf, int64_t slot_vecs, void* out, int64_
   RankPtrs<W> p = slot_ptrs<W>(rbuf, slot_vecs);
   u32x4* o = static_cast<u32x4*>(out);
   int tail = 0;
+  // Polled batches of two ranks (ranks_per_batch = 2): built for W = 4 ... 16.
+  arf::LamportSourceT<2> src2{src.status, src.spin_limit};
   void* args[] = {&p, &o, &nvec, &tail, &src};
+  void* args2[] = {&p, &o, &nvec, &tail, &src2};
+  if constexpr (W >= 4 && W <= 16) {
+    if (c.ranks_per_batch == 2)
+      return hipLaunchKernel(
+          reinterpret_cast<const void*>(&arf::ar_sum_kernel<T, W, 1, true, arf::LamportSourceT<2>>),
+          dim3(c.grid), dim3(c.threads_per_block), args2, 0, s);
+  }
   const void* fn =
       reinterpret_cast<const void*>(&arf::ar_sum_kernel<T, W, 1, true, arf::LamportSource>);
   return hipLaunchKernel(fn, dim3(c.grid), dim3(c.threads_per_block), args, 0, s);
@@ -180,7 +189,25 @@ hipError_t launch_lamport_norm_v(void* rbuf, int64_t slot_vecs, const void* resi
   int L = c.lanes_per_row;
   int R = c.rows_per_block;
   float count_h = static_cast<float>(H);
+  // Polled batches of two ranks at 2 vectors per thread, one at 4 (ranks_per_batch): built for
+  // W = 4 ... 16.
+  arf::LamportSourceT<1> src1{src.status, src.spin_limit};
+  arf::LamportSourceT<2> src2{src.status, src.spin_limit};
   void* args[] = {&p, &res, &gam, &ro, &no, &M, &V, &L, &R, &eps, &count_h, &src};
+  void* args1[] = {&p, &res, &gam, &ro, &no, &M, &V, &L, &R, &eps, &count_h, &src1};
+  void* args2[] = {&p, &res, &gam, &ro, &no, &M, &V, &L, &R, &eps, &count_h, &src2};
+  if constexpr (W >= 4 && W <= 16 && VPT == 2) {
+    if (c.ranks_per_batch == 2)
+      return hipLaunchKernel(reinterpret_cast<const void*>(
+                                 &arf::ar_norm_kernel<T, W, VPT, true, arf::LamportSourceT<2>>),
+                             dim3(c.grid), dim3(c.threads_per_block), args2, 0, s);
+  }
+  if constexpr (W >= 4 && W <= 16 && VPT == 4) {
+    if (c.ranks_per_batch == 1)
+      return hipLaunchKernel(reinterpret_cast<const void*>(
+                                 &arf::ar_norm_kernel<T, W, VPT, true, arf::LamportSourceT<1>>),
+                             dim3(c.grid), dim3(c.threads_per_block), args1, 0, s);
+  }
   const void* fn = reinterpret_cast<const void*>(
       &arf::ar_norm_kernel<T, W, VPT, true, arf::LamportSource>);
   return hipLaunchKernel(fn, dim3(c.grid), dim3(c.threads_per_block), args, 0, s);

@@ -952,8 +952,15 @@ int run_lamport_sum(void* rbuf, int W, int64_t M, int64_t H, int dtype, int64_t 
   ar_launch_cfg_t cfg;
   plan_sum(W, M * H, dtype, cu, &cfg, 0);
   cfg.vecs_per_thread = 1;  // the Lamport consumer is instantiated for one vector per thread
-  cfg.grid = cap_grid(ceil_div(M * H / (kVecBytes / elem_size(dtype)), cfg.threads_per_block));
+  const int64_t nvec = M * H / (kVecBytes / elem_size(dtype));
+  cfg.grid = cap_grid(ceil_div(nvec, cfg.threads_per_block));
   cfg.nt_store = 1;
+  // Polled batches of two ranks instead of eight from 1024 vectors per CU on (W = 4 ... 16).
+  // Consumer alone over rotated receive buffers, H = 7168, three interleaved rounds: W = 8 bf16
+  // M = 512 / 1024 / 2048 8.8 / 4.9 / 1.5 % faster (M = 4096 even); W = 4 2-3.5 %, W = 16
+  // 1.2-10 % (bf16 and binary32, M = 512 and 2048).  With fewer vectors per CU it ranged from
+  // 9 % faster to 18 % slower (W = 16 bf16 M = 128).
+  cfg.ranks_per_batch = (W >= 4 && W <= 16 && nvec >= int64_t(cu) * 1024) ? 2 : 0;
   arf::LamportSource src{status, spin_limit ? spin_limit : kDefaultSpinLimit};
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
@@ -1022,6 +1029,16 @@ int run_lamport_norm(void* rbuf, int W, int64_t M, int64_t H, int dtype, int64_t
     }
   }
   cfg.nt_store = 1;
+  // Polled batches of a quarter of the stream source's loads instead of half beyond one row per
+  // CU (W = 4 ... 16; two ranks at 2 vectors per thread, one at 4).  Consumer alone over rotated
+  // receive buffers, H = 7168, three interleaved rounds: W = 8 bf16 M = 512 / 1024 / 2048 / 4096
+  // 3.7 / 2.5 / 3.7 / 1.8 % faster; W = 4 and 16, bf16 and binary32, M = 512 and 2048: 1-5.5 %.
+  // At M = 128 it was even to 10 % slower.
+  cfg.ranks_per_batch = 0;
+  if (M > cu && cfg.rows_per_block == 1 && W >= 4 && W <= 16) {
+    if (cfg.vecs_per_thread == 2) cfg.ranks_per_batch = 2;
+    if (cfg.vecs_per_thread == 4) cfg.ranks_per_batch = 1;
+  }
   arf::LamportSource src{status, spin_limit ? spin_limit : kDefaultSpinLimit};
   void* buf = static_cast<char*>(rbuf) + lamport_slot(lamport_buffer(round), W, 0, bytes);
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -1395,7 +1395,10 @@ __device__ inline void store_coherent(u32x4* base, uint32_t boff, u32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, coherent_rsrc(base), boff, 0, kCoherentNt);
 }
 
-struct LamportSource {
+// kRanks: ranks per polled batch (0: half the stream source's batch of loads).  Beyond one row
+// (or 1024 vectors) per CU smaller polled batches run faster; the launch planner picks them.
+template <int kRanks = 0>
+struct LamportSourceT {
   int* status;          // bit 0 set on a poll timeout
   uint32_t spin_limit;  // polls per vector before giving up
 
@@ -1426,8 +1429,9 @@ struct LamportSource {
   template <class T, int W, int N, int kMaxLoads = default_max_loads<T, N>(), bool kStage = false>
   __device__ inline void sum(const RankPtrs<W>& in, int64_t base, const uint32_t (&boff)[N],
                              const bool (&ok)[N], float (&acc)[N][T::kVec]) const {
-    // Polled vectors stay live until accumulated: half the stream source's batch.
-    constexpr int kBatch = rank_batch<W, N, (kMaxLoads / 2 > 0 ? kMaxLoads / 2 : 1)>();
+    // Polled vectors stay live until accumulated: half the stream source's batch by default.
+    constexpr int kBatch = kRanks > 0 ? (kRanks < W ? kRanks : W)
+                                      : rank_batch<W, N, (kMaxLoads / 2 > 0 ? kMaxLoads / 2 : 1)>();
     bool gave_up = false;
 #pragma unroll
     for (int k = 0; k < N; ++k) {
@@ -1466,6 +1470,7 @@ struct LamportSource {
   template <class T>
   __device__ inline float tail_extra(float a, int64_t) const { return a; }
 };
+using LamportSource = LamportSourceT<0>;
 
 // Producer: next[i] = empty, then slot[i] = canonicalize(src[i]), for nvec 16-byte vectors,
 // device-coherent stores.  The thread waits for its emptying store to complete before it stores

@@ -87,6 +87,40 @@ def test_sequential_round(oracle_mod, dtype, W):
     assert_norm_close(host_np(no.cpu()), want_no, dtype, "lamport norm_out")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("W", [4, 8, 16])
+def test_smaller_polled_batches_beyond_one_row_per_cu(oracle_mod, dtype, W):
+    """Two CUs' worth of rows and three more (H = 7168): both consumers poll smaller batches
+    there (the sum two ranks at a time; the fused consumer two ranks with 2 vectors per thread,
+    bf16, and one with 4, binary32).  Every row against the oracle."""
+    M, H = 2 * ar.ar_device_cu_count() + 3, 7168
+    print("case", W, M, H, dtype, flush=True)
+    parts, res, gam = synth.custom(W, M, H, dtype, seed=W * 5 + M)
+    tdt = synth.TORCH_DTYPES[dtype]
+    d_parts = [dev(p) for p in parts]
+    hp = [host_np(p) for p in parts]
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    rbuf = _new_rbuf(W, M, H, tdt)
+    for r, p in enumerate(d_parts):
+        ar.ar_lamport_push(p, r, rbuf, 0)
+    out = torch.empty_like(d_parts[0])
+    ar.ar_lamport_sum(rbuf, 0, out, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert_bit_exact(host_np(out.cpu()), oracle_mod.ar_sum(hp, dtype), dtype, "lamport out")
+    for r, p in enumerate(d_parts):
+        ar.ar_lamport_push(p, r, rbuf, 1)
+    d_res, d_gam = dev(res), dev(gam)
+    ro, no = torch.empty_like(d_res), torch.empty_like(d_res)
+    ar.ar_lamport_residual_rmsnorm(rbuf, 1, d_res, d_gam, 1e-6, ro, no, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    check_round_state(rbuf, 1, d_parts)
+    want_ro, want_no = oracle_mod.ar_residual_rmsnorm(hp, host_np(res), gam.numpy(), 1e-6, dtype)
+    assert_bit_exact(host_np(ro.cpu()), want_ro, dtype, "lamport residual_out")
+    assert_norm_close(host_np(no.cpu()), want_no, dtype, "lamport norm_out")
+
+
 def test_rounds_rotate_through_three_buffers(oracle_mod):
     """Seven rounds (the rotation wraps twice) without re-arming: each push empties the next
     round's slots, so every round finds its buffer empty."""
