@@ -19,7 +19,9 @@ __device__ inline void stamp(int phase, V value, const void* tensor) {
   asm volatile("" ::"v"(value));
   if (threadIdx.x == 0) {
     const uint64_t set = (reinterpret_cast<uintptr_t>(tensor) - g_base) >> g_set_shift;
-    g_stamps[(set * gridDim.x + blockIdx.x) * 8 + phase] = __builtin_amdgcn_s_memrealtime();
+    const uint64_t blocks = uint64_t(gridDim.x) * gridDim.y;
+    const uint64_t b = uint64_t(blockIdx.y) * gridDim.x + blockIdx.x;
+    g_stamps[(set * blocks + b) * 8 + phase] = __builtin_amdgcn_s_memrealtime();
   }
 }
 }  // namespace arfp
@@ -118,9 +120,11 @@ int run(const Shape& c, double* out) {
       } else {
         int S = c.segments;
         uint32_t polls = 1u << 14;
-        void* a[] = {&in, &res, &gm, &ro, &no, &Vv, &S, &eps, &ch, &ws, &polls};
-        e = hipLaunchKernel((const void*)&ar_norm_split_kernel<Bf16, W, 1, true>, dim3(c.grid),
-                            dim3(c.threads), a, 0, s);
+        int rows = c.M;
+        void* a[] = {&in, &res, &gm, &ro, &no, &Vv, &S, &eps, &ch, &ws, &polls, &rows};
+        const SplitDims g = split_dims(c.M, S);
+        e = hipLaunchKernel((const void*)&ar_norm_split_kernel<Bf16, W, 1, true>,
+                            dim3(unsigned(g.x), unsigned(g.y)), dim3(c.threads), a, 0, s);
       }
       if (e != hipSuccess) {
         hipGraph_t dead = nullptr;
@@ -208,7 +212,8 @@ extern "C" int ar_probe_phases(int kind, int W, int M, int H, int threads, int v
   // Every launch must cover exactly its set's vectors (no access outside the buffers).
   if (kind == 0 && int64_t(grid) * threads * vpt != int64_t(M) * V) return 1;
   if (kind == 1 && (grid != M || int64_t(threads) * vpt < V)) return 1;
-  if (kind == 2 && (segments < 1 || segments > kSplitSlots || grid != M * segments || vpt != 1 ||
+  if (kind == 2 && (segments < 1 || segments > kSplitSlots ||
+                    grid != split_dims(M, segments).x * split_dims(M, segments).y || vpt != 1 ||
                     int64_t(segments) * threads < V))
     return 1;
   if (kind == 3 && grid != 1) return 1;

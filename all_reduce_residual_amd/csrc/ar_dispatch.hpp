@@ -398,9 +398,12 @@ hipError_t launch_norm_split_v(const void* const* inputs, const void* residual,
   float count_h = static_cast<float>(H);  // exact: H <= 2^16
   uint64_t* slots = static_cast<uint64_t*>(workspace);
   uint32_t polls = c.max_polls;
-  void* args[] = {&p, &res, &gam, &ro, &no, &V, &S, &eps, &count_h, &slots, &polls};
+  int rows = static_cast<int>(M);
+  void* args[] = {&p, &res, &gam, &ro, &no, &V, &S, &eps, &count_h, &slots, &polls, &rows};
   const void* fn = reinterpret_cast<const void*>(&arf::ar_norm_split_kernel<T, W, VPT, true>);
-  return hipLaunchKernel(fn, dim3(static_cast<unsigned>(M * S)), dim3(c.threads), args, 0, s);
+  const arf::SplitDims g = arf::split_dims(M, S);
+  return hipLaunchKernel(fn, dim3(static_cast<unsigned>(g.x), static_cast<unsigned>(g.y)),
+                         dim3(c.threads), args, 0, s);
 }
 
 // vecs_per_thread 1 or 2.

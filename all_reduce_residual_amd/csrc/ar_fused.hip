@@ -443,7 +443,7 @@ int check_split_cfg(int64_t M, int64_t H, int dtype, const ar_split_cfg_t* c) {
   const int64_t V = H / (kVecBytes / elem_size(dtype));
   const int64_t S = ceil_div(V, int64_t(t) * c->vecs_per_thread);
   if (S > arf::kSplitSlots || c->segments != S) return AR_ERR_INVALID_ARG;
-  if (M > INT_MAX / S) return AR_ERR_UNSUPPORTED;  // grid = M * S blocks
+  if (M > arf::split_max_rows) return AR_ERR_UNSUPPORTED;  // grid: S x M blocks (y <= 65535)
   return AR_OK;
 }
 

@@ -252,6 +252,26 @@ __device__ inline P* at(P* base, uint32_t byte_off) {
 // memory, so the batch's adds stay before it and the next batch's loads stay after it.  It
 // emits no instruction.  Latency is hidden by the other waves on the SIMD.
 
+// Reads a kernel's arguments in one round: up to 16 rank pointers and the given scalars are made
+// operands of one empty asm at the kernel's start.  Left alone, the compiler read the arguments
+// in two or three dependent rounds (each a scalar-cache miss) before the first load, which a
+// decode-size call pays in full.  With more than 16 ranks the pointers are left to the walk over
+// groups of 16 (forced reads there put full waits inside the sum kernel's fp16 rank batches), and
+// only the scalars are read at once.
+#define AR_RANK_PTR(i) "s"(in.p[(i) < W ? (i) : W - 1])
+#define AR_READ_ARGS(...)                                                                      \
+  do {                                                                                         \
+    if constexpr (W <= 16) {                                                                   \
+      asm volatile("" ::AR_RANK_PTR(0), AR_RANK_PTR(1), AR_RANK_PTR(2), AR_RANK_PTR(3),        \
+                   AR_RANK_PTR(4), AR_RANK_PTR(5), AR_RANK_PTR(6), AR_RANK_PTR(7),             \
+                   AR_RANK_PTR(8), AR_RANK_PTR(9), AR_RANK_PTR(10), AR_RANK_PTR(11),           \
+                   AR_RANK_PTR(12), AR_RANK_PTR(13), AR_RANK_PTR(14), AR_RANK_PTR(15),         \
+                   __VA_ARGS__);                                                               \
+    } else {                                                                                   \
+      asm volatile("" ::__VA_ARGS__);                                                          \
+    }                                                                                          \
+  } while (0)
+
 template <int W, int N, int kMaxLoads>
 constexpr int rank_batch() {
   int b = kMaxLoads / N;
@@ -446,6 +466,8 @@ template <class T, int W, int U, bool kNtStore, class Src = StreamSource>
 __global__ __launch_bounds__(kMaxThreads) void ar_sum_kernel(RankPtrs<W> in, u32x4* out,
                                                              int64_t nvec, int tail, Src src) {
   constexpr int kVec = T::kVec;
+  // Every argument the first loads need is read at once (left alone: two dependent rounds).
+  AR_READ_ARGS("s"(out), "s"(nvec), "s"(tail), "s"(blockDim.x), "s"(gridDim.x));
   AR_PHASE(0, 0, in.p[0]);
   const int64_t chunk = static_cast<int64_t>(blockDim.x) * U;
   if (static_cast<int64_t>(gridDim.x) * chunk >= nvec) {
@@ -545,11 +567,18 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_kernel(
   __shared__ float red_wide[2][kMaxWavesPerBlock];
   __shared__ bool wide_sh[kMaxWavesPerBlock];
 
+  // Every argument the first loads need is read at once: left alone, the compiler read the
+  // arguments in three dependent rounds (and divided by L and R) before the first load, which
+  // a decode-size call pays in full.
+  AR_READ_ARGS("s"(residual), "s"(gamma), "s"(residual_out), "s"(norm_out), "s"(M), "s"(V),
+               "s"(L), "s"(R), "s"(blockDim.x), "s"(gridDim.x));
   const int tid = threadIdx.x;
-  const int slot = tid / L;
-  const int lane = tid - slot * L;
+  int slot = 0, lane = tid;  // one row per block (R = 1): no division
+  if (R > 1) {
+    slot = tid / L;
+    lane = tid - slot * L;
+  }
   const int wave = tid >> 6;
-  const int64_t groups = (M + R - 1) / R;
 
   int idx[VPT];
   bool col_ok[VPT];
@@ -647,7 +676,7 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_kernel(
   // binary32 range of the sum of squares: with the partials' sum those rows are normalised
   // again after the loop (see below).
   bool any_wide = false;
-  for (int64_t grp = blockIdx.x; grp < groups; grp += gridDim.x) {
+  for (int64_t grp = blockIdx.x; grp * R < M; grp += gridDim.x) {
     const bool row_ok = grp * R + slot < M;
     const int64_t base = grp * R * static_cast<int64_t>(V);
     uint32_t boff[VPT];
@@ -811,7 +840,7 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_kernel(
       // back (the rounded values) and checked again: the same values in the same order give
       // the same sums of squares, so exactly the rows found outside the range above.
       __threadfence();
-      for (int64_t grp = blockIdx.x; grp < groups; grp += gridDim.x) {
+      for (int64_t grp = blockIdx.x; grp * R < M; grp += gridDim.x) {
         const bool row_ok = grp * R + slot < M;
         const int64_t base = grp * R * static_cast<int64_t>(V);
         uint32_t boff[VPT];
@@ -1147,13 +1176,27 @@ __device__ inline float split_segment(const RankPtrs<W>& in, const u32x4* residu
   return ss;
 }
 
-// Grid: M * S blocks of L threads; block b serves segment b % S of row b / S.  Requires
-// 1 <= S <= kSplitSlots, L a multiple of 64, and S * L * VPT >= V.
+// Launch grid of the split kernel (blocks in x and y).  The dispatcher places workgroups on the
+// 8 XCDs round-robin in linear order (x fastest).  With fewer rows than XCDs an 8 x S grid puts
+// the S segments of row m on XCD m (block (m, s)), so a row's blocks share one L2: 4-8 % faster
+// at M = 1 and 2 (W = 4, 8, 16) than segments spread over the XCDs.  Otherwise an S x M grid
+// (block (s, m)) for up to 65535 rows.  Results do not depend on the placement.
+constexpr int split_xcds = 8;
+constexpr int64_t split_max_rows = 65535;
+struct SplitDims {
+  int64_t x, y;
+};
+inline SplitDims split_dims(int64_t M, int64_t S) {
+  return M < split_xcds ? SplitDims{split_xcds, S} : SplitDims{S, M};
+}
+
+// Grid: split_dims(M, S) blocks of L threads (blocks that map to no row return at once).
+// Requires 1 <= S <= kSplitSlots, L a multiple of 64, and S * L * VPT >= V.
 template <class T, int W, int VPT, bool kNtStore>
 __global__ __launch_bounds__(kMaxThreads) void ar_norm_split_kernel(
     RankPtrs<W> in, const u32x4* residual, const f32x4* gamma, u32x4* residual_out,
     u32x4* norm_out, int V, int S, float eps, float count_h, uint64_t* slots,
-    uint32_t max_polls) {
+    uint32_t max_polls, int M) {
   constexpr int kVec = T::kVec;
   __shared__ float red[kMaxWavesPerBlock];
   __shared__ float part[kSplitSlots];
@@ -1162,8 +1205,14 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_split_kernel(
 
   const int tid = threadIdx.x;
   AR_PHASE(0, 0, in.p[0]);
-  const int m = blockIdx.x / S;
-  const int s = blockIdx.x - m * S;
+  const bool few = M < split_xcds;
+  const int m = static_cast<int>(few ? blockIdx.x : blockIdx.y);
+  const int s = static_cast<int>(few ? blockIdx.y : blockIdx.x);
+  // The arguments the block needs first are read with M, before the branch below: left alone,
+  // the compiler read M, branched, then read the rest, a round trip more before the first load.
+  AR_READ_ARGS("s"(residual), "s"(gamma), "s"(slots), "s"(V), "s"(S), "s"(blockDim.x),
+               "s"(M));
+  if (m >= M) return;  // the whole block, before any barrier
   const int64_t base = static_cast<int64_t>(m) * V;
   uint64_t* row = slots + static_cast<int64_t>(m) * kSplitSlots;
 

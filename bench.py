@@ -89,6 +89,15 @@ def metric_bytes(pattern: str, W: int, M: int, H: int, esize: int) -> int:
 
 # ---- GPU cases -------------------------------------------------------------------------------
 
+def split_dims(M: int, S: int):
+    """The split kernel's launch grid (blocks in x, y) for M rows of S segments: 8 x S with
+    fewer than 8 rows (block (m, s); a row's segments on one XCD), S x M up to 65535 rows, else
+    one dimension of M S blocks."""
+    if M < 8:
+        return 8, S
+    return (S, M) if M <= 65535 else (M * S, 1)
+
+
 class Case:
     """One (pattern, W, M, H) problem with R rotated buffer sets carved from one allocation per
     tensor role, and pre-marshalled C-ABI arguments for every set."""
@@ -498,7 +507,8 @@ def phase_table(ar, torch) -> str:
             if sp["segments"]:
                 cases.append(("kARResidualRMSNorm, %d segments per row" % sp["segments"],
                               "rms_ws", 2, W, M, H, sp["threads_per_block"], 1,
-                              M * sp["segments"], sp["segments"]))
+                              split_dims(M, sp["segments"])[0] * split_dims(M, sp["segments"])[1],
+                              sp["segments"]))
     cases.insert(0, ("empty kernel (launch floor)", None, 3, 8, 1, 7168, 64, 1, 1, 0))
     rows = ["| kernel | W | M | H | launch | per call, library (µs) | per call, stamped (µs) "
             "| span (µs) | gap (µs) | phases (µs after the first block's entry) |",
@@ -798,7 +808,13 @@ def summarize_sweep_trace(d: str, bench_json: str) -> str:
         sp = re.search(r"ar_norm_split_kernel<arf::Bf16, (\d+), (\d+), \w+>", name)
         if sp and int(sp.group(1)) == W:
             segments = -(-V // (wg * int(sp.group(2))))
-            durs.setdefault(("kARResidualRMSNorm, split rows", grid // wg // segments), []).append(
+            gy = int(r.get("Grid_Size_Y", 1) or 1)
+            if grid // wg == 8 and gy == segments:     # fewer than 8 rows: the sweep's one such M
+                few = [k[1] for k in per_call if k[0].endswith("split rows") and k[1] < 8]
+                M = few[0] if len(few) == 1 else None
+            else:
+                M = gy if gy > 1 else grid // wg // segments
+            durs.setdefault(("kARResidualRMSNorm, split rows", M), []).append(
                 (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
             continue
         m = re.search(r"ar_(norm|sum)_kernel<arf::Bf16, (\d+), (\d+), \w+, arf::StreamSource", name)

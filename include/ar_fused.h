@@ -189,7 +189,9 @@ int ar_residual_rmsnorm_with_config(const void* const* inputs, int W, int64_t M,
  *   threads_per_block : L, multiple of 64, 64..1024
  *   vecs_per_thread   : 1 or 2
  *   segments          : S = ceil((H / (16 / sizeof(T))) / (L * vecs_per_thread)), 1..64
- *                       (checked; blocks in the grid = M * S)
+ *                       (checked).  Split launches take up to 65535 rows (AR_ERR_UNSUPPORTED
+ *                       beyond; the planner splits only far fewer rows): a grid of 8 x S blocks
+ *                       below 8 rows, S x M from 8
  *   max_polls         : polls of the exchange before a block computes the row alone (0: never
  *                       wait; every block then reads the whole row) */
 typedef struct {

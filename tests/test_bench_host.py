@@ -140,3 +140,27 @@ def test_headline_windows_cover_exactly_the_timed_steps():
         assert min(lens) >= 1 and max(lens) - min(lens) <= 1
     assert bench.median([3.0, 1.0, 2.0]) == 2.0
     assert bench.median([4.0, 1.0, 2.0, 3.0]) == 2.5
+
+
+def test_split_grid_covers_every_segment_once():
+    """The split kernel's launch grid (bench mirrors the library's): 8 x S blocks with fewer
+    than 8 rows, block (m, s) on XCD m; S x M otherwise.  Every (row, segment) gets exactly one
+    block and every other block maps to a row past the last."""
+    for S in (1, 2, 3, 4, 7, 14, 64):
+        for M in list(range(1, 40)) + [63, 64, 65, 512, 65535, 65536]:
+            gx, gy = bench.split_dims(M, S)
+            if M > 4096:
+                assert (gx, gy) == ((S, M) if M <= 65535 else (M * S, 1))
+                continue
+            seen = set()
+            for y in range(gy):
+                for x in range(gx):
+                    if M < 8:
+                        m, s = x, y
+                        assert (y * gx + x) % 8 == m % 8    # linear order: XCD = id % 8
+                    else:
+                        m, s = y, x
+                    if m < M:
+                        assert s < S and (m, s) not in seen, (M, S, x, y)
+                        seen.add((m, s))
+            assert len(seen) == M * S, (M, S)
