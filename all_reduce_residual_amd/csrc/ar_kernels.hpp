@@ -944,6 +944,9 @@ __global__ __launch_bounds__(kMaxThreads) void ar_rmsnorm_rows_kernel(const void
                                                                       float count_h) {
   constexpr int kVec = T::kVec;
   __shared__ float red[kMaxWavesPerBlock];
+  // The arguments in one round (left alone: two dependent rounds before the first load).
+  asm volatile("" ::"s"(x), "s"(gamma), "s"(y), "s"(M), "s"(H), "s"(blockDim.x),
+               "s"(gridDim.x));
   const int64_t nthreads = blockDim.x;
   // Whole vectors in the tensor; a vector index at or past this one is not wholly inside it.
   const int64_t nfull = (M * H) / kVec;
