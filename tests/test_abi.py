@@ -509,6 +509,12 @@ def test_split_validation_rejects_before_device_access(L):
     assert L.ar_residual_rmsnorm_split_with_config(
         _ptrs(p[:8]), 8, M, 65536, BF16, res, gam, 1e-6, ro, no, ws, need, None,
         ctypes.byref(cfg)) == ar.AR_ERR_INVALID_ARG
+    # Split launches take up to 65535 rows (their grid is S x M blocks).
+    big = 65536
+    q = [(i + 1) << 32 for i in range(8)]                 # 4 GiB apart: no overlaps
+    assert L.ar_residual_rmsnorm_split_with_config(
+        _ptrs(q), 8, big, H, BF16, 20 << 32, 21 << 32, 1e-6, 22 << 32, 23 << 32, 24 << 32,
+        L.ar_split_workspace_bytes(big), None, ctypes.byref(good)) == ar.AR_ERR_UNSUPPORTED
     # The explicit split refuses outputs that alias the residual or an input.
     assert ws_call(ws, need, good, r_out=res) == ar.AR_ERR_ALIAS
     assert ws_call(ws, need, good, n_out=p[2]) == ar.AR_ERR_ALIAS
