@@ -221,6 +221,49 @@ def test_missing_producer_times_out_and_reports(oracle_mod):
                      "bf16", "after re-arm")
 
 
+@pytest.mark.parametrize("pattern", ["sum", "rms"])
+def test_missing_producer_times_out_with_smaller_polled_batches(oracle_mod, pattern):
+    """The consumers' smaller polled batches (two CUs' worth of rows and three more) are bounded
+    the same way: one rank never pushes, a spin limit of 4 polls, the status bit is set and the
+    call finishes; after re-arming the next round is exact."""
+    W, M, H = 8, 2 * ar.ar_device_cu_count() + 3, 7168
+    print("case", pattern, W, M, H, flush=True)
+    parts, res, gam = synth.custom(W, M, H, "bf16", seed=17 + M)
+    rbuf = _new_rbuf(W, M, H, torch.bfloat16)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    d_parts = [dev(p) for p in parts]
+    d_res, d_gam = dev(res), dev(gam)
+    out = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+    ro, no = torch.empty_like(out), torch.empty_like(out)
+
+    def consume(rnd, **kw):
+        if pattern == "sum":
+            ar.ar_lamport_sum(rbuf, rnd, out, status, **kw)
+        else:
+            ar.ar_lamport_residual_rmsnorm(rbuf, rnd, d_res, d_gam, 1e-6, ro, no, status, **kw)
+
+    for r, p in enumerate(d_parts[:-1]):
+        ar.ar_lamport_push(p, r, rbuf, 0)
+    consume(0, spin_limit=4)
+    torch.cuda.synchronize()
+    assert int(status.item()) & 1 == 1
+    ar.ar_lamport_arm(rbuf)
+    status.zero_()
+    for r, p in enumerate(d_parts):
+        ar.ar_lamport_push(p, r, rbuf, 1)
+    consume(1)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    hp = [host_np(p) for p in parts]
+    if pattern == "sum":
+        assert_bit_exact(host_np(out.cpu()), oracle_mod.ar_sum(hp, "bf16"), "bf16", "after re-arm")
+    else:
+        want_ro, want_no = oracle_mod.ar_residual_rmsnorm(hp, host_np(res), gam.numpy(), 1e-6,
+                                                          "bf16")
+        assert_bit_exact(host_np(ro.cpu()), want_ro, "bf16", "residual_out after re-arm")
+        assert_norm_close(host_np(no.cpu()), want_no, "bf16", "norm_out after re-arm")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
 def test_all_ones_input_is_not_mistaken_for_empty(oracle_mod, dtype):
     """A partial element that is all ones (a NaN) is delivered as a NaN with its lowest bit
