@@ -903,10 +903,21 @@ __device__ inline void store_row_vec(void* y, const float* gamma, int64_t e0, in
     for (int e = 0; e < T::kVec; ++e) o[e] = norm(f[e], g[e]);
     store_vec<true>(static_cast<u32x4*>(y) + v, T::narrow(o));
   } else {
+    // A vector the row shares with a neighbour: element stores.  gamma is read for every
+    // element first, at indices clamped into the row, so its loads go out together: read
+    // under each element's branch they went out a round trip apart (H = 7170 bf16 M = 2048:
+    // the row ends cost 0.96 of 12.6 us).
+    float g[T::kVec];
 #pragma unroll
     for (int e = 0; e < T::kVec; ++e) {
       const int64_t idx = a + e;
-      if (idx >= e0 && idx < e1) T::store1(y, idx, norm(f[e], gamma[idx - e0]));
+      const int64_t gi = idx < e0 ? 0 : (idx < e1 ? idx - e0 : e1 - 1 - e0);
+      g[e] = gamma[gi];
+    }
+#pragma unroll
+    for (int e = 0; e < T::kVec; ++e) {
+      const int64_t idx = a + e;
+      if (idx >= e0 && idx < e1) T::store1(y, idx, norm(f[e], g[e]));
     }
   }
 }
@@ -937,16 +948,35 @@ __device__ inline float block_sum(float v, float* red) {
 // that read it (a whole-vector load may also read a neighbouring row's elements while that row's
 // block rewrites them; those values are discarded).
 template <class T, int K>
-__global__ __launch_bounds__(kMaxThreads) void ar_rmsnorm_rows_kernel(const void* x,
+// K < 8: held to 64 VGPRs (8 waves per SIMD); left alone, the row-end code below took K = 4 to 68
+// and the blocks of 640 threads from three per CU to two (H = 16386 bf16 M = 768: 13 % slower).
+__global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(K == 8 ? 1 : 8)))
+void ar_rmsnorm_rows_kernel(const void* x,
                                                                       const float* gamma,
                                                                       void* y, int64_t M,
                                                                       int64_t H, float eps,
                                                                       float count_h) {
   constexpr int kVec = T::kVec;
   __shared__ float red[kMaxWavesPerBlock];
+  // gamma's first and last 8 values (indices clamped into the row): a row's partial first
+  // vector needs gamma[0, 8), its partial last one gamma[H - 8, H).
+  __shared__ float gends[16];
   // The arguments in one round (left alone: two dependent rounds before the first load).
   asm volatile("" ::"s"(x), "s"(gamma), "s"(y), "s"(M), "s"(H), "s"(blockDim.x),
                "s"(gridDim.x));
+  // Written to LDS in the first row, after its loads are out (a barrier at the start would put a
+  // round trip before every block's first load).  With 8 vectors per thread the value is read at
+  // the start (0.3 us of a 12 us call at H = 7170); with fewer, where registers bound the waves
+  // per SIMD, where it is stored.
+  auto gamma_end = [&]() {
+    const int64_t i = threadIdx.x < 8 ? int64_t(threadIdx.x) : H - 16 + int64_t(threadIdx.x);
+    return gamma[i < 0 ? 0 : (i < H ? i : H - 1)];
+  };
+  float gend = 0.0f;
+  bool gends_set = false;
+  if constexpr (K == 8) {
+    if (threadIdx.x < 16) gend = gamma_end();
+  }
   const int64_t nthreads = blockDim.x;
   // Whole vectors in the tensor; a vector index at or past this one is not wholly inside it.
   const int64_t nfull = (M * H) / kVec;
@@ -964,30 +994,41 @@ __global__ __launch_bounds__(kMaxThreads) void ar_rmsnorm_rows_kernel(const void
       // only its first and last can be partial: elements [lo, hi) belong to the row, lo = s
       // in the first, hi = t in the last, whole vectors otherwise.  (The launch gives the block
       // K * blockDim.x >= nv + 7 slots.)
+      // Slot arithmetic in 32 bits (a row spans at most H / kVec + 2 vectors, H <= 65536; slots
+      // < K blockDim.x): the 64-bit compares and selects it replaced were a measurable part of
+      // each row's latency.
       const int64_t vb = v0 & ~int64_t(7);
-      const int64_t off = v0 - vb;
+      const int off = static_cast<int>(v0 - vb);
+      const int nvi = static_cast<int>(nv);
+      const int nt32 = static_cast<int>(nthreads);
       const int s = static_cast<int>(e0 - v0 * kVec);
       const int t = static_cast<int>(e1 - (v0 + nv - 1) * kVec);
-      auto live = [&](int64_t j) { return j >= off && j < off + nv; };
-      auto lo_of = [&](int64_t j) { return j == off ? s : 0; };
-      auto hi_of = [&](int64_t j) { return j == off + nv - 1 ? t : kVec; };
+      auto live = [&](int j) { return j >= off && j < off + nvi; };
+      auto lo_of = [&](int j) { return j == off ? s : 0; };
+      auto hi_of = [&](int j) { return j == off + nvi - 1 ? t : kVec; };
+      // Slots from this one on hold vectors past the last whole one of the tensor.
+      const int64_t jf64 = nfull - vb;
+      const int jfull = jf64 > INT32_MAX ? INT32_MAX : static_cast<int>(jf64);
       float f[K][kVec];
       if (nfull > 0) {
         // Uniform base and 32-bit lane offsets.  A slot outside the row re-reads the row's first
         // vector (a line the wave loads anyway) rather than a neighbouring row's data.
         const int64_t bidx = vb < nfull ? vb : nfull - 1;
         const u32x4* xb = xv + bidx;
+        const int shift = static_cast<int>(vb - bidx);  // > 0 only past the last whole vector
+        const int64_t lim64 = nfull - 1 - bidx;
+        const int lim = lim64 > INT32_MAX ? INT32_MAX : static_cast<int>(lim64);
         u32x4 raw[K];
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-          const int64_t j = threadIdx.x + k * nthreads;
-          int64_t vi = live(j) ? vb + j : v0;
-          vi = vi < nfull ? vi : nfull - 1;
-          raw[k] = load_stream(at(xb, static_cast<uint32_t>(vi - bidx) * 16u));
+          const int j = static_cast<int>(threadIdx.x) + k * nt32;
+          int r = (live(j) ? j : off) + shift;
+          r = r < lim ? r : lim;
+          raw[k] = load_stream(at(xb, static_cast<uint32_t>(r) * 16u));
         }
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-          const int64_t j = threadIdx.x + k * nthreads;
+          const int j = static_cast<int>(threadIdx.x) + k * nt32;
           if (!live(j)) raw[k] = u32x4{0, 0, 0, 0};
           T::widen(raw[k], f[k]);
           const int lo = lo_of(j), hi = hi_of(j);
@@ -1005,13 +1046,20 @@ __global__ __launch_bounds__(kMaxThreads) void ar_rmsnorm_rows_kernel(const void
       }
 #pragma unroll
       for (int k = 0; k < K; ++k) {
-        const int64_t j = threadIdx.x + k * nthreads;
-        if (live(j) && vb + j >= nfull) load_row_vec<T, false>(x, e0, e1, vb + j, f[k]);
+        const int j = static_cast<int>(threadIdx.x) + k * nt32;
+        if (live(j) && j >= jfull) load_row_vec<T, false>(x, e0, e1, vb + j, f[k]);
 #pragma unroll
         for (int e = 0; e < kVec; ++e) ss += f[k][e] * f[k][e];
       }
       // gamma is read in the epilogue, per vector (L2): moving all of it before the barrier
       // measured slower (H = 7170: 15.9 -> 18.3 us), the other blocks on the CU hide its latency.
+      // gamma's ends go to LDS before the block's first barrier (a one-wave block has none, and
+      // its LDS accesses stay in program order).
+      if (!gends_set) {
+        if (threadIdx.x < 16) gends[threadIdx.x] = K == 8 ? gend : gamma_end();
+        gends_set = true;
+        if (nthreads == 64) __builtin_amdgcn_wave_barrier();
+      }
       const float x32 = block_sum(ss, red) / count_h + eps;
       float m = rsqrtf(x32);
       int E = 0;
@@ -1031,9 +1079,10 @@ __global__ __launch_bounds__(kMaxThreads) void ar_rmsnorm_rows_kernel(const void
       }
       auto norm = [&](float a, float g) { return norm_elem_scaled(a, m, E, g); };
       u32x4* yb = static_cast<u32x4*>(y) + vb;
+      const int Hi = static_cast<int>(H);
 #pragma unroll
       for (int k = 0; k < K; ++k) {
-        const int64_t j = threadIdx.x + k * nthreads;
+        const int j = static_cast<int>(threadIdx.x) + k * nt32;
         if (!live(j)) continue;
         if (lo_of(j) == 0 && hi_of(j) == kVec) {
           // A whole vector of the row (so wholly inside the tensor): gamma[(j - off) kVec - s ...]
@@ -1053,7 +1102,17 @@ __global__ __launch_bounds__(kMaxThreads) void ar_rmsnorm_rows_kernel(const void
           for (int e = 0; e < kVec; ++e) o[e] = norm(f[k][e], gv[e]);
           store_vec<true>(at(yb, static_cast<uint32_t>(j) * 16u), T::narrow(o));
         } else {
-          store_row_vec<T>(y, gamma, e0, e1, vb + j, f[k], norm);
+          // A vector the row shares with a neighbour (its first or last): element stores,
+          // gamma from the block's copy of its first and last 8 values in LDS (a read of
+          // global gamma here cost the row a round trip at its end).
+          const int lo = lo_of(j), hi = hi_of(j);
+          const int gb = (j - off) * kVec - s;  // gamma index of the vector's element 0
+          void* yv = yb + j;
+#pragma unroll
+          for (int e = 0; e < kVec; ++e) {
+            const int gi = gb + e;
+            if (e >= lo && e < hi) T::store1(yv, e, norm(f[k][e], gends[gi < 8 ? gi : gi - Hi + 16]));
+          }
         }
       }
     } else {
