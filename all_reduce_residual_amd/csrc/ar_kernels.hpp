@@ -1272,8 +1272,8 @@ __global__ __launch_bounds__(kMaxThreads) void ar_norm_split_kernel(
   const int s = static_cast<int>(few ? blockIdx.y : blockIdx.x);
   // The arguments the block needs first are read with M, before the branch below: left alone,
   // the compiler read M, branched, then read the rest, a round trip more before the first load.
-  AR_READ_ARGS("s"(residual), "s"(gamma), "s"(slots), "s"(V), "s"(S), "s"(blockDim.x),
-               "s"(M));
+  AR_READ_ARGS("s"(residual), "s"(gamma), "s"(residual_out), "s"(norm_out), "s"(slots), "s"(V),
+               "s"(S), "s"(blockDim.x), "s"(M));
   if (m >= M) return;  // the whole block, before any barrier
   const int64_t base = static_cast<int64_t>(m) * V;
   uint64_t* row = slots + static_cast<int64_t>(m) * kSplitSlots;

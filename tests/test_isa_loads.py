@@ -41,6 +41,7 @@ TN = {"Bf16": "4Bf16", "F16": "3F16", "F32": "3F32"}
 
 
 SUM_W = (1, 2, 4, 8, 16, 32, 64)
+ROWS_K = (0, 1, 2, 4, 8)
 SUM_U = (1, 2, 4)
 KVEC = {"Bf16": 8, "F16": 8, "F32": 4}
 
@@ -61,6 +62,9 @@ def _source() -> str:
             for u in SUM_U:
                 refs.append("reinterpret_cast<const void*>(&arf::ar_sum_kernel<arf::%s, %d, %d, "
                             "true>)" % (t, w, u))
+        for k in ROWS_K:
+            refs.append("reinterpret_cast<const void*>(&arf::ar_rmsnorm_rows_kernel<arf::%s, %d>)"
+                        % (t, k))
     return ('#include "ar_kernels.hpp"\n'
             "const void* const kKernels[] = {\n  " + ",\n  ".join(refs) + "};\n")
 
@@ -233,6 +237,48 @@ def test_rank_batches_wait_only_between_batches(norm_asm):
             if loads[sym[0]] < (ranks + 1) * v or waits[sym[0]] > ranks // n:
                 bad.append((t, w, v, n, loads[sym[0]], waits[sym[0]]))
     assert not bad, "(type, W, vectors per thread, ranks per batch, loads, full waits): %s" % bad
+
+
+def _argument_rounds(asm: str, kernel: str) -> dict:
+    """Per kernel symbol: the scalar-memory waits (`s_waitcnt lgkmcnt`) from the kernel's entry
+    to its first streaming (non-temporal) load of the data, i.e. the dependent rounds of
+    kernel-argument reads before the data is requested."""
+    out, name = {}, None
+    for line in asm.splitlines():
+        m = re.match(r"^(_Z\S*%s\S*):" % kernel, line)
+        if m:
+            name = m.group(1)
+            out[name] = 0
+        elif name is not None:
+            if re.search(r"\b(global|buffer)_load\S* .* nt", line):
+                name = None
+            elif "s_waitcnt" in line and "lgkmcnt" in line:
+                out[name] += 1
+            elif "s_endpgm" in line:
+                name = None
+    return out
+
+
+def test_kernel_arguments_read_in_one_round(norm_asm):
+    """Every kernel reads the arguments its first loads need in one round: one scalar wait before
+    its first load of the data (two or three dependent rounds cost a decode-size call 2-3.5 %).
+    Checked on the norm kernel's planned shapes, every sum and split kernel up to 16 ranks and
+    the one-pass rows kernels, all three element types (the earlier form: 3 / 2 / 2 / 2)."""
+    bad = []
+    for kernel in ("ar_norm_kernel", "ar_sum_kernel", "ar_norm_split_kernel",
+                   "ar_rmsnorm_rows_kernel"):
+        rounds = _argument_rounds(norm_asm, kernel)
+        assert rounds, kernel
+        for sym, n in rounds.items():
+            w = int(re.search(r"kernelINS_\w+?ELi(\d+)E", sym).group(1))
+            # W > 16 ranks: the pointers stay with the 16-rank walk.  Rows kernel with K = 0
+            # (rows past 8 vectors per thread): two passes over cached loads, no streaming one.
+            if (kernel != "ar_rmsnorm_rows_kernel" and w > 16) or \
+                    (kernel == "ar_rmsnorm_rows_kernel" and w == 0):
+                continue
+            if n != 1:
+                bad.append((sym, n))
+    assert not bad, "kernels reading their arguments in more than one round: %s" % bad
 
 
 def test_checker_sees_a_serialized_load():
