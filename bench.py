@@ -1042,9 +1042,9 @@ def main():
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU's share of the fused all-reduce on a single MI355X; "
-              "runs on more than one GPU are not part of this build (got --gpus %d, "
-              "WORLD_SIZE=%d)." % (args.gpus, world), file=sys.stderr)
+        print("bench.py measures one GPU's share of the fused all-reduce on a single MI355X and "
+              "does not run on more than one GPU (got --gpus %d, WORLD_SIZE=%d)."
+              % (args.gpus, world), file=sys.stderr)
         return 2
 
     import torch

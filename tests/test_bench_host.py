@@ -164,3 +164,17 @@ def test_split_grid_covers_every_segment_once():
                         assert s < S and (m, s) not in seen, (M, S, x, y)
                         seen.add((m, s))
             assert len(seen) == M * S, (M, S)
+
+
+def test_more_than_one_gpu_is_refused():
+    """--gpus N > 1 (or a multi-rank launch) exits with status 2 and says why, before touching
+    a GPU."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for argv, env in ((["--gpus", "2"], {}), (["--gpus", "1"], {"WORLD_SIZE": "2"})):
+        r = subprocess.run([sys.executable, os.path.join(root, "bench.py")] + argv,
+                           capture_output=True, text=True, env=dict(os.environ, **env),
+                           timeout=120)
+        assert r.returncode == 2, (argv, r.returncode, r.stderr)
+        assert "does not run on more than one GPU" in r.stderr
