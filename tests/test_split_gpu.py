@@ -73,6 +73,20 @@ def test_split_matches_oracle(oracle_mod, W, M, H, threads, vpt, dtype):
     _check(oracle_mod, parts, res, gam, 1e-6, dtype, ro, no)
 
 
+@pytest.mark.parametrize("M", [7, 8, 9, 1000, 65535])
+def test_split_grid_forms_and_row_limit(oracle_mod, M):
+    """Both grid forms (8 x S blocks below 8 rows, one row's segments on one XCD; S x M from 8
+    rows) and the most rows the S x M grid takes (65535, its y limit), two segments per row,
+    every row against the oracle."""
+    W, H, dtype = 2, 1024, "bf16"
+    print("case split grid W=%d M=%d H=%d" % (W, M, H), flush=True)
+    parts, res, gam = synth.custom(W, M, H, dtype, seed=M)
+    cfg = _cfg(H, dtype, 64, 1)
+    assert cfg["segments"] == 2
+    ro, no = _run(parts, res, gam, 1e-6, ar.new_workspace(M, "cuda"), config=cfg)
+    _check(oracle_mod, parts, res, gam, 1e-6, dtype, ro, no)
+
+
 @pytest.mark.parametrize("M", [1, 8, 32, 64, 128])
 def test_wide_hidden_decode_sizes_planned(oracle_mod, M):
     """The wide-hidden workload (W = 8, H = 7168 bf16) at decode sizes, planned shape."""
