@@ -49,6 +49,21 @@ def test_noalloc_matches_workspace_form(oracle_mod):
         assert_norm_close(host_np(no_b.cpu()), want_no, dtype)
 
 
+def test_noalloc_most_rows_accepted(oracle_mod):
+    """The largest row count the array is sized for runs and matches the oracle."""
+    W, M, H, dtype = 2, ar.NOALLOC_MAX_ROWS, 256, "bf16"
+    print("case noalloc rows", M, flush=True)
+    parts, res, gam = synth.custom(W, M, H, dtype, seed=6)
+    d_parts, d_res = [dev(p) for p in parts], dev(res)
+    ro, no = torch.empty_like(d_res), torch.empty_like(d_res)
+    ar.ar_residual_rmsnorm_noalloc(d_parts, d_res, dev(gam), 1e-6, ro, no)
+    torch.cuda.synchronize()
+    want_ro, want_no = oracle_mod.ar_residual_rmsnorm([host_np(p) for p in parts], host_np(res),
+                                                      gam.numpy(), 1e-6, dtype)
+    assert_bit_exact(host_np(ro.cpu()), want_ro, dtype, "residual_out")
+    assert_norm_close(host_np(no.cpu()), want_no, dtype)
+
+
 def test_noalloc_rows_beyond_the_array_rejected():
     W, M, H = 2, ar.NOALLOC_MAX_ROWS + 1, 256
     parts, res, gam = synth.custom(W, M, H, "bf16", seed=5)
